@@ -1,0 +1,185 @@
+"""CPU oracle for the RaggedShard shard step -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path never does: it has
+its own GPU library and fails loudly when that library is missing.
+
+``ve_oracle.c`` holds the arithmetic (plain C, fp64 updates; see its header
+for the method and the readings taken where the pages are silent).  This
+module only builds it with gcc and marshals numpy arrays through ctypes.
+``bruteforce.py`` is a second, unsharded numpy formulation used to pin the
+C oracle's layout logic.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ve_oracle.c")
+_LIB = os.path.join(_HERE, "_build", "libve_oracle.so")
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no FMA contraction, IEEE semantics)."""
+    if force or not os.path.exists(_LIB):
+        os.makedirs(os.path.dirname(_LIB), exist_ok=True)
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off",
+                               "-fno-fast-math", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Tensor(C.Structure):
+    _fields_ = [("rows", C.c_int64), ("cols", C.c_int64), ("block_rows", C.c_int64),
+                ("block_cols", C.c_int64), ("offset", C.c_int64)]
+
+
+class _HParams(C.Structure):
+    _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
+                ("eps", C.c_double), ("wd", C.c_double)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = C.CDLL(_LIB)
+        P = C.c_void_p
+        L.ora_last_error.restype = C.c_char_p
+        L.ora_validate.argtypes = [P, C.c_int, C.c_int, C.c_int64]
+        L.ora_rank_blocks.restype = C.c_int64
+        L.ora_rank_blocks.argtypes = [P, C.c_int, C.c_int64, C.c_int64, P]
+        L.ora_slice.argtypes = [P, C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int, P, P, P]
+        L.ora_copy_in.restype = None
+        L.ora_copy_in.argtypes = [P, C.c_int, C.c_int, C.c_int64, C.c_int64, P, P, P]
+        L.ora_quantize.restype = None
+        L.ora_quantize.argtypes = [P, C.c_int64, P, P]
+        L.ora_shard_step.argtypes = [P, C.c_int, C.c_int, C.c_int64, C.c_int64, P, P,
+                                     P, P, P, P, P, P, P, P, C.c_int64, P, C.c_int64]
+        _lib = L
+    return _lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _specs(spec: np.ndarray):
+    spec = np.ascontiguousarray(spec, dtype=np.int64).reshape(-1, 5)
+    arr = (_Tensor * max(1, len(spec)))()
+    for i, row in enumerate(spec):
+        arr[i] = _Tensor(*[int(v) for v in row])
+    return arr, len(spec)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(C.c_void_p) if a is not None else None
+
+
+def quantize(x) -> tuple:
+    """The oracle's block quantiser on one fp32 block: (int8 codes, fp32 scale)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    q = np.zeros(x.size, dtype=np.int8)
+    s = np.zeros(1, dtype=np.float32)
+    lib().ora_quantize(_ptr(x), x.size, _ptr(q), _ptr(s))
+    return q, np.float32(s[0])
+
+
+def validate(spec, m: int, S: int) -> None:
+    arr, n = _specs(spec)
+    if lib().ora_validate(arr, n, m, S) != 0:
+        raise OracleError(lib().ora_last_error().decode())
+
+
+def rank_blocks(spec, S: int, rank: int):
+    """(number of quantisation blocks, number of valid elements) on ``rank``."""
+    arr, n = _specs(spec)
+    v = C.c_int64(0)
+    nb = lib().ora_rank_blocks(arr, n, S, rank, C.byref(v))
+    return int(nb), int(v.value)
+
+
+def slice_(spec, m: int, S: int, rank: int, k: int):
+    """(shard_offset, elem_start, elem_end) of tensor k on ``rank``, or None."""
+    arr, n = _specs(spec)
+    a, b, c = C.c_int64(), C.c_int64(), C.c_int64()
+    ok = lib().ora_slice(arr, n, m, S, rank, k, C.byref(a), C.byref(b), C.byref(c))
+    return (a.value, b.value, c.value) if ok else None
+
+
+def _grad_table(grads, bases, n):
+    ptrs = (C.c_void_p * max(1, n))()
+    base = np.zeros(max(1, n), dtype=np.int64)
+    keep = []
+    for k in range(n):
+        g = grads[k]
+        if g is None:
+            ptrs[k] = None
+            continue
+        g = np.ascontiguousarray(g, dtype=np.uint16)
+        keep.append(g)
+        ptrs[k] = g.ctypes.data
+        base[k] = 0 if bases is None else int(bases[k])
+    return ptrs, base, keep
+
+
+def copy_in(spec, m: int, S: int, rank: int, grads, bases=None) -> np.ndarray:
+    """Group copy-in of ``rank``'s chunk (rank -1: the whole bucket)."""
+    arr, n = _specs(spec)
+    ptrs, base, keep = _grad_table(grads, bases, n)
+    out = np.empty(m * S if rank < 0 else S, dtype=np.uint16)
+    lib().ora_copy_in(arr, n, m, S, rank, ptrs, _ptr(base), _ptr(out))
+    return out
+
+
+def shard_step(spec, m: int, S: int, rank: int, grads, state: dict, hp: dict, t: int,
+               bases=None, blocks=None) -> dict:
+    """One fused step on ``rank``; ``state`` arrays are updated in place.
+
+    ``state`` keys: grad_shard (uint16[S]), master (float32[S]), m_q, v_q
+    (int8[S]), m_scale, v_scale (float32[B_r]), param_shard (uint16[S]).
+    ``hp`` values are rounded to fp32 first (the step's hyper-parameters are
+    fp32 numbers).
+    ``blocks``: optional list of block indices to process (the rest is
+    untouched).
+    """
+    arr, n = _specs(spec)
+    ptrs, base, keep = _grad_table(grads, bases, n)
+    want = {"grad_shard": np.uint16, "master": np.float32, "m_q": np.int8, "v_q": np.int8,
+            "m_scale": np.float32, "v_scale": np.float32, "param_shard": np.uint16}
+    for key, dt in want.items():
+        a = state[key]
+        if a.dtype != dt or not a.flags.c_contiguous:
+            raise TypeError(f"{key}: need contiguous {np.dtype(dt)}")
+    # the step's hyper-parameters are fp32 quantities; the oracle works on
+    # exactly those values, widened to double
+    f = lambda key: float(np.float32(hp[key]))
+    h = _HParams(f("lr"), f("beta1"), f("beta2"), f("eps"), f("weight_decay"))
+    sel = None if blocks is None else np.ascontiguousarray(blocks, dtype=np.int64)
+    rc = lib().ora_shard_step(arr, n, m, S, rank, ptrs, _ptr(base),
+                              _ptr(state["grad_shard"]), _ptr(state["master"]), _ptr(state["m_q"]),
+                              _ptr(state["v_q"]), _ptr(state["m_scale"]), _ptr(state["v_scale"]),
+                              _ptr(state["param_shard"]), C.byref(h), int(t),
+                              _ptr(sel), 0 if sel is None else len(sel))
+    if rc != 0:
+        raise OracleError(lib().ora_last_error().decode())
+    return state
+
+
+def new_state(spec, S: int, rank: int, master: np.ndarray) -> dict:
+    """Zero optimizer state (codes and scales 0) around an fp32 master shard."""
+    nb, _ = rank_blocks(spec, S, rank)
+    return dict(grad_shard=np.zeros(S, np.uint16), master=np.array(master, np.float32, copy=True),
+                m_q=np.zeros(S, np.int8), v_q=np.zeros(S, np.int8),
+                m_scale=np.zeros(nb, np.float32), v_scale=np.zeros(nb, np.float32),
+                param_shard=np.zeros(S, np.uint16))
