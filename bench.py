@@ -1,0 +1,196 @@
+"""Benchmark of the fused RaggedShard shard step on one MI355X.
+
+One step = one ``ve_shard_adam8bit_step`` call over every bucket of the
+workload on one rank (group copy-in of the bf16 gradients, block-wise 8-bit
+AdamW with one absmax scale per block, bf16 parameter write-back).  Default
+workload: LLaMA-3-70B-shaped buckets, 80 layers, 1-row blocks, FSDP size 128,
+rank 0 (6,709,248 elements and 234 blocks of 28,672 per bucket).  Inputs are
+synthetic, seeded, resident in HBM before timing.
+
+Prints one JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--workload llama|gptoss|deepseek|adversarial]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
+METRIC = "fused shard-step HBM GB/s and params/s on 1 GPU; % of HBM peak"
+# algorithmic bytes: per valid element, per quantisation block, per padding element
+BYTES_PER_ELEM = 18   # grad read 2 + grad-slice write 2 + master r/w 8 + codes r/w 4 + bf16 param write 2
+BYTES_PER_BLOCK = 16  # two fp32 scales read + written
+BYTES_PER_PAD = 4     # two bf16 zero writes
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("ve_kernels.hip", "ve_internal.h", "ve_host.cpp"):
+        with open(os.path.join(ROOT, "ragged_shard_optimizer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"shard_step_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, lay, rank, budget_s=12.0):
+    """The oracle (single-threaded plain C) on a bounded sample of the same
+    workload: a few distinct host buckets of the rank's shard, stepped in turn
+    until about ``budget_s`` of CPU time is spent."""
+    import numpy as np
+    import oracle
+    from synth.data import f32_to_bf16_bits
+    spec, S = lay.spec_array(), lay.shard
+    pieces = list(lay.chunk_intervals(rank))
+    rng = np.random.default_rng(1)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    sets = []
+    n_sets = 4
+    for _ in range(n_sets):
+        grads, bases = [None] * len(lay.tensors), [0] * len(lay.tensors)
+        for k, lo, hi, _dst in pieces:
+            grads[k] = f32_to_bf16_bits((rng.standard_normal(hi - lo) * cfg.grad_scale).astype(np.float32))
+            bases[k] = lo
+        st = oracle.new_state(spec, S, rank, (rng.standard_normal(S) * cfg.param_std).astype(np.float32))
+        sets.append((grads, bases, st))
+    oracle.shard_step(spec, lay.fsdp, S, rank, sets[0][0], sets[0][2], hp, 1, bases=sets[0][1])  # warm
+    done, t0, step = 0, time.perf_counter(), 2
+    while True:
+        grads, bases, st = sets[done % n_sets]
+        oracle.shard_step(spec, lay.fsdp, S, rank, grads, st, hp, step, bases=bases)
+        done += 1
+        if done % n_sets == 0:
+            step += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s and done >= n_sets:
+            break
+    nb, nv = oracle.rank_blocks(spec, S, rank)
+    alg = BYTES_PER_ELEM * nv + BYTES_PER_BLOCK * nb + BYTES_PER_PAD * (S - nv)
+    return {"value": round(alg * done / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "params_per_s": round(nv * done / el, 1),
+            "sample": f"{done} bucket-steps of rank {rank} ({nv} elements each, {n_sets} distinct host "
+                      f"buckets stepped in turn), {el:.1f} s wall, single thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama", choices=["llama", "gptoss", "deepseek", "adversarial"])
+    ap.add_argument("--buckets", type=int, default=None, help="override the number of buckets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the data-parallel step; --gpus {args.gpus} is not "
+              f"supported (the collectives around the step are outside this library)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    sys.path.insert(0, ROOT)
+    import ragged_shard_optimizer_amd as ve
+    from synth import CONFIGS, HPARAMS, plan_p0
+    from synth.workload import device_buckets
+
+    cfg = CONFIGS[args.workload]
+    lay = plan_p0(cfg.tensors, cfg.fsdp)
+    rank = lay.largest_rank()
+    nbk = args.buckets or cfg.n_buckets
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
+    valid, nblocks, nseg = plan.query(rank)
+    log(f"[bench] {cfg.name}: rank {rank}, {nbk} buckets, S={lay.shard}, valid={valid}, blocks={nblocks}")
+    t0 = time.time()
+    buckets = device_buckets(cfg, lay, rank, dev, n_buckets=nbk)
+    states = [ve.new_state(plan, rank, ve.grad_pointer_table(g, dev), m) for g, m in buckets]
+    table = ve.state_table(plan, rank, states)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident in HBM ({time.time() - t0:.1f} s)")
+
+    hp = dict(HPARAMS)
+    stream = torch.cuda.current_stream()
+    step = 0
+    for _ in range(args.warmup):
+        step += 1
+        plan.step(rank, table, hp, step, stream)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        step += 1
+        starts[i].record(stream)
+        plan.step(rank, table, hp, step, stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]  # ms, on the launch stream
+    ms = sum(per) / len(per)
+    ms_wall = wall * 1e3 / args.steps
+    log(f"[bench] timed {args.steps} steps: event avg {ms:.4f} ms, min {min(per):.4f}, max {max(per):.4f}; "
+        f"wall {ms_wall:.4f} ms/step")
+
+    S = lay.shard
+    alg_bytes = nbk * (BYTES_PER_ELEM * valid + BYTES_PER_BLOCK * nblocks + BYTES_PER_PAD * (S - valid))
+    gbs = alg_bytes / (ms / 1e3) / 1e9
+    params_s = nbk * valid / (ms / 1e3)
+    traffic = measured_traffic(args.workload)
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.description + f"; rank {rank}", "buckets": nbk, "fsdp": lay.fsdp,
+                   "shard_elems": S, "valid_elems_per_bucket": valid, "blocks_per_bucket": nblocks,
+                   "alg_bytes_per_step": alg_bytes},
+        "params_per_s": round(params_s, 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "ms_per_step_wall": round(ms_wall, 5),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic / (ms / 1e3) / 1e9, 2)},
+    }
+    del states, table, buckets
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on host cores")
+        out["cpu_baseline"] = cpu_baseline(cfg, lay, rank)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

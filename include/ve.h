@@ -1,0 +1,159 @@
+/*
+ * ve.h -- C ABI of the MI355X RaggedShard shard-step library (libve.so).
+ *
+ * The library runs the data-parallel hot path of veScale-FSDP ("veScale-FSDP:
+ * Flexible and High-Performance FSDP at Scale") on one rank's slice of a
+ * planned DBuffer bucket:
+ *
+ *   1. group copy-in of per-parameter bf16 gradients into the flat, padded
+ *      bucket slice (talk notes, "3. DBuffer": tensors enter the buffer
+ *      through group-level operators, zero-copy);
+ *   2. a block-wise 8-bit AdamW step on the local shard, one absmax scale per
+ *      RaggedShard quantisation block, so no rank needs another rank's data
+ *      (talk notes, "1. RaggedShard": sync-free block-wise quantisation;
+ *      "Case study: 8-bit Adam and distributed Muon");
+ *   3. write-back of the bf16 parameter shard for the next all-gather.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Bucket: m = fsdp_size equal chunks of S = shard_elems elements; rank r
+ *    owns bucket elements [r*S, (r+1)*S) ("shard coordinates" 0..S-1).
+ *    Equal chunks are what in-place all-gather / reduce-scatter need
+ *    (talk notes, "3. DBuffer").
+ *  - Tensor k is a row-major rows x cols matrix (1-D: numel x 1) stored
+ *    contiguously at bucket elements [offset, offset + rows*cols).  Padding
+ *    exists only between tensors (talk notes, "2. Structure-aware planning";
+ *    Dutch summary, "2B").
+ *  - RaggedShard block of tensor k: the shard unit is a row panel of
+ *    block_rows rows (block_rows*cols elements); a chunk boundary may cut a
+ *    tensor only at a unit boundary.  The quantisation block is the
+ *    block_rows x block_cols tile inside a panel (block_cols divides cols;
+ *    block_cols == cols gives whole-row blocks).  A last panel with fewer
+ *    than block_rows rows is a shorter block with its own scale.
+ *  - Piece: tensor k's intersection with rank r's chunk, tensor elements
+ *    [elem_start, elem_end), stored at shard coordinates
+ *    [shard_offset, shard_offset + elem_end - elem_start).
+ *  - Rank-local block order (index into m_scale / v_scale): pieces by
+ *    ascending bucket offset; inside a piece, panels top to bottom, and
+ *    inside a panel, tiles left to right.  B_r is the rank's block count.
+ *  - Pointers named "device" are device (or managed) memory on the plan's
+ *    device; "host" pointers are host memory.  The caller owns every data
+ *    buffer and pointer table; the library never allocates or copies per
+ *    call.  Device arrays of pointers cannot be inspected from the host:
+ *    entries the call reads must be valid, or the kernel faults.
+ *  - Streams: `stream` is a hipStream_t (NULL = the null stream).  No call
+ *    synchronises; device-side faults surface at the caller's next sync.
+ *  - Errors: every entry point returns a ve_status; on failure
+ *    ve_last_error() returns a thread-local message.  No C++ exception
+ *    crosses the ABI.  A call rejected by its argument checks has launched
+ *    nothing; a VE_ERR_DEVICE from a launch may leave earlier launches of
+ *    the same call queued.
+ *  - Concurrency: a loaded plan is immutable; calls on different streams
+ *    with disjoint output buffers may overlap.
+ */
+#ifndef VE_H
+#define VE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    VE_OK = 0,
+    VE_ERR_INVALID_ARG = 1,  /* NULL / out-of-range argument */
+    VE_ERR_LAYOUT = 2,       /* the bucket layout breaks a RaggedShard invariant */
+    VE_ERR_OOM = 3,          /* device allocation for the plan tables failed */
+    VE_ERR_DEVICE = 4,       /* a HIP runtime call or kernel launch failed */
+    VE_ERR_UNSUPPORTED = 5   /* valid layout outside this build's limits */
+} ve_status;
+
+typedef struct ve_plan ve_plan; /* opaque; created by ve_plan_load */
+
+/* One tensor of the bucket (any order; the library sorts by offset). */
+typedef struct {
+    int64_t rows, cols;             /* dim 0 and prod(dims[1:]); both >= 1 */
+    int64_t block_rows, block_cols; /* RaggedShard block: >= 1, block_cols | cols */
+    int64_t offset;                 /* first element's bucket offset */
+} ve_tensor_spec;
+
+/* AdamW hyper-parameters (fp32, as the step consumes them). */
+typedef struct {
+    float lr, beta1, beta2, eps, weight_decay;
+} ve_adam_hparams;
+
+/* One bucket's buffers on one rank.  All members are device pointers.
+ * Arrays of S elements must be 16-byte aligned for the vector path (any
+ * alignment is correct, misaligned ones are slower). */
+typedef struct {
+    const uint16_t* const* grad_ptrs; /* device array [n_tensors] of bf16 gradient
+                                         pointers, tensor k's element e at
+                                         grad_ptrs[k][e]; entries of tensors without
+                                         a piece on the rank are not read (may be NULL) */
+    uint16_t* grad_shard;  /* bf16 [S] out: copied-in gradient slice, padding 0 */
+    float* master;         /* fp32 [S] in/out: master weights (padding untouched) */
+    int8_t* m_q;           /* int8 [S] in/out: first-moment codes */
+    int8_t* v_q;           /* int8 [S] in/out: second-moment codes (0..127) */
+    float* m_scale;        /* fp32 [B_r] in/out: first-moment block scales */
+    float* v_scale;        /* fp32 [B_r] in/out: second-moment block scales */
+    uint16_t* param_shard; /* bf16 [S] out: RNE(master), padding 0 */
+} ve_shard_state;
+
+/* Validate a bucket layout and upload its per-rank segment tables to
+ * `device` (host specs[n_tensors]).  Checks: shapes and blocks positive,
+ * block_cols | cols; tensors disjoint and inside [0, fsdp_size*shard_elems);
+ * every chunk boundary inside a tensor on a unit boundary (talk notes,
+ * "1. RaggedShard").  VE_ERR_LAYOUT names the tensor and boundary that
+ * fail.  VE_ERR_UNSUPPORTED: a block of more than 2^30 elements.
+ * device == -1 builds a host-only plan: validation, ve_plan_query and
+ * ve_dbuffer_slice work, kernel entry points return VE_ERR_INVALID_ARG.
+ * On success *out owns the tables until ve_plan_free. */
+ve_status ve_plan_load(const ve_tensor_spec* specs, int32_t n_tensors, int32_t fsdp_size,
+                       int64_t shard_elems, int32_t device, ve_plan** out);
+
+/* Release a plan (NULL is a no-op).  No call may still be using it. */
+ve_status ve_plan_free(ve_plan* plan);
+
+/* Per-rank sizes (host outputs; any may be NULL): valid elements, B_r, and
+ * the number of pieces. */
+ve_status ve_plan_query(const ve_plan* plan, int32_t rank, int64_t* valid_elems,
+                        int64_t* n_blocks, int32_t* n_segments);
+
+/* Group copy-in (talk notes, "3. DBuffer").  rank >= 0: bucket is bf16 [S],
+ * receives rank's pieces at their shard coordinates; rank == -1: bucket is
+ * bf16 [fsdp_size*S], receives every tensor.  Padding is written as 0.
+ * grad_ptrs: device array as in ve_shard_state. */
+ve_status ve_dbuffer_copy_in(const ve_plan* plan, int32_t rank, const uint16_t* const* grad_ptrs,
+                             uint16_t* bucket, void* stream);
+
+/* The fused shard step on `rank` for n_states buckets that share this plan
+ * (one launch per path; states is a DEVICE array [n_states]).  For every
+ * piece element: copy the gradient into grad_shard, dequantise the moments
+ * with the block's stored scales, update the Adam moments, update master
+ * with decoupled weight decay and bias correction for step `step` (>= 1),
+ * write param_shard = bf16_rne(master); then requantise each block's fresh
+ * moments with a new absmax scale (scale = amax/127, code =
+ * clamp(rint(x*127/amax), -127, 127); amax 0 gives scale 0 and code 0).
+ * Padding of grad_shard and param_shard is written 0; master and the codes
+ * at padding are not touched. */
+ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_shard_state* states,
+                                 int32_t n_states, const ve_adam_hparams* hp, int64_t step,
+                                 void* stream);
+
+/* Zero-copy extraction (talk notes, "3. DBuffer"; Korean summary, "2.3"):
+ * where tensor `tensor`'s piece on `rank` sits (host outputs).  rank == -1
+ * refers to the whole bucket (shard_offset = offset, [0, numel)).  If the
+ * rank holds none of the tensor: *shard_offset = -1, *elem_start =
+ * *elem_end = 0 and VE_OK. */
+ve_status ve_dbuffer_slice(const ve_plan* plan, int32_t rank, int32_t tensor,
+                           int64_t* shard_offset, int64_t* elem_start, int64_t* elem_end);
+
+/* Thread-local message of this thread's last failing call ("" if none). */
+const char* ve_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VE_H */

@@ -74,11 +74,19 @@ class OracleError(RuntimeError):
     pass
 
 
+_spec_cache: dict = {}
+
+
 def _specs(spec: np.ndarray):
     spec = np.ascontiguousarray(spec, dtype=np.int64).reshape(-1, 5)
-    arr = (_Tensor * max(1, len(spec)))()
-    for i, row in enumerate(spec):
-        arr[i] = _Tensor(*[int(v) for v in row])
+    key = spec.tobytes()
+    hit = _spec_cache.get(key)
+    if hit is not None:
+        return hit
+    arr = (_Tensor * max(1, len(spec))).from_buffer_copy(spec.tobytes() if len(spec) else bytes(40))
+    if len(_spec_cache) > 64:
+        _spec_cache.clear()
+    _spec_cache[key] = (arr, len(spec))
     return arr, len(spec)
 
 

@@ -1,0 +1,262 @@
+"""Python binding of libve, the MI355X RaggedShard shard-step library.
+
+Argument marshalling only: every step of the hot path runs in the HIP
+kernels behind the C ABI in ``include/ve.h``.  PyTorch supplies device memory
+and streams.  Importing this module fails loudly when the library has not
+been built (``python -m ragged_shard_optimizer_amd.build``); there is no
+fallback implementation.
+
+Names follow the C ABI: ``plan_load`` / ``Plan.query`` / ``Plan.slice`` /
+``Plan.copy_in`` / ``Plan.step`` wrap ``ve_plan_load``, ``ve_plan_query``,
+``ve_dbuffer_slice``, ``ve_dbuffer_copy_in`` and ``ve_shard_adam8bit_step``.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "libve.so")
+
+VE_OK, VE_ERR_INVALID_ARG, VE_ERR_LAYOUT, VE_ERR_OOM, VE_ERR_DEVICE, VE_ERR_UNSUPPORTED = range(6)
+_STATUS = {0: "VE_OK", 1: "VE_ERR_INVALID_ARG", 2: "VE_ERR_LAYOUT", 3: "VE_ERR_OOM",
+           4: "VE_ERR_DEVICE", 5: "VE_ERR_UNSUPPORTED"}
+
+# every symbol include/ve.h declares
+EXPORTS = ("ve_plan_load", "ve_plan_free", "ve_plan_query", "ve_dbuffer_copy_in",
+           "ve_shard_adam8bit_step", "ve_dbuffer_slice", "ve_last_error")
+
+
+class VeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class TensorSpec(C.Structure):
+    _fields_ = [("rows", C.c_int64), ("cols", C.c_int64), ("block_rows", C.c_int64),
+                ("block_cols", C.c_int64), ("offset", C.c_int64)]
+
+
+class AdamHParams(C.Structure):
+    _fields_ = [("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
+                ("weight_decay", C.c_float)]
+
+
+# ve_shard_state: eight device pointers, in this order
+STATE_FIELDS = ("grad_ptrs", "grad_shard", "master", "m_q", "v_q", "m_scale", "v_scale", "param_shard")
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libve.so is not built ({LIB_PATH}); run "
+                              "`python -m ragged_shard_optimizer_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        P = C.c_void_p
+        L.ve_last_error.restype = C.c_char_p
+        L.ve_plan_load.argtypes = [P, C.c_int32, C.c_int32, C.c_int64, C.c_int32, C.POINTER(C.c_void_p)]
+        L.ve_plan_free.argtypes = [P]
+        L.ve_plan_query.argtypes = [P, C.c_int32, P, P, P]
+        L.ve_dbuffer_copy_in.argtypes = [P, C.c_int32, P, P, P]
+        L.ve_shard_adam8bit_step.argtypes = [P, C.c_int32, P, C.c_int32, P, C.c_int64, P]
+        L.ve_dbuffer_slice.argtypes = [P, C.c_int32, C.c_int32, P, P, P]
+        for name in EXPORTS[:-1]:
+            getattr(L, name).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != VE_OK:
+        raise VeError(rc, lib().ve_last_error().decode())
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return C.c_void_p(stream)
+    return C.c_void_p(stream.cuda_stream)
+
+
+class Plan:
+    """A validated bucket layout (``ve_plan_load``).
+
+    ``specs``: int64 array ``[n, 5]`` of (rows, cols, block_rows, block_cols,
+    offset); ``device`` -1 gives a host-only plan (layout queries only).
+    """
+
+    def __init__(self, specs, fsdp_size: int, shard_elems: int, device: int = 0):
+        spec = np.ascontiguousarray(specs, dtype=np.int64).reshape(-1, 5)
+        arr = (TensorSpec * max(1, len(spec)))()
+        for i, row in enumerate(spec):
+            arr[i] = TensorSpec(*[int(v) for v in row])
+        h = C.c_void_p()
+        _check(lib().ve_plan_load(arr, len(spec), int(fsdp_size), int(shard_elems), int(device), C.byref(h)))
+        self._h = h
+        self.n_tensors = len(spec)
+        self.fsdp_size = int(fsdp_size)
+        self.shard_elems = int(shard_elems)
+        self.device = int(device)
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            _check(lib().ve_plan_free(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self):
+        return self._h
+
+    def query(self, rank: int):
+        """(valid_elems, n_blocks, n_segments) of ``rank``."""
+        v, b, s = C.c_int64(), C.c_int64(), C.c_int32()
+        _check(lib().ve_plan_query(self._h, int(rank), C.byref(v), C.byref(b), C.byref(s)))
+        return v.value, b.value, s.value
+
+    def slice(self, rank: int, tensor: int):
+        """(shard_offset, elem_start, elem_end), or None if ``rank`` holds none of it."""
+        o, a, b = C.c_int64(), C.c_int64(), C.c_int64()
+        _check(lib().ve_dbuffer_slice(self._h, int(rank), int(tensor), C.byref(o), C.byref(a), C.byref(b)))
+        return None if o.value < 0 else (o.value, a.value, b.value)
+
+    def copy_in(self, rank: int, grad_table, bucket, stream=None):
+        """``ve_dbuffer_copy_in``: ``grad_table`` from :func:`grad_pointer_table`,
+        ``bucket`` a contiguous 16-bit device tensor of S (or m*S for rank -1)
+        elements."""
+        need = self.shard_elems * (self.fsdp_size if rank < 0 else 1)
+        _require_buffer(bucket, need, 2, "bucket")
+        if len(grad_table.grads) != self.n_tensors:
+            raise ValueError("grad table length != number of tensors in the plan")
+        for k in range(self.n_tensors):
+            sl = self.slice(rank, k)
+            g = grad_table.grads[k]
+            if sl is not None and (g is None or g.numel() < sl[2]):
+                raise ValueError(f"tensor {k} is copied on rank {rank} but its gradient is missing or short")
+        _check(lib().ve_dbuffer_copy_in(self._h, int(rank), C.c_void_p(grad_table.table.data_ptr()),
+                                        C.c_void_p(bucket.data_ptr()), _stream_handle(stream)))
+
+    def step(self, rank: int, states, hparams: dict, step: int, stream=None):
+        """``ve_shard_adam8bit_step`` over a :class:`StateTable`."""
+        hp = AdamHParams(float(hparams["lr"]), float(hparams["beta1"]), float(hparams["beta2"]),
+                         float(hparams["eps"]), float(hparams["weight_decay"]))
+        _check(lib().ve_shard_adam8bit_step(self._h, int(rank), C.c_void_p(states.table.data_ptr()),
+                                            len(states), C.byref(hp), int(step), _stream_handle(stream)))
+
+
+def plan_load(specs, fsdp_size, shard_elems, device=0) -> Plan:
+    return Plan(specs, fsdp_size, shard_elems, device)
+
+
+def _require_buffer(t, numel: int, itemsize: int, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous() or t.element_size() != itemsize:
+        raise ValueError(f"{name}: need a contiguous tensor of {itemsize}-byte elements")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements < required {numel}")
+
+
+class GradTable:
+    """Device array of per-parameter gradient pointers (``grad_ptrs``).
+    Keeps the tensors alive while the table exists."""
+
+    def __init__(self, grads, device):
+        import torch
+        ptrs = []
+        for g in grads:
+            if g is None:
+                ptrs.append(0)
+                continue
+            if not g.is_cuda or not g.is_contiguous() or g.element_size() != 2:
+                raise ValueError("gradients must be contiguous 16-bit device tensors")
+            ptrs.append(g.data_ptr())
+        self.grads = list(grads)
+        self.table = torch.tensor(ptrs if ptrs else [0], dtype=torch.int64, device=device)
+
+
+def grad_pointer_table(grads, device=None) -> GradTable:
+    """Per-tensor bf16 gradient tensors (flat or shaped, contiguous; None for
+    tensors the call never reads), in the plan's tensor order."""
+    if device is None:
+        device = next(g.device for g in grads if g is not None)
+    return GradTable(grads, device)
+
+
+class StateTable:
+    """Device array of ``ve_shard_state`` records (one per bucket)."""
+
+    def __init__(self, plan: Plan, rank: int, states, device):
+        import torch
+        S = plan.shard_elems
+        _, nb, _ = plan.query(rank)
+        rows = []
+        self.keep = []
+        for st in states:
+            gt = st["grad_table"]
+            if len(gt.grads) != plan.n_tensors:
+                raise ValueError("grad table length != number of tensors in the plan")
+            for k in range(plan.n_tensors):
+                if plan.slice(rank, k) is not None and gt.grads[k] is None:
+                    raise ValueError(f"tensor {k} has a piece on rank {rank} but no gradient")
+                if gt.grads[k] is not None and gt.grads[k].numel() < self._numel(plan, k):
+                    raise ValueError(f"gradient {k} is smaller than the tensor")
+            _require_buffer(st["grad_shard"], S, 2, "grad_shard")
+            _require_buffer(st["master"], S, 4, "master")
+            _require_buffer(st["m_q"], S, 1, "m_q")
+            _require_buffer(st["v_q"], S, 1, "v_q")
+            _require_buffer(st["m_scale"], nb, 4, "m_scale")
+            _require_buffer(st["v_scale"], nb, 4, "v_scale")
+            _require_buffer(st["param_shard"], S, 2, "param_shard")
+            rows.append([gt.table.data_ptr()] + [st[f].data_ptr() for f in STATE_FIELDS[1:]])
+            self.keep.append(st)
+        self.table = torch.tensor(rows, dtype=torch.int64, device=device).reshape(-1)
+        self.n = len(rows)
+
+    @staticmethod
+    def _numel(plan, k):
+        off, lo, hi = plan.slice(-1, k)
+        return hi
+
+    def __len__(self):
+        return self.n
+
+
+def state_table(plan: Plan, rank: int, states, device=None) -> StateTable:
+    """``states``: list of dicts with keys ``grad_table`` (a GradTable) and
+    grad_shard, master, m_q, v_q, m_scale, v_scale, param_shard (device
+    tensors)."""
+    if device is None:
+        device = states[0]["master"].device
+    return StateTable(plan, rank, states, device)
+
+
+def new_state(plan: Plan, rank: int, grad_table: GradTable, master, device=None) -> dict:
+    """Allocate one bucket's state around an fp32 master shard (codes and
+    scales zero, outputs zero)."""
+    import torch
+    device = device or master.device
+    S = plan.shard_elems
+    _, nb, _ = plan.query(rank)
+    return dict(grad_table=grad_table,
+                grad_shard=torch.zeros(S, dtype=torch.int16, device=device),
+                master=master,
+                m_q=torch.zeros(S, dtype=torch.int8, device=device),
+                v_q=torch.zeros(S, dtype=torch.int8, device=device),
+                m_scale=torch.zeros(max(nb, 1), dtype=torch.float32, device=device),
+                v_scale=torch.zeros(max(nb, 1), dtype=torch.float32, device=device),
+                param_shard=torch.zeros(S, dtype=torch.int16, device=device))

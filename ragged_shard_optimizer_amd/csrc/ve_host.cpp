@@ -1,0 +1,507 @@
+// ve_host.cpp -- host side of libve: layout validation, per-rank segment and
+// run tables, and the C entry points declared in include/ve.h.
+//
+// A plan is built once per bucket layout (the planner runs once at
+// initialisation; veScale-FSDP talk notes, "2. Structure-aware planning").
+// For every rank it derives the pieces ("segments") of the tensors that fall
+// in the rank's chunk, the rank-local block numbering, the block-size class
+// of each segment, and the copy / padding runs, and uploads all of it to the
+// device in one allocation.  Entry points afterwards only launch kernels.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "ve.h"
+#include "ve_internal.h"
+
+using namespace ve;
+
+namespace {
+
+thread_local std::string g_err;
+
+ve_status fail(ve_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+// host-side copies of one work list / run table, with byte offsets into the
+// single device allocation filled in at upload
+struct HostWork {
+    std::vector<int32_t> seg_idx;
+    std::vector<int64_t> prefix{0};
+    size_t off_idx = 0, off_pref = 0;
+};
+
+struct HostRuns {
+    std::vector<Run> runs;
+    std::vector<int64_t> tile_prefix{0};
+    std::vector<int32_t> tile_run;
+    size_t off_runs = 0, off_pref = 0, off_tiles = 0;
+    int64_t zero_elems = 0;
+};
+
+struct RankTables {
+    std::vector<Seg> segs;
+    size_t off_segs = 0;
+    HostWork small, wg, huge;
+    int32_t wg_max_chunks = 0;
+    HostRuns copy;  // pieces + padding of the rank slice
+    HostRuns pad;   // padding only (the step's zero fill)
+    int64_t valid = 0, nblocks = 0;
+};
+
+void add_run(HostRuns& h, int64_t dst, int64_t src, int64_t len, int32_t tensor) {
+    if (len <= 0) return;
+    Run r{dst, src, len, tensor, 0};
+    const int32_t ri = (int32_t)h.runs.size();
+    h.runs.push_back(r);
+    const int64_t tiles = (len + kRunTile - 1) / kRunTile;
+    h.tile_prefix.push_back(h.tile_prefix.back() + tiles);
+    for (int64_t t = 0; t < tiles; ++t) h.tile_run.push_back(ri);
+    if (tensor < 0) h.zero_elems += len;
+}
+
+int32_t next_pow2(int32_t x) {
+    int32_t g = 1;
+    while (g < x) g <<= 1;
+    return g;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+struct ve_plan {
+    int device = 0;
+    int32_t m = 0;
+    int64_t S = 0;
+    std::vector<ve_tensor_spec> specs;
+    std::vector<int32_t> order;  // tensor indices by ascending offset
+    std::vector<RankTables> ranks;
+    HostRuns whole;              // rank == -1 copy-in
+    char* dev = nullptr;         // one device allocation holding every table
+    size_t dev_bytes = 0;
+
+    template <class T>
+    const T* dptr(size_t off) const { return reinterpret_cast<const T*>(dev + off); }
+};
+
+namespace {
+
+// -------------------------------------------------------------------------
+// validation (the RaggedShard layout rules; talk notes "1. RaggedShard" and
+// "2. Structure-aware planning")
+ve_status validate(const ve_tensor_spec* sp, int32_t n, int32_t m, int64_t S, std::vector<int32_t>& order) {
+    if (n < 0) return fail(VE_ERR_INVALID_ARG, "n_tensors %d < 0", n);
+    if (m < 1) return fail(VE_ERR_INVALID_ARG, "fsdp_size %d < 1", m);
+    if (S < 1) return fail(VE_ERR_INVALID_ARG, "shard_elems %lld < 1", (long long)S);
+    if (S > INT64_MAX / m) return fail(VE_ERR_INVALID_ARG, "bucket size overflows");
+    const int64_t total = S * m;
+    for (int32_t k = 0; k < n; ++k) {
+        const ve_tensor_spec& t = sp[k];
+        if (t.rows < 1 || t.cols < 1 || t.block_rows < 1 || t.block_cols < 1)
+            return fail(VE_ERR_LAYOUT, "tensor %d: shape %lldx%lld / block %lldx%lld must be positive", k,
+                        (long long)t.rows, (long long)t.cols, (long long)t.block_rows, (long long)t.block_cols);
+        if (t.cols % t.block_cols != 0)
+            return fail(VE_ERR_LAYOUT, "tensor %d: block_cols %lld does not divide cols %lld", k,
+                        (long long)t.block_cols, (long long)t.cols);
+        if (t.rows > total / t.cols) return fail(VE_ERR_LAYOUT, "tensor %d: larger than the bucket", k);
+        const int64_t numel = t.rows * t.cols;
+        if (t.offset < 0 || t.offset > total - numel)
+            return fail(VE_ERR_LAYOUT, "tensor %d: elements [%lld, %lld) leave the bucket [0, %lld)", k,
+                        (long long)t.offset, (long long)(t.offset + numel), (long long)total);
+        const int64_t br = std::min(t.block_rows, t.rows);
+        const int64_t block_elems = br * t.block_cols;
+        if (block_elems > (int64_t(1) << 30))
+            return fail(VE_ERR_UNSUPPORTED, "tensor %d: quantisation block of %lld elements exceeds 2^30", k,
+                        (long long)block_elems);
+        if (br > INT32_MAX || t.cols / t.block_cols > INT32_MAX)
+            return fail(VE_ERR_UNSUPPORTED, "tensor %d: block geometry beyond 32-bit counters", k);
+    }
+    order.resize((size_t)n);
+    for (int32_t k = 0; k < n; ++k) order[(size_t)k] = k;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return sp[a].offset < sp[b].offset; });
+    for (int32_t i = 1; i < n; ++i) {
+        const ve_tensor_spec& a = sp[order[(size_t)i - 1]];
+        const ve_tensor_spec& b = sp[order[(size_t)i]];
+        if (a.offset + a.rows * a.cols > b.offset)
+            return fail(VE_ERR_LAYOUT, "tensors %d and %d overlap at bucket offset %lld", order[(size_t)i - 1],
+                        order[(size_t)i], (long long)b.offset);
+    }
+    // every chunk boundary strictly inside a tensor sits on one of its units
+    for (int32_t k = 0; k < n; ++k) {
+        const ve_tensor_spec& t = sp[k];
+        // a block taller than the tensor is the whole tensor (clamped: no overflow)
+        const int64_t numel = t.rows * t.cols, unit = std::min(t.block_rows, t.rows) * t.cols;
+        for (int64_t b = (t.offset / S + 1) * S; b < t.offset + numel; b += S) {
+            if ((b - t.offset) % unit != 0)
+                return fail(VE_ERR_LAYOUT,
+                            "tensor %d: chunk boundary at bucket offset %lld cuts it at element %lld, "
+                            "not a multiple of its unit %lld (block_rows %lld x cols %lld)",
+                            k, (long long)b, (long long)(b - t.offset), (long long)unit, (long long)t.block_rows,
+                            (long long)t.cols);
+        }
+    }
+    return VE_OK;
+}
+
+void build_rank(ve_plan& P, int32_t r, RankTables& rt) {
+    const int64_t c0 = (int64_t)r * P.S, c1 = c0 + P.S;
+    int64_t cursor = 0;  // shard coordinate covered so far (for padding runs)
+    int64_t block0 = 0;
+    for (int32_t k : P.order) {
+        const ve_tensor_spec& t = P.specs[(size_t)k];
+        const int64_t numel = t.rows * t.cols;
+        const int64_t a = std::max(t.offset, c0), b = std::min(t.offset + numel, c1);
+        if (a >= b) continue;
+        Seg s{};
+        s.shard_base = t.offset - c0;
+        s.elem_lo = a - t.offset;
+        s.elem_hi = b - t.offset;
+        s.rows = t.rows;
+        s.cols = t.cols;
+        s.block_rows = std::min(t.block_rows, t.rows);
+        s.block_cols = t.block_cols;
+        const int64_t unit = s.block_rows * t.cols;
+        s.panel0 = s.elem_lo / unit;
+        const int64_t panels = ceil_div(s.elem_hi, unit) - s.panel0;
+        s.tiles = (int32_t)(t.cols / t.block_cols);
+        s.nblocks = panels * s.tiles;
+        s.block0 = block0;
+        s.tensor = k;
+        const int64_t br = std::min(t.block_rows, t.rows);
+        int64_t chunks;
+        if (s.tiles == 1) chunks = ceil_div(br * t.cols, kChunk);
+        else chunks = br * ceil_div(t.block_cols, kChunk);
+        s.max_chunks = (int32_t)std::min<int64_t>(chunks, INT32_MAX);
+        if (chunks <= kSmallMaxChunks) {
+            s.cls = kSmall;
+            s.group = next_pow2((int32_t)chunks);
+        } else if (chunks <= (int64_t)kWgMaxChunksPerThread * kWgMaxThreads) {
+            s.cls = kWg;
+            s.group = 0;
+        } else {
+            s.cls = kHuge;
+            s.group = 0;
+        }
+        const int32_t si = (int32_t)rt.segs.size();
+        rt.segs.push_back(s);
+        block0 += s.nblocks;
+        rt.valid += s.elem_hi - s.elem_lo;
+        HostWork& w = s.cls == kSmall ? rt.small : (s.cls == kWg ? rt.wg : rt.huge);
+        const int64_t items = s.cls == kSmall ? ceil_div(s.nblocks, 64 / s.group) : s.nblocks;
+        w.seg_idx.push_back(si);
+        w.prefix.push_back(w.prefix.back() + items);
+        if (s.cls == kWg) rt.wg_max_chunks = std::max(rt.wg_max_chunks, s.max_chunks);
+        const int64_t dst = a - c0;
+        add_run(rt.copy, cursor, 0, dst - cursor, -1);
+        add_run(rt.pad, cursor, 0, dst - cursor, -1);
+        add_run(rt.copy, dst, s.elem_lo, b - a, k);
+        cursor = b - c0;
+    }
+    add_run(rt.copy, cursor, 0, P.S - cursor, -1);
+    add_run(rt.pad, cursor, 0, P.S - cursor, -1);
+    rt.nblocks = block0;
+}
+
+void build_whole(ve_plan& P) {
+    int64_t cursor = 0;
+    for (int32_t k : P.order) {
+        const ve_tensor_spec& t = P.specs[(size_t)k];
+        add_run(P.whole, cursor, 0, t.offset - cursor, -1);
+        add_run(P.whole, t.offset, 0, t.rows * t.cols, k);
+        cursor = t.offset + t.rows * t.cols;
+    }
+    add_run(P.whole, cursor, 0, P.S * P.m - cursor, -1);
+}
+
+// layout of the single device allocation
+struct Packer {
+    std::vector<char> buf;
+    template <class T>
+    size_t put(const std::vector<T>& v) {
+        size_t off = (buf.size() + 255) & ~size_t(255);
+        buf.resize(off + sizeof(T) * v.size());
+        if (!v.empty()) std::memcpy(buf.data() + off, v.data(), sizeof(T) * v.size());
+        return off;
+    }
+};
+
+void pack_runs(Packer& pk, HostRuns& h) {
+    h.off_runs = pk.put(h.runs);
+    h.off_pref = pk.put(h.tile_prefix);
+    h.off_tiles = pk.put(h.tile_run);
+}
+
+void pack_work(Packer& pk, HostWork& w) {
+    w.off_idx = pk.put(w.seg_idx);
+    w.off_pref = pk.put(w.prefix);
+}
+
+RunArgs run_args(const ve_plan& P, const HostRuns& h) {
+    RunArgs r;
+    r.runs = P.dptr<Run>(h.off_runs);
+    r.tile_prefix = P.dptr<int64_t>(h.off_pref);
+    r.tile_run = P.dptr<int32_t>(h.off_tiles);
+    r.n_runs = (int32_t)h.runs.size();
+    r.n_tiles = h.tile_prefix.back();
+    return r;
+}
+
+WorkList work_list(const ve_plan& P, const HostWork& w) {
+    WorkList l;
+    l.seg_idx = P.dptr<int32_t>(w.off_idx);
+    l.prefix = P.dptr<int64_t>(w.off_pref);
+    l.n = (int32_t)w.seg_idx.size();
+    l.total = w.prefix.back();
+    return l;
+}
+
+// Workgroup path shape: threads and chunks per thread for blocks of up to
+// `chunks` chunks.  Overridable for tuning with VE_WG_THREADS / VE_WG_CPT.
+void wg_shape(int32_t chunks, int& threads, int& cpt) {
+    const char* et = std::getenv("VE_WG_THREADS");
+    const char* ec = std::getenv("VE_WG_CPT");
+    if (et && ec) {
+        threads = std::atoi(et);
+        cpt = std::atoi(ec);
+        if (wg_config_supported(threads, cpt) && (int64_t)threads * cpt >= chunks) return;
+    }
+    // fewest threads (of 256/512/1024) with at most 8 chunks each; 12 if the block needs it
+    for (int t : {256, 512, 1024}) {
+        const int c = (int)ceil_div(chunks, t);
+        if (c <= 8) {
+            threads = t;
+            cpt = c;
+            return;
+        }
+    }
+    threads = 1024;
+    cpt = (int)ceil_div(chunks, 1024);
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = false;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+ve_status launch_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return VE_OK;
+    return fail(VE_ERR_DEVICE, "%s launch failed: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+extern "C" {
+
+const char* ve_last_error(void) { return g_err.c_str(); }
+
+ve_status ve_plan_load(const ve_tensor_spec* specs, int32_t n_tensors, int32_t fsdp_size, int64_t shard_elems,
+                       int32_t device, ve_plan** out) {
+    try {
+        if (!out) return fail(VE_ERR_INVALID_ARG, "out is NULL");
+        *out = nullptr;
+        if (n_tensors > 0 && !specs) return fail(VE_ERR_INVALID_ARG, "specs is NULL");
+        int ndev = 0;
+        if (device != -1 && (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev))
+            return fail(VE_ERR_INVALID_ARG, "device %d not available (%d devices)", device, ndev);
+        auto P = new ve_plan();
+        P->device = device;
+        P->m = fsdp_size;
+        P->S = shard_elems;
+        P->specs.assign(specs, specs + (n_tensors > 0 ? n_tensors : 0));
+        ve_status st = validate(P->specs.data(), n_tensors, fsdp_size, shard_elems, P->order);
+        if (st != VE_OK) {
+            delete P;
+            return st;
+        }
+        P->ranks.resize((size_t)fsdp_size);
+        for (int32_t r = 0; r < fsdp_size; ++r) build_rank(*P, r, P->ranks[(size_t)r]);
+        build_whole(*P);
+        Packer pk;
+        for (auto& rt : P->ranks) {
+            rt.off_segs = pk.put(rt.segs);
+            pack_work(pk, rt.small);
+            pack_work(pk, rt.wg);
+            pack_work(pk, rt.huge);
+            pack_runs(pk, rt.copy);
+            pack_runs(pk, rt.pad);
+        }
+        pack_runs(pk, P->whole);
+        P->dev_bytes = std::max<size_t>(pk.buf.size(), 256);
+        if (device == -1) {  // host-only plan: layout queries, no kernels
+            *out = P;
+            return VE_OK;
+        }
+        DeviceGuard g(device);
+        if (!g.ok) {
+            delete P;
+            return fail(VE_ERR_DEVICE, "hipSetDevice(%d) failed", device);
+        }
+        if (hipMalloc((void**)&P->dev, P->dev_bytes) != hipSuccess) {
+            delete P;
+            return fail(VE_ERR_OOM, "hipMalloc of %zu bytes of plan tables failed", pk.buf.size());
+        }
+        if (!pk.buf.empty() && hipMemcpy(P->dev, pk.buf.data(), pk.buf.size(), hipMemcpyHostToDevice) != hipSuccess) {
+            (void)hipFree(P->dev);
+            delete P;
+            return fail(VE_ERR_DEVICE, "upload of plan tables failed");
+        }
+        *out = P;
+        return VE_OK;
+    } catch (const std::bad_alloc&) {
+        return fail(VE_ERR_OOM, "host allocation failed while building the plan");
+    } catch (...) {
+        return fail(VE_ERR_DEVICE, "unexpected host exception in ve_plan_load");
+    }
+}
+
+ve_status ve_plan_free(ve_plan* plan) {
+    if (!plan) return VE_OK;
+    ve_status st = VE_OK;
+    if (plan->dev && plan->device >= 0) {
+        DeviceGuard g(plan->device);
+        if (hipFree(plan->dev) != hipSuccess) st = fail(VE_ERR_DEVICE, "hipFree of plan tables failed");
+    }
+    delete plan;
+    return st;
+}
+
+ve_status ve_plan_query(const ve_plan* plan, int32_t rank, int64_t* valid_elems, int64_t* n_blocks,
+                        int32_t* n_segments) {
+    if (!plan) return fail(VE_ERR_INVALID_ARG, "plan is NULL");
+    if (rank < 0 || rank >= plan->m) return fail(VE_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, plan->m);
+    const RankTables& rt = plan->ranks[(size_t)rank];
+    if (valid_elems) *valid_elems = rt.valid;
+    if (n_blocks) *n_blocks = rt.nblocks;
+    if (n_segments) *n_segments = (int32_t)rt.segs.size();
+    return VE_OK;
+}
+
+ve_status ve_dbuffer_slice(const ve_plan* plan, int32_t rank, int32_t tensor, int64_t* shard_offset,
+                           int64_t* elem_start, int64_t* elem_end) {
+    if (!plan) return fail(VE_ERR_INVALID_ARG, "plan is NULL");
+    if (!shard_offset || !elem_start || !elem_end) return fail(VE_ERR_INVALID_ARG, "output pointer is NULL");
+    if (rank < -1 || rank >= plan->m) return fail(VE_ERR_INVALID_ARG, "rank %d outside [-1, %d)", rank, plan->m);
+    if (tensor < 0 || tensor >= (int32_t)plan->specs.size())
+        return fail(VE_ERR_INVALID_ARG, "tensor %d outside [0, %zu)", tensor, plan->specs.size());
+    const ve_tensor_spec& t = plan->specs[(size_t)tensor];
+    const int64_t numel = t.rows * t.cols;
+    if (rank < 0) {
+        *shard_offset = t.offset;
+        *elem_start = 0;
+        *elem_end = numel;
+        return VE_OK;
+    }
+    const int64_t c0 = (int64_t)rank * plan->S;
+    const int64_t a = std::max(t.offset, c0), b = std::min(t.offset + numel, c0 + plan->S);
+    if (a >= b) {
+        *shard_offset = -1;
+        *elem_start = *elem_end = 0;
+    } else {
+        *shard_offset = a - c0;
+        *elem_start = a - t.offset;
+        *elem_end = b - t.offset;
+    }
+    return VE_OK;
+}
+
+ve_status ve_dbuffer_copy_in(const ve_plan* plan, int32_t rank, const uint16_t* const* grad_ptrs, uint16_t* bucket,
+                             void* stream) {
+    if (!plan) return fail(VE_ERR_INVALID_ARG, "plan is NULL");
+    if (rank < -1 || rank >= plan->m) return fail(VE_ERR_INVALID_ARG, "rank %d outside [-1, %d)", rank, plan->m);
+    if (!bucket) return fail(VE_ERR_INVALID_ARG, "bucket is NULL");
+    if (!plan->dev) return fail(VE_ERR_INVALID_ARG, "host-only plan (device -1) cannot launch kernels");
+    const HostRuns& h = rank < 0 ? plan->whole : plan->ranks[(size_t)rank].copy;
+    bool needs_grads = false;
+    for (const Run& r : h.runs) needs_grads |= r.tensor >= 0;
+    if (needs_grads && !grad_ptrs) return fail(VE_ERR_INVALID_ARG, "grad_ptrs is NULL");
+    if (h.tile_prefix.back() == 0) return VE_OK;
+    if (h.tile_prefix.back() > INT32_MAX) return fail(VE_ERR_UNSUPPORTED, "copy of more than 2^31 tiles");
+    DeviceGuard g(plan->device);
+    if (!g.ok) return fail(VE_ERR_DEVICE, "hipSetDevice(%d) failed", plan->device);
+    (void)hipGetLastError();
+    return launch_status(launch_runs_copy(run_args(*plan, h), grad_ptrs, bucket, (hipStream_t)stream), "copy-in");
+}
+
+ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_shard_state* states, int32_t n_states,
+                                 const ve_adam_hparams* hp, int64_t step, void* stream) {
+    if (!plan) return fail(VE_ERR_INVALID_ARG, "plan is NULL");
+    if (rank < 0 || rank >= plan->m) return fail(VE_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, plan->m);
+    if (!states) return fail(VE_ERR_INVALID_ARG, "states is NULL");
+    if (n_states < 1 || n_states > 65535) return fail(VE_ERR_INVALID_ARG, "n_states %d outside [1, 65535]", n_states);
+    if (!hp) return fail(VE_ERR_INVALID_ARG, "hparams is NULL");
+    if (step < 1) return fail(VE_ERR_INVALID_ARG, "step %lld < 1", (long long)step);
+    if (!(hp->beta1 >= 0.f && hp->beta1 < 1.f) || !(hp->beta2 >= 0.f && hp->beta2 < 1.f))
+        return fail(VE_ERR_INVALID_ARG, "betas (%g, %g) outside [0, 1)", (double)hp->beta1, (double)hp->beta2);
+    if (!std::isfinite(hp->lr) || !std::isfinite(hp->eps) || !std::isfinite(hp->weight_decay) || hp->eps <= 0.f)
+        return fail(VE_ERR_INVALID_ARG, "lr / eps / weight_decay must be finite and eps > 0");
+    if (!plan->dev) return fail(VE_ERR_INVALID_ARG, "host-only plan (device -1) cannot launch kernels");
+    const RankTables& rt = plan->ranks[(size_t)rank];
+    for (const HostWork* w : {&rt.small, &rt.wg, &rt.huge})
+        if (w->prefix.back() > INT32_MAX) return fail(VE_ERR_UNSUPPORTED, "more than 2^31 work items on rank %d", rank);
+
+    StepArgs a{};
+    a.states = states;
+    a.segs = plan->dptr<Seg>(rt.off_segs);
+    const double b1 = hp->beta1, b2 = hp->beta2, lr = hp->lr;
+    a.sc.beta1 = hp->beta1;
+    a.sc.beta2 = hp->beta2;
+    a.sc.omb1 = 1.0f - hp->beta1;  // exact: Sterbenz for beta in [0.5, 1); rounded once otherwise
+    a.sc.omb2 = 1.0f - hp->beta2;
+    a.sc.step_size = (float)(lr / (1.0 - std::pow(b1, (double)step)));
+    a.sc.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(1.0 - std::pow(b2, (double)step)));
+    a.sc.eps = hp->eps;
+    a.sc.decay = (float)(1.0 - lr * (double)hp->weight_decay);
+
+    DeviceGuard g(plan->device);
+    if (!g.ok) return fail(VE_ERR_DEVICE, "hipSetDevice(%d) failed", plan->device);
+    (void)hipGetLastError();
+    hipStream_t s = (hipStream_t)stream;
+    ve_status st;
+    if (rt.wg.prefix.back() > 0) {
+        int threads, cpt;
+        wg_shape(rt.wg_max_chunks, threads, cpt);
+        a.work = work_list(*plan, rt.wg);
+        if ((st = launch_status(launch_step_wg(a, n_states, threads, cpt, s), "workgroup step")) != VE_OK) return st;
+    }
+    if (rt.small.prefix.back() > 0) {
+        a.work = work_list(*plan, rt.small);
+        if ((st = launch_status(launch_step_small(a, n_states, s), "small-block step")) != VE_OK) return st;
+    }
+    if (rt.huge.prefix.back() > 0) {
+        a.work = work_list(*plan, rt.huge);
+        if ((st = launch_status(launch_step_huge(a, n_states, s), "large-block step")) != VE_OK) return st;
+    }
+    if (rt.pad.tile_prefix.back() > 0) {
+        if ((st = launch_status(launch_runs_pad(run_args(*plan, rt.pad), states, n_states, s), "padding fill")) != VE_OK)
+            return st;
+    }
+    return VE_OK;
+}
+
+}  // extern "C"

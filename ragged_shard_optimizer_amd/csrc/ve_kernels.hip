@@ -1,0 +1,654 @@
+// ve_kernels.hip -- gfx950 kernels of the RaggedShard shard step.
+//
+// Per element the step streams 18 bytes through HBM (bf16 gradient read and
+// copy-in write, fp32 master read+write, two int8 codes read+write, bf16
+// parameter write) and does ~60 VALU operations, so it is bandwidth-bound;
+// nothing here is a dense contraction and no MFMA is used.
+//
+// The one non-local step is the block absmax: every quantisation block's new
+// codes need the maximum of its *fresh* moments (veScale-FSDP talk notes,
+// "1. RaggedShard": one scale per block, and a block never straddles ranks,
+// so the reduction never leaves the GPU).  To keep the HBM traffic at the
+// algorithmic 18 B/element, a block's inputs (bf16 gradient + both int8
+// codes = exactly one dword per element) stay in VGPRs across the reduction
+// and the moments are recomputed from them afterwards:
+//
+//   phase 1  load inputs (+ master), compute moments, update master, write
+//            master / bf16 param / gradient copy, running absmax;
+//   reduce   DPP / ds_swizzle inside a wave, LDS across waves;
+//   phase 2  recompute the moments from the registers, quantise with the new
+//            scale, write the codes.
+//
+// Block-size classes (decided per rank segment at plan load):
+//   small  <= 64 chunks of 16 elements: a group of G (power of two) lanes of
+//          one wave owns a block, 64/G blocks per wave (1-, 16-, 128-element
+//          blocks of ragged buckets);
+//   wg     one workgroup owns a block, CPT chunks per thread held in VGPRs
+//          (row blocks of 8K..46K elements, 128x128 tiles);
+//   huge   one workgroup, two passes (inputs re-read) for blocks too large to
+//          hold on chip.
+// Runs (copy-in, padding zero-fill) are plain tiled copies.
+//
+// Floating point: fp32 with fused multiply-adds, hardware sqrt/reciprocal
+// (about 1 ulp) in the weight update, correctly rounded 127/amax per block,
+// round-half-even for codes and bf16.  The moment formulas are written once
+// (moments()) and the compiler is kept from contracting differently, so the
+// recomputed moments equal the ones whose maximum was taken.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ve_internal.h"
+
+namespace ve {
+namespace {
+
+// ---------------------------------------------------------------------------
+// scalar helpers
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float code_at(uint32_t w, int b) {
+    return (float)((int32_t)(w << (24 - 8 * b)) >> 24);  // sign-extended byte b
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    f32x2 v = {a, b};
+    bf16x2 h = __builtin_convertvector(v, bf16x2);  // v_cvt_pk_bf16_f32, RNE
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// Keep the compiler from proving a value equal to an earlier one (forces the
+// moments to be recomputed from registers instead of kept alive).
+__device__ __forceinline__ void opaque(uint32_t& x) { asm volatile("" : "+v"(x)); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xb1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4e;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+__device__ __forceinline__ float swz_xor16(float v) {
+    // ds_swizzle bit-mask mode: and 0x1f, or 0, xor 0x10 (within 32 lanes)
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401f));
+}
+
+// Maximum over aligned groups of G lanes (G a power of two <= 64, wave-
+// uniform); every lane of a group receives the group maximum.  Values are
+// non-negative.
+__device__ __forceinline__ float group_max(float v, int G) {
+    if (G > 1) v = fmaxf(v, dpp<kQuadXor1>(v));
+    if (G > 2) v = fmaxf(v, dpp<kQuadXor2>(v));
+    if (G > 4) v = fmaxf(v, dpp<kRowHalfMirror>(v));  // lane i <-> 7-i: the other quad
+    if (G > 8) v = fmaxf(v, dpp<kRowMirror>(v));      // lane i <-> 15-i: the other half-row
+    if (G > 16) v = fmaxf(v, swz_xor16(v));
+    if (G > 32) v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+// Wave maximum, returned as a wave-uniform value.
+__device__ __forceinline__ float wave_max(float v) {
+    v = group_max(v, 32);
+    const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    return fmaxf(lo, hi);
+}
+
+// ---------------------------------------------------------------------------
+// block and chunk geometry
+struct Geo {
+    int64_t e0;      // tensor element of the block's first element
+    int64_t stride;  // tensor elements between consecutive runs (rows of a tile)
+    int32_t run;     // contiguous elements per run
+    int32_t nruns;
+    int32_t cpr;     // chunks per run
+    int32_t nchunks;
+    int64_t blk;     // rank-local block index (scale slot)
+};
+
+__device__ __forceinline__ Geo block_geo(const Seg& sg, int64_t k) {
+    Geo g;
+    const int64_t q = k / sg.tiles;
+    const int64_t j = k - q * sg.tiles;
+    const int64_t r0 = (sg.panel0 + q) * sg.block_rows;
+    const int64_t rows_in = min(sg.block_rows, sg.rows - r0);
+    if (sg.tiles == 1) {  // whole-row blocks: one contiguous run
+        g.e0 = r0 * sg.cols;
+        g.run = (int32_t)(rows_in * sg.cols);
+        g.nruns = 1;
+        g.stride = 0;
+    } else {              // a tile: rows_in runs of block_cols, row stride cols
+        g.e0 = r0 * sg.cols + j * sg.block_cols;
+        g.run = (int32_t)sg.block_cols;
+        g.nruns = (int32_t)rows_in;
+        g.stride = sg.cols;
+    }
+    g.cpr = (g.run + kChunk - 1) / kChunk;
+    g.nchunks = g.nruns * g.cpr;
+    g.blk = sg.block0 + k;
+    return g;
+}
+
+struct ChunkPos {
+    int64_t e;  // tensor element of the chunk's first element
+    int64_t s;  // shard coordinate of the same element
+    int32_t n;  // valid elements (1..16), contiguous
+};
+
+__device__ __forceinline__ ChunkPos chunk_pos(const Geo& g, int64_t shard_base, int ci) {
+    int ri = 0, w = ci * kChunk;
+    if (g.nruns != 1) {
+        ri = ci / g.cpr;
+        w = (ci - ri * g.cpr) * kChunk;
+    }
+    ChunkPos c;
+    c.e = g.e0 + (int64_t)ri * g.stride + w;
+    c.s = shard_base + c.e;
+    c.n = min(kChunk, g.run - w);
+    return c;
+}
+
+// ---------------------------------------------------------------------------
+// per-chunk data movement and arithmetic
+struct In {
+    uint32_t g[8];  // 16 bf16 gradients
+    uint32_t m[4];  // 16 first-moment codes
+    uint32_t v[4];  // 16 second-moment codes
+};
+
+// Pointers read from the state table are generic; the buffers live in device
+// global memory, so address them as such (global_* instead of flat_* accesses).
+#define VE_GLOBAL __attribute__((address_space(1)))
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct Ptrs {
+    const VE_GLOBAL uint16_t* __restrict__ grad;
+    VE_GLOBAL uint16_t* __restrict__ grad_shard;
+    VE_GLOBAL float* __restrict__ master;
+    VE_GLOBAL int8_t* __restrict__ m_q;
+    VE_GLOBAL int8_t* __restrict__ v_q;
+    VE_GLOBAL uint16_t* __restrict__ param;
+    bool aligned;  // every base pointer 16-byte aligned
+};
+
+__device__ __forceinline__ Ptrs make_ptrs(const ve_shard_state& st, int tensor) {
+    Ptrs p;
+    const uint16_t* g = st.grad_ptrs[tensor];
+    p.aligned = (((uintptr_t)g | (uintptr_t)st.grad_shard | (uintptr_t)st.master | (uintptr_t)st.m_q |
+                  (uintptr_t)st.v_q | (uintptr_t)st.param_shard) & 15) == 0;
+    p.grad = (const VE_GLOBAL uint16_t*)g;
+    p.grad_shard = (VE_GLOBAL uint16_t*)st.grad_shard;
+    p.master = (VE_GLOBAL float*)st.master;
+    p.m_q = (VE_GLOBAL int8_t*)st.m_q;
+    p.v_q = (VE_GLOBAL int8_t*)st.v_q;
+    p.param = (VE_GLOBAL uint16_t*)st.param_shard;
+    return p;
+}
+
+__device__ __forceinline__ bool vec_ok(const Ptrs& p, const ChunkPos& c) {
+    return p.aligned && c.n == kChunk && (c.s & 15) == 0 && (c.e & 7) == 0;
+}
+
+// Both access paths produce plain values and the registers are assigned
+// once afterwards (stores from two branches into one array would otherwise be
+// merged into a store through a selected address, which demotes the array to
+// scratch memory).
+__device__ __forceinline__ void load_in(In& x, const Ptrs& p, const ChunkPos& c, bool vec) {
+    u32x4 g0, g1, m, v;
+    if (vec) {
+        g0 = *(const VE_GLOBAL u32x4*)(p.grad + c.e);
+        g1 = *(const VE_GLOBAL u32x4*)(p.grad + c.e + 8);
+        m = *(const VE_GLOBAL u32x4*)(p.m_q + c.s);
+        v = *(const VE_GLOBAL u32x4*)(p.v_q + c.s);
+    } else {
+        uint32_t gw[8], mw[4], vw[4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t lo = (2 * i < c.n) ? p.grad[c.e + 2 * i] : 0u;
+            const uint32_t hi = (2 * i + 1 < c.n) ? p.grad[c.e + 2 * i + 1] : 0u;
+            gw[i] = lo | (hi << 16);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t a = 0, b = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (4 * i + k < c.n) {
+                    a |= (uint32_t)(uint8_t)p.m_q[c.s + 4 * i + k] << (8 * k);
+                    b |= (uint32_t)(uint8_t)p.v_q[c.s + 4 * i + k] << (8 * k);
+                }
+            }
+            mw[i] = a;
+            vw[i] = b;
+        }
+        g0 = u32x4{gw[0], gw[1], gw[2], gw[3]};
+        g1 = u32x4{gw[4], gw[5], gw[6], gw[7]};
+        m = u32x4{mw[0], mw[1], mw[2], mw[3]};
+        v = u32x4{vw[0], vw[1], vw[2], vw[3]};
+    }
+    x.g[0] = g0.x; x.g[1] = g0.y; x.g[2] = g0.z; x.g[3] = g0.w;
+    x.g[4] = g1.x; x.g[5] = g1.y; x.g[6] = g1.z; x.g[7] = g1.w;
+    x.m[0] = m.x; x.m[1] = m.y; x.m[2] = m.z; x.m[3] = m.w;
+    x.v[0] = v.x; x.v[1] = v.y; x.v[2] = v.z; x.v[3] = v.w;
+}
+
+__device__ __forceinline__ void load_master(float (&mst)[16], const Ptrs& p, const ChunkPos& c, bool vec) {
+    f32x4 f[4];
+    if (vec) {
+        const VE_GLOBAL f32x4* mp = (const VE_GLOBAL f32x4*)(p.master + c.s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = mp[i];
+    } else {
+        float t[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) t[k] = (k < c.n) ? p.master[c.s + k] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = f32x4{t[4 * i], t[4 * i + 1], t[4 * i + 2], t[4 * i + 3]};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        mst[4 * i] = f[i].x; mst[4 * i + 1] = f[i].y; mst[4 * i + 2] = f[i].z; mst[4 * i + 3] = f[i].w;
+    }
+}
+
+// Adam moments from the dequantised stored moments (the one definition used
+// by both phases).
+__device__ __forceinline__ void moments(float g, float cm, float cv, float sm, float sv,
+                                        const StepScalars& sc, float& m1, float& v1) {
+    m1 = __builtin_fmaf(sc.beta1, cm * sm, sc.omb1 * g);
+    v1 = __builtin_fmaf(sc.beta2, cv * sv, sc.omb2 * (g * g));
+}
+
+__device__ __forceinline__ float elem_g(const In& x, int i) {
+    return (i & 1) ? bf_hi(x.g[i >> 1]) : bf_lo(x.g[i >> 1]);
+}
+
+// Phase 1 on one chunk: moments, AdamW update, writes of master, bf16 param
+// and the gradient copy; folds the chunk into the running absmax.
+__device__ __forceinline__ void phase1(const In& x, float (&mst)[16], const Ptrs& p, const ChunkPos& c,
+                                       bool vec, float sm, float sv, const StepScalars& sc, float& am,
+                                       float& av) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float m1, v1;
+        moments(elem_g(x, i), code_at(x.m[i >> 2], i & 3), code_at(x.v[i >> 2], i & 3), sm, sv, sc, m1, v1);
+        am = fmaxf(am, fabsf(m1));
+        av = fmaxf(av, v1);
+        const float d = __builtin_fmaf(__builtin_amdgcn_sqrtf(v1), sc.inv_sqrt_bc2, sc.eps);
+        const float u = m1 * __builtin_amdgcn_rcpf(d);
+        mst[i] = __builtin_fmaf(-sc.step_size, u, mst[i] * sc.decay);
+    }
+    uint32_t pb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pb[i] = pack_bf16x2(mst[2 * i], mst[2 * i + 1]);
+    if (vec) {
+        VE_GLOBAL f32x4* mp = (VE_GLOBAL f32x4*)(p.master + c.s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mp[i] = f32x4{mst[4 * i], mst[4 * i + 1], mst[4 * i + 2], mst[4 * i + 3]};
+        VE_GLOBAL u32x4* pp = (VE_GLOBAL u32x4*)(p.param + c.s);
+        pp[0] = u32x4{pb[0], pb[1], pb[2], pb[3]};
+        pp[1] = u32x4{pb[4], pb[5], pb[6], pb[7]};
+        VE_GLOBAL u32x4* gp = (VE_GLOBAL u32x4*)(p.grad_shard + c.s);
+        gp[0] = u32x4{x.g[0], x.g[1], x.g[2], x.g[3]};
+        gp[1] = u32x4{x.g[4], x.g[5], x.g[6], x.g[7]};
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            if (k < c.n) {
+                p.master[c.s + k] = mst[k];
+                p.param[c.s + k] = (uint16_t)(pb[k >> 1] >> (16 * (k & 1)));
+                p.grad_shard[c.s + k] = (uint16_t)(x.g[k >> 1] >> (16 * (k & 1)));
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t quant_byte(float x, float inv) {
+    float q = __builtin_rintf(x * inv);
+    q = __builtin_fminf(__builtin_fmaxf(q, -127.f), 127.f);
+    return (uint32_t)((int32_t)q) & 0xffu;
+}
+
+// Phase 2 on one chunk: recompute the moments from the held inputs and write
+// their codes under the block's new scales.
+__device__ __forceinline__ void phase2(const In& x, const Ptrs& p, const ChunkPos& c, bool vec, float sm,
+                                       float sv, float im, float iv, const StepScalars& sc) {
+    uint32_t qm[4] = {0, 0, 0, 0}, qv[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float m1, v1;
+        moments(elem_g(x, i), code_at(x.m[i >> 2], i & 3), code_at(x.v[i >> 2], i & 3), sm, sv, sc, m1, v1);
+        qm[i >> 2] |= quant_byte(m1, im) << (8 * (i & 3));
+        qv[i >> 2] |= quant_byte(v1, iv) << (8 * (i & 3));
+    }
+    if (vec) {
+        *(VE_GLOBAL u32x4*)(p.m_q + c.s) = u32x4{qm[0], qm[1], qm[2], qm[3]};
+        *(VE_GLOBAL u32x4*)(p.v_q + c.s) = u32x4{qv[0], qv[1], qv[2], qv[3]};
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            if (k < c.n) {
+                p.m_q[c.s + k] = (int8_t)(qm[k >> 2] >> (8 * (k & 3)));
+                p.v_q[c.s + k] = (int8_t)(qv[k >> 2] >> (8 * (k & 3)));
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void make_opaque(In& x) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) opaque(x.g[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        opaque(x.m[i]);
+        opaque(x.v[i]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// work lookup: the segmented descriptor table of the rank's class, staged in
+// LDS when it fits.  Returns the list index i with prefix[i] <= w < prefix[i+1]
+// and the item's offset inside that segment.  Contains a barrier: call from
+// converged code with every thread of the workgroup.
+extern __shared__ int64_t s_pref[];  // dynamic: prefix table (n + 1 entries) when staged
+
+__device__ __forceinline__ int find_item(const WorkList& wl, int64_t w, int64_t& local) {
+    const bool staged = wl.n <= kLdsPrefixCap;
+    if (staged) {
+        for (int i = threadIdx.x; i <= wl.n; i += blockDim.x) s_pref[i] = wl.prefix[i];
+    }
+    __syncthreads();
+    const int64_t* pref = staged ? s_pref : wl.prefix;
+    int lo = 0, hi = wl.n - 1;  // largest i with pref[i] <= w
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pref[mid] <= w) lo = mid; else hi = mid - 1;
+    }
+    local = w - pref[lo];
+    return lo;
+}
+
+// ---------------------------------------------------------------------------
+// kernels
+__global__ void __launch_bounds__(256) k_step_small(StepArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    int64_t local;
+    const int si = find_item(a.work, min(gw, a.work.total - 1), local);
+    if (gw >= a.work.total) return;  // whole waves only; no barrier follows
+    const ve_shard_state st = a.states[blockIdx.y];
+    const Seg sg = a.segs[a.work.seg_idx[si]];
+    const int G = sg.group;
+    const int64_t k = local * (64 / G) + lane / G;
+    const int li = lane & (G - 1);
+    const bool active = k < sg.nblocks;
+    const Ptrs p = make_ptrs(st, sg.tensor);
+
+    Geo geo;
+    ChunkPos cp;
+    bool vec = false, has = false;
+    float sm = 0.f, sv = 0.f, am = 0.f, av = 0.f;
+    In x;
+    if (active) {
+        geo = block_geo(sg, k);
+        has = li < geo.nchunks;
+        if (has) {
+            sm = st.m_scale[geo.blk];
+            sv = st.v_scale[geo.blk];
+            float mst[16];
+            cp = chunk_pos(geo, sg.shard_base, li);
+            vec = vec_ok(p, cp);
+            load_in(x, p, cp, vec);
+            load_master(mst, p, cp, vec);
+            phase1(x, mst, p, cp, vec, sm, sv, a.sc, am, av);
+        }
+    }
+    am = group_max(am, G);
+    av = group_max(av, G);
+    if (active) {
+        const float im = am > 0.f ? 127.0f / am : 0.f;
+        const float iv = av > 0.f ? 127.0f / av : 0.f;
+        if (li == 0) {
+            st.m_scale[geo.blk] = am / 127.0f;
+            st.v_scale[geo.blk] = av / 127.0f;
+        }
+        if (has) {
+            make_opaque(x);
+            phase2(x, p, cp, vec, sm, sv, im, iv, a.sc);
+        }
+    }
+}
+
+template <int T, int CPT>
+__global__ void __launch_bounds__(T) k_step_wg(StepArgs a) {
+    __shared__ float s_red[2][T / 64];
+    const int tid = threadIdx.x;
+    int64_t local;
+    const int si = find_item(a.work, blockIdx.x, local);
+    const ve_shard_state st = a.states[blockIdx.y];
+    const Seg sg = a.segs[a.work.seg_idx[si]];
+    const Geo geo = block_geo(sg, local);
+    const Ptrs p = make_ptrs(st, sg.tensor);
+    const float sm = st.m_scale[geo.blk], sv = st.v_scale[geo.blk];
+
+    In x[CPT];
+    float am = 0.f, av = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {  // every input load first: they stay in VGPRs
+        const int ci = tid + c * T;
+        if (ci < geo.nchunks) {
+            const ChunkPos cp = chunk_pos(geo, sg.shard_base, ci);
+            load_in(x[c], p, cp, vec_ok(p, cp));
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {  // master streamed chunk by chunk
+        const int ci = tid + c * T;
+        if (ci < geo.nchunks) {
+            const ChunkPos cp = chunk_pos(geo, sg.shard_base, ci);
+            const bool vec = vec_ok(p, cp);
+            float mst[16];
+            load_master(mst, p, cp, vec);
+            phase1(x[c], mst, p, cp, vec, sm, sv, a.sc, am, av);
+        }
+    }
+    am = wave_max(am);
+    av = wave_max(av);
+    if ((tid & 63) == 0) {
+        s_red[0][tid >> 6] = am;
+        s_red[1][tid >> 6] = av;
+    }
+    __syncthreads();
+    am = 0.f;
+    av = 0.f;
+#pragma unroll
+    for (int i = 0; i < T / 64; ++i) {
+        am = fmaxf(am, s_red[0][i]);
+        av = fmaxf(av, s_red[1][i]);
+    }
+    const float im = am > 0.f ? 127.0f / am : 0.f;
+    const float iv = av > 0.f ? 127.0f / av : 0.f;
+    if (tid == 0) {
+        st.m_scale[geo.blk] = am / 127.0f;
+        st.v_scale[geo.blk] = av / 127.0f;
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        const int ci = tid + c * T;
+        if (ci < geo.nchunks) {
+            make_opaque(x[c]);
+            const ChunkPos cp = chunk_pos(geo, sg.shard_base, ci);
+            phase2(x[c], p, cp, vec_ok(p, cp), sm, sv, im, iv, a.sc);
+        }
+    }
+}
+
+// Blocks too large for registers: two sweeps, the second re-reading inputs.
+__global__ void __launch_bounds__(256) k_step_huge(StepArgs a) {
+    __shared__ float s_red[2][4];
+    const int tid = threadIdx.x, T = blockDim.x;
+    int64_t local;
+    const int si = find_item(a.work, blockIdx.x, local);
+    const ve_shard_state st = a.states[blockIdx.y];
+    const Seg sg = a.segs[a.work.seg_idx[si]];
+    const Geo geo = block_geo(sg, local);
+    const Ptrs p = make_ptrs(st, sg.tensor);
+    const float sm = st.m_scale[geo.blk], sv = st.v_scale[geo.blk];
+    float am = 0.f, av = 0.f;
+    for (int ci = tid; ci < geo.nchunks; ci += T) {
+        In x;
+        const ChunkPos cp = chunk_pos(geo, sg.shard_base, ci);
+        load_in(x, p, cp, vec_ok(p, cp));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float m1, v1;
+            moments(elem_g(x, i), code_at(x.m[i >> 2], i & 3), code_at(x.v[i >> 2], i & 3), sm, sv, a.sc, m1, v1);
+            am = fmaxf(am, fabsf(m1));
+            av = fmaxf(av, v1);
+        }
+    }
+    am = wave_max(am);
+    av = wave_max(av);
+    if ((tid & 63) == 0) {
+        s_red[0][tid >> 6] = am;
+        s_red[1][tid >> 6] = av;
+    }
+    __syncthreads();
+    am = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+    av = fmaxf(fmaxf(s_red[1][0], s_red[1][1]), fmaxf(s_red[1][2], s_red[1][3]));
+    const float im = am > 0.f ? 127.0f / am : 0.f;
+    const float iv = av > 0.f ? 127.0f / av : 0.f;
+    for (int ci = tid; ci < geo.nchunks; ci += T) {
+        In x;
+        float mst[16];
+        const ChunkPos cp = chunk_pos(geo, sg.shard_base, ci);
+        const bool vec = vec_ok(p, cp);
+        load_in(x, p, cp, vec);
+        load_master(mst, p, cp, vec);
+        float dm = 0.f, dv = 0.f;
+        phase1(x, mst, p, cp, vec, sm, sv, a.sc, dm, dv);
+        phase2(x, p, cp, vec, sm, sv, im, iv, a.sc);
+    }
+    if (tid == 0) {
+        st.m_scale[geo.blk] = am / 127.0f;
+        st.v_scale[geo.blk] = av / 127.0f;
+    }
+}
+
+// Tiled runs: copy a tensor range into the output, or write zeros.
+// mode 0: one output `out`; mode 1: grad_shard and param_shard of states[y].
+__global__ void __launch_bounds__(256) k_runs(RunArgs r, const uint16_t* const* grad_ptrs, uint16_t* out,
+                                              const ve_shard_state* states, int mode) {
+    const int64_t tile = blockIdx.x;
+    const int ri = r.tile_run[tile];
+    const Run rn = r.runs[ri];
+    const int64_t t0 = (tile - r.tile_prefix[ri]) * kRunTile;
+    const int64_t len = min((int64_t)kRunTile, rn.len - t0);
+    uint16_t* o0 = out;
+    uint16_t* o1 = nullptr;
+    if (mode == 1) {
+        o0 = states[blockIdx.y].grad_shard;
+        o1 = states[blockIdx.y].param_shard;
+    }
+    const uint16_t* src = rn.tensor >= 0 ? grad_ptrs[rn.tensor] + rn.src + t0 : nullptr;
+    const bool aligned = (((uintptr_t)(o0 + rn.dst + t0) | (uintptr_t)(o1 ? o1 + rn.dst + t0 : nullptr) |
+                           (uintptr_t)src) & 15) == 0;
+    const VE_GLOBAL uint16_t* s = (const VE_GLOBAL uint16_t*)src;
+    VE_GLOBAL uint16_t* d0 = (VE_GLOBAL uint16_t*)(o0 + rn.dst + t0);
+    VE_GLOBAL uint16_t* d1 = o1 ? (VE_GLOBAL uint16_t*)(o1 + rn.dst + t0) : nullptr;
+    const int64_t i0 = (int64_t)threadIdx.x * kChunk;
+    if (i0 >= len) return;
+    if (aligned && i0 + kChunk <= len) {
+        u32x4 a = u32x4{0, 0, 0, 0}, b = a;
+        if (s) {
+            a = *(const VE_GLOBAL u32x4*)(s + i0);
+            b = *(const VE_GLOBAL u32x4*)(s + i0 + 8);
+        }
+        ((VE_GLOBAL u32x4*)(d0 + i0))[0] = a;
+        ((VE_GLOBAL u32x4*)(d0 + i0))[1] = b;
+        if (d1) {
+            ((VE_GLOBAL u32x4*)(d1 + i0))[0] = a;
+            ((VE_GLOBAL u32x4*)(d1 + i0))[1] = b;
+        }
+    } else {
+        const int64_t n = min((int64_t)kChunk, len - i0);
+        for (int64_t k = 0; k < n; ++k) {
+            const uint16_t v = s ? s[i0 + k] : (uint16_t)0;
+            d0[i0 + k] = v;
+            if (d1) d1[i0 + k] = v;
+        }
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// launchers
+static inline unsigned grid_x(int64_t n) { return (unsigned)n; }
+static inline size_t lds_bytes(const WorkList& w) {
+    return w.n <= kLdsPrefixCap ? sizeof(int64_t) * (size_t)(w.n + 1) : 0;
+}
+
+hipError_t launch_step_small(const StepArgs& a, int n_states, hipStream_t s) {
+    const int64_t wgs = (a.work.total + 3) / 4;
+    hipLaunchKernelGGL(k_step_small, dim3(grid_x(wgs), n_states), dim3(256), lds_bytes(a.work), s, a);
+    return hipGetLastError();
+}
+
+template <int T, int CPT>
+static hipError_t launch_wg_t(const StepArgs& a, int n_states, hipStream_t s) {
+    hipLaunchKernelGGL((k_step_wg<T, CPT>), dim3(grid_x(a.work.total), n_states), dim3(T), lds_bytes(a.work), s, a);
+    return hipGetLastError();
+}
+
+#define VE_WG_CASES(T)                                              \
+    switch (cpt) {                                                  \
+        case 1: return launch_wg_t<T, 1>(a, n_states, s);           \
+        case 2: return launch_wg_t<T, 2>(a, n_states, s);           \
+        case 3: return launch_wg_t<T, 3>(a, n_states, s);           \
+        case 4: return launch_wg_t<T, 4>(a, n_states, s);           \
+        case 5: return launch_wg_t<T, 5>(a, n_states, s);           \
+        case 6: return launch_wg_t<T, 6>(a, n_states, s);           \
+        case 7: return launch_wg_t<T, 7>(a, n_states, s);           \
+        case 8: return launch_wg_t<T, 8>(a, n_states, s);           \
+        case 9: return launch_wg_t<T, 9>(a, n_states, s);           \
+        case 10: return launch_wg_t<T, 10>(a, n_states, s);         \
+        case 11: return launch_wg_t<T, 11>(a, n_states, s);         \
+        case 12: return launch_wg_t<T, 12>(a, n_states, s);         \
+        default: return hipErrorInvalidValue;                       \
+    }
+
+bool wg_config_supported(int threads, int cpt) {
+    return (threads == 256 || threads == 512 || threads == 1024) && cpt >= 1 && cpt <= kWgMaxChunksPerThread;
+}
+
+hipError_t launch_step_wg(const StepArgs& a, int n_states, int threads, int cpt, hipStream_t s) {
+    if (threads == 256) { VE_WG_CASES(256) }
+    if (threads == 512) { VE_WG_CASES(512) }
+    if (threads == 1024) { VE_WG_CASES(1024) }
+    return hipErrorInvalidValue;
+}
+#undef VE_WG_CASES
+
+hipError_t launch_step_huge(const StepArgs& a, int n_states, hipStream_t s) {
+    hipLaunchKernelGGL(k_step_huge, dim3(grid_x(a.work.total), n_states), dim3(256), lds_bytes(a.work), s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_runs_copy(const RunArgs& r, const uint16_t* const* grad_ptrs, uint16_t* out, hipStream_t s) {
+    hipLaunchKernelGGL(k_runs, dim3(grid_x(r.n_tiles), 1), dim3(256), 0, s, r, grad_ptrs, out,
+                       (const ve_shard_state*)nullptr, 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_runs_pad(const RunArgs& r, const ve_shard_state* states, int n_states, hipStream_t s) {
+    hipLaunchKernelGGL(k_runs, dim3(grid_x(r.n_tiles), n_states), dim3(256), 0, s, r,
+                       (const uint16_t* const*)nullptr, (uint16_t*)nullptr, states, 1);
+    return hipGetLastError();
+}
+
+}  // namespace ve

@@ -91,8 +91,7 @@ def device_grad(cfg: Config, layout: Layout, bucket: int, k: int, device, step: 
         x = z[0] / torch.sqrt((z[1] ** 2 + z[2] ** 2 + z[3] ** 2) / 3.0)
         del z
     x.mul_(cfg.grad_scale)
-    return x.to(torch.bfloat16).view(torch.uint16) if hasattr(torch, "uint16") else \
-        x.to(torch.bfloat16).view(torch.int16)
+    return x.to(torch.bfloat16).view(torch.int16)
 
 
 def device_master(cfg: Config, layout: Layout, bucket: int, rank: int, device, mask=None):

@@ -1,0 +1,136 @@
+"""GPU-test plumbing: put seeded host inputs on the device around guard bands,
+run the library, pull results back, and compare with the oracle under the
+parity gates."""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from synth.data import host_grads, host_master
+
+DEV = "cuda:0"
+GUARD = 4096          # elements of guard band on each side (keeps 16-byte alignment)
+GUARD_BYTE = 0xA5
+CANARY16 = -1         # 0xFFFF in an int16 buffer: padding must come back as 0
+
+# parity gates (fp32 master, scales: relative error with an lr floor; codes
+# may differ by one step in a tiny fraction of elements)
+MASTER_RTOL = 1e-5
+SCALE_RTOL = 1e-5
+CODE_MAX_FRAC = 1e-4
+
+
+class Guarded:
+    """A device buffer with guard bands of GUARD_BYTE on both sides."""
+
+    def __init__(self, n, dtype, fill=None):
+        import torch
+        self.n = n
+        itemsize = torch.empty((), dtype=dtype).element_size()
+        self.raw = torch.full(((2 * GUARD + max(n, 1)) * itemsize,), GUARD_BYTE, dtype=torch.uint8, device=DEV)
+        self.view = self.raw[GUARD * itemsize:(GUARD + max(n, 1)) * itemsize].view(dtype)[:max(n, 1)]
+        if fill is not None:
+            self.view.fill_(fill)
+
+    def guards_intact(self) -> bool:
+        itemsize = self.view.element_size()
+        g = GUARD * itemsize
+        return bool((self.raw[:g] == GUARD_BYTE).all()) and bool((self.raw[-g:] == GUARD_BYTE).all())
+
+
+def to_dev_u16(a: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV)
+
+
+class RankProblem:
+    """One bucket on one rank: seeded inputs on the GPU, state in guarded
+    buffers, and the matching host arrays for the oracle."""
+
+    def __init__(self, ve, cfg, lay, plan, rank, bucket=0):
+        import torch
+        self.ve, self.cfg, self.lay, self.plan, self.rank, self.bucket = ve, cfg, lay, plan, rank, bucket
+        S = lay.shard
+        _, nb, _ = plan.query(rank)
+        self.nb = nb
+        self.buf = dict(grad_shard=Guarded(S, torch.int16, CANARY16), master=Guarded(S, torch.float32),
+                        m_q=Guarded(S, torch.int8, 0), v_q=Guarded(S, torch.int8, 0),
+                        m_scale=Guarded(nb, torch.float32, 0.0), v_scale=Guarded(nb, torch.float32, 0.0),
+                        param_shard=Guarded(S, torch.int16, CANARY16))
+        self.buf["master"].view.copy_(torch.from_numpy(host_master(cfg, lay, bucket, rank)))
+        self.grads_host = None
+        self.grad_dev = None
+        self.table = None
+
+    def set_grads(self, step):
+        self.grads_host = host_grads(self.cfg, self.lay, self.bucket, step)
+        self.grad_dev = [to_dev_u16(g) for g in self.grads_host]
+        self.gt = self.ve.grad_pointer_table(self.grad_dev)
+        st = {k: b.view for k, b in self.buf.items()}
+        st["grad_table"] = self.gt
+        self.table = self.ve.state_table(self.plan, self.rank, [st])
+
+    def download(self) -> dict:
+        out = {}
+        for k, b in self.buf.items():
+            a = b.view.cpu().numpy()
+            out[k] = a.view(np.uint16) if k in ("grad_shard", "param_shard") else a
+        out["m_scale"] = out["m_scale"][:self.nb].copy()
+        out["v_scale"] = out["v_scale"][:self.nb].copy()
+        return out
+
+    def guards_intact(self) -> bool:
+        return all(b.guards_intact() for b in self.buf.values())
+
+
+def bf16_of(master: np.ndarray) -> np.ndarray:
+    import torch
+    return torch.from_numpy(master).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+class Tally:
+    """Accumulates code mismatches across calls (the fraction gate is global)."""
+
+    def __init__(self):
+        self.elems = 0
+        self.mismatch = 0
+
+    def check(self):
+        assert self.mismatch <= CODE_MAX_FRAC * max(self.elems, 1), (self.mismatch, self.elems)
+
+
+def compare(got: dict, want: dict, valid: np.ndarray, lr: float, tally: Tally, where=""):
+    """Parity gates between a GPU result and the oracle's, on one shard."""
+    # pack/unpack: bit exact, padding zero
+    assert np.array_equal(got["grad_shard"], want["grad_shard"]), f"grad_shard {where}"
+    assert not got["param_shard"][~valid].any(), f"param padding {where}"
+    # fp32 master
+    g, w = got["master"][valid].astype(np.float64), want["master"][valid].astype(np.float64)
+    rel = np.abs(g - w) / np.maximum(np.abs(w), lr)
+    assert rel.size == 0 or rel.max() <= MASTER_RTOL, f"master rel {rel.max():.3g} {where}"
+    assert np.array_equal(got["master"][~valid].view(np.uint32), want["master"][~valid].view(np.uint32)), \
+        f"master padding touched {where}"
+    # bf16 param is the round-to-nearest-even image of the GPU's own master
+    assert np.array_equal(got["param_shard"][valid], bf16_of(got["master"][valid])), f"param != bf16(master) {where}"
+    # codes: off by at most one, in a tiny fraction of elements
+    for key in ("m_q", "v_q"):
+        d = np.abs(got[key][valid].astype(np.int16) - want[key][valid].astype(np.int16))
+        assert d.size == 0 or d.max() <= 1, f"{key} differs by {d.max()} {where}"
+        tally.elems += d.size
+        tally.mismatch += int((d != 0).sum())
+        assert np.array_equal(got[key][~valid], want[key][~valid]), f"{key} padding touched {where}"
+    assert got["v_q"].min() >= 0
+    # scales
+    for key in ("m_scale", "v_scale"):
+        g, w = got[key].astype(np.float64), want[key].astype(np.float64)
+        tiny = np.finfo(np.float32).tiny
+        rel = np.abs(g - w) / np.maximum(np.abs(w), tiny)
+        assert rel.size == 0 or rel.max() <= SCALE_RTOL, f"{key} rel {rel.max():.3g} {where}"
+
+
+def oracle_step(prob: RankProblem, before: dict, hp: dict, t: int) -> dict:
+    """The oracle's result for one step from ``before`` (copied)."""
+    st = {k: v.copy() for k, v in before.items()}
+    oracle.shard_step(prob.lay.spec_array(), prob.lay.fsdp, prob.lay.shard, prob.rank, prob.grads_host, st, hp, t)
+    return st

@@ -1,0 +1,132 @@
+"""Full-size workloads in the launch configuration the benchmark times (all
+buckets of a workload in one call): sampled blocks against the oracle, the
+whole gradient slice and padding through properties that hold at any size."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from synth.workload import device_buckets
+
+from gpu_common import DEV, Tally, bf16_of, MASTER_RTOL, SCALE_RTOL
+from helpers import hp32, layout_of, rank_block_coords
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _download(st, nb):
+    out = {}
+    for k in ("grad_shard", "master", "m_q", "v_q", "m_scale", "v_scale", "param_shard"):
+        a = st[k].cpu().numpy()
+        out[k] = a.view(np.uint16) if k in ("grad_shard", "param_shard") else a
+    out["m_scale"] = out["m_scale"][:nb].copy()
+    out["v_scale"] = out["v_scale"][:nb].copy()
+    return out
+
+
+def _block_positions(lay, rank, coord):
+    k, p, j = coord
+    t = lay.tensors[k]
+    (_, lo, _, dst) = next(x for x in lay.chunk_intervals(rank) if x[0] == k)
+    r0, r1 = p * t.block_rows, min((p + 1) * t.block_rows, t.rows)
+    rows = np.arange(r0, r1, dtype=np.int64)[:, None]
+    cols = np.arange(j * t.block_cols, (j + 1) * t.block_cols, dtype=np.int64)[None, :]
+    return (dst + rows * t.cols + cols - lo).reshape(-1)
+
+
+@pytest.mark.parametrize("name", ["llama", "gptoss", "deepseek", "adversarial"])
+def test_full_size_sampled(name):
+    import torch
+    import ragged_shard_optimizer_amd as ve
+    cfg, lay = layout_of(name)
+    rank = lay.largest_rank()
+    spec, m, S = lay.spec_array(), lay.fsdp, lay.shard
+    hp = hp32()
+    plan = ve.Plan(spec, m, S, device=0)
+    _, nb, _ = plan.query(rank)
+    _say(f"[gpu] full-size {name}: rank {rank}, {cfg.n_buckets} buckets, S={S}, blocks={nb}")
+    buckets = device_buckets(cfg, lay, rank, DEV)
+    states = [ve.new_state(plan, rank, ve.grad_pointer_table(g, DEV), master) for g, master in buckets]
+    table = ve.state_table(plan, rank, states)
+    coords = rank_block_coords(lay, rank)
+    assert len(coords) == nb
+    rng = np.random.default_rng(0)
+    sel = sorted({0, nb - 1} | set(rng.choice(nb, min(nb, 10), replace=False).tolist()))
+    sample_b = sorted({0, cfg.n_buckets // 2, cfg.n_buckets - 1})
+    pieces = list(lay.chunk_intervals(rank))
+    mask = torch.from_numpy(lay.valid_mask(rank)).to(DEV)
+    tally = Tally()
+    for t in (1, 2):
+        pre = {b: _download(states[b], nb) for b in sample_b}
+        _say(f"[gpu] full-size {name}: step {t}, {len(states)} states in one call")
+        plan.step(rank, table, hp, t)
+        torch.cuda.synchronize()
+        for b in sample_b:
+            grads_dev, _ = buckets[b]
+            # whole gradient slice: every piece bit-exact, padding zero (on the device)
+            gs = states[b]["grad_shard"]
+            for k, lo, hi, dst in pieces:
+                assert torch.equal(gs[dst:dst + hi - lo], grads_dev[k][lo:hi]), (name, b, k)
+            assert not gs[~mask].any() and not states[b]["param_shard"][~mask].any()
+            # sampled blocks through the oracle
+            got = _download(states[b], nb)
+            grads, bases = [None] * len(lay.tensors), [0] * len(lay.tensors)
+            for k, lo, hi, dst in pieces:
+                grads[k] = grads_dev[k][lo:hi].cpu().numpy().view(np.uint16)
+                bases[k] = lo
+            want = {k: v.copy() for k, v in pre[b].items()}
+            oracle.shard_step(spec, m, S, rank, grads, want, hp, t, bases=bases, blocks=sel)
+            for blk in sel:
+                pos = _block_positions(lay, rank, coords[blk])
+                g, w = got["master"][pos].astype(np.float64), want["master"][pos].astype(np.float64)
+                rel = np.abs(g - w) / np.maximum(np.abs(w), hp["lr"])
+                assert rel.max() <= MASTER_RTOL, (name, b, blk, rel.max())
+                assert np.array_equal(got["param_shard"][pos], bf16_of(got["master"][pos]))
+                for key in ("m_q", "v_q"):
+                    d = np.abs(got[key][pos].astype(np.int16) - want[key][pos].astype(np.int16))
+                    assert d.max() <= 1, (name, key, blk)
+                    tally.elems += d.size
+                    tally.mismatch += int((d != 0).sum())
+                for key in ("m_scale", "v_scale"):
+                    gs_, ws_ = float(got[key][blk]), float(want[key][blk])
+                    assert abs(gs_ - ws_) <= SCALE_RTOL * max(abs(ws_), np.finfo(np.float32).tiny), (key, blk)
+    tally.check()
+    del states, table, buckets
+    torch.cuda.empty_cache()
+
+
+def test_adversarial_whole_bucket_copy_in():
+    """Copy-in of the whole adversarial bucket (10,000 tensors, ~2.9 GB
+    moved): every tensor lands at its offset bit for bit, all padding zero."""
+    import torch
+    import ragged_shard_optimizer_amd as ve
+    from synth.data import device_grad
+    cfg, lay = layout_of("adversarial")
+    plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
+    grads = [device_grad(cfg, lay, 0, k, DEV) for k in range(len(lay.tensors))]
+    gt = ve.grad_pointer_table(grads, DEV)
+    bucket = torch.full((lay.bucket_elems,), -1, dtype=torch.int16, device=DEV)
+    _say(f"[gpu] whole-bucket copy-in: {lay.bucket_elems} elements")
+    plan.copy_in(-1, gt, bucket)
+    torch.cuda.synchronize()
+    covered = torch.zeros(lay.bucket_elems, dtype=torch.bool, device=DEV)
+    for k, o in enumerate(lay.offsets):
+        n = lay.tensors[k].numel
+        assert torch.equal(bucket[o:o + n], grads[k]), k
+        covered[o:o + n] = True
+    assert not bucket[~covered].any()
+    # spot-check against the oracle on a few ranks' chunks
+    host = [g.cpu().numpy().view(np.uint16) for g in grads]
+    got = bucket.cpu().numpy().view(np.uint16)
+    for r in (0, lay.largest_rank(), lay.fsdp - 1):
+        want = oracle.copy_in(lay.spec_array(), lay.fsdp, lay.shard, r, host)
+        assert np.array_equal(got[r * lay.shard:(r + 1) * lay.shard], want)

@@ -1,0 +1,232 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Small workloads are compared element by element over
+several teacher-forced steps; edge-case layouts exercise every kernel path
+(small groups of 1..64 lanes, workgroup blocks, two-pass huge blocks,
+unaligned and misaligned data, empty ranks, padding)."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import CONFIGS, TensorDef, plan_p0
+from synth.configs import Config
+from synth.layout import Layout
+
+from gpu_common import (DEV, Guarded, RankProblem, Tally, compare, oracle_step, to_dev_u16, CANARY16)
+from helpers import hp32, layout_of
+
+pytestmark = pytest.mark.gpu
+
+
+def _ve():
+    import ragged_shard_optimizer_amd as ve
+    return ve
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _ranks(lay, limit=6):
+    if lay.fsdp <= limit:
+        return list(range(lay.fsdp))
+    return sorted({0, 1, lay.fsdp // 2, lay.largest_rank(), lay.fsdp - 1})
+
+
+def _run_parity(cfg, lay, ranks, steps, tally, bucket=0):
+    import torch
+    ve = _ve()
+    hp = hp32()
+    plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
+    for r in ranks:
+        prob = RankProblem(ve, cfg, lay, plan, r, bucket)
+        valid = lay.valid_mask(r)
+        for t in range(1, steps + 1):
+            prob.set_grads(t)
+            before = prob.download()
+            _say(f"[gpu] {cfg.name} rank {r} step {t}: S={lay.shard} blocks={prob.nb}")
+            plan.step(r, prob.table, hp, t)
+            torch.cuda.synchronize()
+            got = prob.download()
+            want = oracle_step(prob, before, hp, t)
+            compare(got, want, valid, hp["lr"], tally, where=f"{cfg.name} r{r} t{t}")
+        assert prob.guards_intact(), f"guard band overwritten {cfg.name} r{r}"
+    plan.close()
+
+
+SMALL = ["toy_mix", "toy_r1", "toy_r4", "toy_r16", "toy_tile", "llama_mini", "llama_rowblk", "gptoss_mini",
+         "deepseek_mini", "adversarial_mini"]
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_step_parity(name):
+    cfg, lay = layout_of(name)
+    tally = Tally()
+    _run_parity(cfg, lay, _ranks(lay), cfg.steps if name.startswith("toy") else 2, tally)
+    tally.check()
+
+
+@pytest.mark.parametrize("name", ["toy_mix", "toy_tile", "llama_mini", "deepseek_mini", "adversarial_mini"])
+def test_copy_in_bit_exact(name):
+    import torch
+    ve = _ve()
+    cfg, lay = layout_of(name)
+    plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
+    from synth.data import host_grads
+    grads = host_grads(cfg, lay, 0, 1)
+    gt = ve.grad_pointer_table([to_dev_u16(g) for g in grads])
+    for r in _ranks(lay) + [-1]:
+        n = lay.shard * (lay.fsdp if r < 0 else 1)
+        out = Guarded(n, torch.int16, CANARY16)
+        _say(f"[gpu] copy-in {name} rank {r} n={n}")
+        plan.copy_in(r, gt, out.view)
+        torch.cuda.synchronize()
+        want = oracle.copy_in(lay.spec_array(), lay.fsdp, lay.shard, r, grads)
+        assert np.array_equal(out.view.cpu().numpy().view(np.uint16), want), (name, r)
+        assert out.guards_intact()
+        # zero-copy extraction: every tensor piece read back through its slice
+        got = out.view.cpu().numpy().view(np.uint16)
+        for k in range(len(lay.tensors)):
+            sl = plan.slice(r, k)
+            if sl:
+                off, lo, hi = sl
+                assert np.array_equal(got[off:off + hi - lo], grads[k][lo:hi])
+    plan.close()
+
+
+# ---------------------------------------------------------------------------
+# edge-case layouts, placed by hand
+def _explicit(name, tensors, offsets, m, S, grad_scale=1e-3, steps=2):
+    lay = Layout(list(tensors), list(offsets), m, S, list(range(len(tensors))))
+    oracle.validate(lay.spec_array(), m, S)
+    return Config(name, list(tensors), fsdp=m, grad_scale=grad_scale, steps=steps), lay
+
+
+def _group_sizes_case():
+    # one tensor per small-path group size (1..64 lanes) and two workgroup sizes
+    ts, offs, cur = [], [], 0
+    for i, (rows, cols, br, bc) in enumerate([
+            (33, 1, 1, 1), (40, 1, 16, 1), (9, 24, 1, 24), (7, 64, 1, 64), (5, 96, 2, 96),
+            (6, 128, 2, 128), (8, 64, 8, 64), (4, 256, 4, 256), (3, 1024, 1, 1024),
+            (2, 2048, 2, 2048), (40, 48, 8, 12), (64, 80, 16, 16), (17, 7, 3, 7)]):
+        ts.append(TensorDef(f"g{i}", rows, cols, br, bc))
+        offs.append(cur)
+        cur += rows * cols + (16 if i % 2 else 0)
+    S = -(-cur // 16) * 16
+    return _explicit("group_sizes", ts, offs, 1, S)
+
+
+def _unaligned_case():
+    # odd offsets: pieces start at shard positions that are not 16-aligned,
+    # chunk boundaries inside tensors stay on units
+    ts = [TensorDef("u0", 37, 1, 1, 1), TensorDef("u1", 20, 48, 4, 48), TensorDef("u2", 300, 1, 16, 1),
+          TensorDef("u3", 12, 40, 3, 8), TensorDef("u4", 10, 1000, 1, 1000)]
+    offs = [3, 41, 1001, 1301, 2000]
+    return _explicit("unaligned", ts, offs, 4, 3000)
+
+
+def _huge_case():
+    # a block of 96 x 2304 = 221,184 elements: beyond the register-resident path
+    ts = [TensorDef("h0", 200, 2304, 96, 2304), TensorDef("h1", 64, 64, 8, 8)]
+    return _explicit("huge", ts, [0, 200 * 2304 + 16], 1, 200 * 2304 + 16 + 4096)
+
+
+def _empty_rank_case():
+    # ranks 1 and 2 hold only padding; rank 0 a partial bucket
+    ts = [TensorDef("e0", 10, 16, 4, 16), TensorDef("e1", 3, 1, 1, 1)]
+    return _explicit("empty_rank", ts, [0, 160], 3, 256)
+
+
+def _straddle_case():
+    # one tensor over five ranks with a short last panel; another starting mid-chunk
+    ts = [TensorDef("s0", 50, 32, 4, 16), TensorDef("s1", 9, 128, 1, 128)]
+    return _explicit("straddle", ts, [0, 1664], 5, 768)
+
+
+EDGE = {"group_sizes": _group_sizes_case, "unaligned": _unaligned_case, "huge": _huge_case,
+        "empty_rank": _empty_rank_case, "straddle": _straddle_case}
+
+
+@pytest.mark.parametrize("case", list(EDGE))
+def test_edge_layouts(case):
+    cfg, lay = EDGE[case]()
+    tally = Tally()
+    _run_parity(cfg, lay, list(range(lay.fsdp)), 3, tally)
+    tally.check()
+
+
+def test_one_element_blocks_codes_exact():
+    # 1-element blocks: every nonzero code is +-127 and the scale is |m|/127
+    cfg, lay = _explicit("unit", [TensorDef("a", 999, 1, 1, 1), TensorDef("b", 21, 17, 1, 1)], [0, 1008], 2, 768)
+    tally = Tally()
+    _run_parity(cfg, lay, [0, 1], 3, tally)
+    assert tally.mismatch == 0
+
+
+def test_misaligned_state_buffers_take_scalar_path():
+    """State arrays shifted by one element (not 16-byte aligned) must give
+    bit-identical results to aligned ones."""
+    import torch
+    ve = _ve()
+    cfg, lay = layout_of("toy_mix")
+    plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
+    hp = hp32()
+    r = 1
+    prob = RankProblem(ve, cfg, lay, plan, r)
+    prob.set_grads(1)
+    S, nb = lay.shard, prob.nb
+    shifted = {}
+    for k, b in prob.buf.items():
+        n = b.view.numel()
+        big = torch.zeros(n + 1, dtype=b.view.dtype, device=DEV)
+        big[1:].copy_(b.view)
+        shifted[k] = big[1:]
+    st = dict(shifted)
+    st["grad_table"] = prob.gt
+    table = ve.state_table(plan, r, [st])
+    _say("[gpu] misaligned toy_mix rank 1")
+    plan.step(r, prob.table, hp, 1)
+    plan.step(r, table, hp, 1)
+    torch.cuda.synchronize()
+    for k in prob.buf:
+        a = prob.buf[k].view.cpu().numpy()
+        b = shifted[k].cpu().numpy()
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), k
+    plan.close()
+
+
+def test_batched_states_equal_single_calls_and_deterministic():
+    import torch
+    ve = _ve()
+    cfg, lay = layout_of("gptoss_mini")
+    plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
+    hp = hp32()
+    r = 0
+    probs = [RankProblem(ve, cfg, lay, plan, r, bucket=b) for b in range(3)]
+    for p in probs:
+        p.set_grads(1)
+    twins = [RankProblem(ve, cfg, lay, plan, r, bucket=b) for b in range(3)]
+    for p in twins:
+        p.set_grads(1)
+    states = []
+    for p in probs:
+        st = {k: b.view for k, b in p.buf.items()}
+        st["grad_table"] = p.gt
+        states.append(st)
+    batched = ve.state_table(plan, r, states)
+    _say("[gpu] batched gptoss_mini x3")
+    for t in (1, 2):
+        plan.step(r, batched, hp, t)
+        for p in twins:
+            plan.step(r, p.table, hp, t)
+    torch.cuda.synchronize()
+    for p, q in zip(probs, twins):
+        a, b = p.download(), q.download()
+        for k in a:
+            assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+    plan.close()
