@@ -16,7 +16,8 @@ from synth import CONFIGS, TensorDef, plan_p0
 from synth.configs import Config
 from synth.layout import Layout
 
-from gpu_common import (DEV, Guarded, RankProblem, Tally, compare, oracle_step, to_dev_u16, CANARY16)
+from gpu_common import (DEV, Guarded, RankProblem, Tally, block_ids, compare, oracle_step, scale_bound,
+                        to_dev_u16, CANARY16)
 from helpers import hp32, layout_of
 
 pytestmark = pytest.mark.gpu
@@ -46,6 +47,7 @@ def _run_parity(cfg, lay, ranks, steps, tally, bucket=0):
     for r in ranks:
         prob = RankProblem(ve, cfg, lay, plan, r, bucket)
         valid = lay.valid_mask(r)
+        ids = block_ids(lay, r)
         for t in range(1, steps + 1):
             prob.set_grads(t)
             before = prob.download()
@@ -54,7 +56,8 @@ def _run_parity(cfg, lay, ranks, steps, tally, bucket=0):
             torch.cuda.synchronize()
             got = prob.download()
             want = oracle_step(prob, before, hp, t)
-            compare(got, want, valid, hp["lr"], tally, where=f"{cfg.name} r{r} t{t}")
+            bounds = scale_bound(before, want["grad_shard"], ids, prob.nb, hp)
+            compare(got, want, valid, hp["lr"], tally, where=f"{cfg.name} r{r} t{t}", bounds=bounds)
         assert prob.guards_intact(), f"guard band overwritten {cfg.name} r{r}"
     plan.close()
 
