@@ -94,6 +94,26 @@ def cpu_baseline(cfg, lay, rank, budget_s=12.0):
                       f"buckets stepped in turn), {el:.1f} s wall, single thread"}
 
 
+def copy_ceiling(torch, dev, gib, reps=10):
+    """A plain device-to-device copy (torch's copy kernel) of ``gib`` GiB:
+    read + write bytes over its time -- the practical streaming ceiling."""
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes": 2 * 4 * n, "ms": round(ms, 5), "gbs": round(2 * 4 * n / (ms / 1e3) / 1e9, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +122,8 @@ def main():
     ap.add_argument("--workload", default="llama", choices=["llama", "gptoss", "deepseek", "adversarial"])
     ap.add_argument("--buckets", type=int, default=None, help="override the number of buckets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-gib", type=float, default=2.0,
+                    help="size of the plain device copy that measures the copy ceiling (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the data-parallel step; --gpus {args.gpus} is not "
@@ -186,6 +208,9 @@ def main():
     }
     del states, table, buckets
     torch.cuda.empty_cache()
+    if args.copy_gib > 0:
+        out["copy_ceiling"] = copy_ceiling(torch, dev, args.copy_gib)
+        out["copy_ceiling_frac"] = round(gbs / out["copy_ceiling"]["gbs"], 4)
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on host cores")
         out["cpu_baseline"] = cpu_baseline(cfg, lay, rank)

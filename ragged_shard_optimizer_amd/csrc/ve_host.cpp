@@ -59,7 +59,7 @@ struct RankTables {
     std::vector<Seg> segs;
     size_t off_segs = 0;
     HostWork small, wg, huge;
-    int32_t wg_max_chunks = 0;
+    int32_t wg_max_groups = 0;
     HostRuns copy;  // pieces + padding of the rank slice
     HostRuns pad;   // padding only (the step's zero fill)
     int64_t valid = 0, nblocks = 0;
@@ -184,15 +184,18 @@ void build_rank(ve_plan& P, int32_t r, RankTables& rt) {
         s.nblocks = panels * s.tiles;
         s.block0 = block0;
         s.tensor = k;
-        const int64_t br = std::min(t.block_rows, t.rows);
-        int64_t chunks;
-        if (s.tiles == 1) chunks = ceil_div(br * t.cols, kChunk);
-        else chunks = br * ceil_div(t.block_cols, kChunk);
+        const int64_t br = s.block_rows;
+        // lane-chunks of a full block: whole-row blocks are one run, tiles br runs
+        auto chunks_of = [&](int64_t ch) {
+            return s.tiles == 1 ? ceil_div(br * t.cols, ch) : br * ceil_div(t.block_cols, ch);
+        };
+        const int64_t chunks = chunks_of(kSmallChunk), groups = chunks_of(kWgChunk);
         s.max_chunks = (int32_t)std::min<int64_t>(chunks, INT32_MAX);
+        s.max_groups = (int32_t)std::min<int64_t>(groups, INT32_MAX);
         if (chunks <= kSmallMaxChunks) {
             s.cls = kSmall;
             s.group = next_pow2((int32_t)chunks);
-        } else if (chunks <= (int64_t)kWgMaxChunksPerThread * kWgMaxThreads) {
+        } else if (groups <= kWgMaxGroups) {
             s.cls = kWg;
             s.group = 0;
         } else {
@@ -207,7 +210,7 @@ void build_rank(ve_plan& P, int32_t r, RankTables& rt) {
         const int64_t items = s.cls == kSmall ? ceil_div(s.nblocks, 64 / s.group) : s.nblocks;
         w.seg_idx.push_back(si);
         w.prefix.push_back(w.prefix.back() + items);
-        if (s.cls == kWg) rt.wg_max_chunks = std::max(rt.wg_max_chunks, s.max_chunks);
+        if (s.cls == kWg) rt.wg_max_groups = std::max(rt.wg_max_groups, s.max_groups);
         const int64_t dst = a - c0;
         add_run(rt.copy, cursor, 0, dst - cursor, -1);
         add_run(rt.pad, cursor, 0, dst - cursor, -1);
@@ -272,27 +275,32 @@ WorkList work_list(const ve_plan& P, const HostWork& w) {
     return l;
 }
 
-// Workgroup path shape: threads and chunks per thread for blocks of up to
-// `chunks` chunks.  Overridable for tuning with VE_WG_THREADS / VE_WG_CPT.
-void wg_shape(int32_t chunks, int& threads, int& cpt) {
+// Workgroup path shape: threads and 4-element groups per thread for blocks
+// of up to `groups` groups.  Default: 512 threads (two workgroups per CU at
+// the usual register count) with the smallest instantiated groups-per-thread
+// that covers the block; 256 threads for small blocks, 1024 for the largest.
+// VE_WG_THREADS / VE_WG_GPT override it (launch-shape tuning).
+void wg_shape(int32_t groups, int& threads, int& gpt) {
     const char* et = std::getenv("VE_WG_THREADS");
-    const char* ec = std::getenv("VE_WG_CPT");
-    if (et && ec) {
+    const char* eg = std::getenv("VE_WG_GPT");
+    if (et && eg) {
         threads = std::atoi(et);
-        cpt = std::atoi(ec);
-        if (wg_config_supported(threads, cpt) && (int64_t)threads * cpt >= chunks) return;
+        gpt = std::atoi(eg);
+        if (wg_config_supported(threads, gpt) && (int64_t)threads * gpt >= groups) return;
     }
-    // fewest threads (of 256/512/1024) with at most 8 chunks each; 12 if the block needs it
     for (int t : {256, 512, 1024}) {
-        const int c = (int)ceil_div(chunks, t);
-        if (c <= 8) {
-            threads = t;
-            cpt = c;
-            return;
+        if (t == 256 && groups > 256 * 4) continue;
+        const int need = (int)ceil_div(groups, t);
+        for (int g = need; g <= 32; ++g) {
+            if (wg_config_supported(t, g)) {
+                threads = t;
+                gpt = g;
+                return;
+            }
         }
     }
-    threads = 1024;
-    cpt = (int)ceil_div(chunks, 1024);
+    threads = 1024;  // unreachable for blocks classed kWg (groups <= kWgMaxGroups)
+    gpt = 16;
 }
 
 struct DeviceGuard {
@@ -484,10 +492,10 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
     hipStream_t s = (hipStream_t)stream;
     ve_status st;
     if (rt.wg.prefix.back() > 0) {
-        int threads, cpt;
-        wg_shape(rt.wg_max_chunks, threads, cpt);
+        int threads, gpt;
+        wg_shape(rt.wg_max_groups, threads, gpt);
         a.work = work_list(*plan, rt.wg);
-        if ((st = launch_status(launch_step_wg(a, n_states, threads, cpt, s), "workgroup step")) != VE_OK) return st;
+        if ((st = launch_status(launch_step_wg(a, n_states, threads, gpt, s), "workgroup step")) != VE_OK) return st;
     }
     if (rt.small.prefix.back() > 0) {
         a.work = work_list(*plan, rt.small);

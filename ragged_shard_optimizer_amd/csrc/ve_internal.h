@@ -8,15 +8,27 @@
 
 namespace ve {
 
-// Elements per chunk: the unit a lane moves with 16-byte vector accesses
-// (16 int8 codes, 2 x 8 bf16, 4 x 4 fp32).
-constexpr int kChunk = 16;
-// A block with at most this many chunks is handled by a group of <= 64 lanes
-// of one wave (one chunk per lane); larger blocks take a whole workgroup.
+// Elements per lane-chunk.  Small blocks: 16 (one 16-byte vector of codes,
+// two of bf16, four of fp32 per lane).  Workgroup blocks: 4 (a dword of
+// codes, 8 bytes of bf16, 16 bytes of fp32 per lane, so that the 64 lanes of
+// a wave touch one contiguous span per access).
+constexpr int kSmallChunk = 16;
+constexpr int kWgChunk = 4;
+// A block with at most this many 16-element chunks is handled by a group of
+// <= 64 lanes of one wave (one chunk per lane); larger blocks take a whole
+// workgroup.
 constexpr int kSmallMaxChunks = 64;
-// Largest chunks-per-thread instantiation of the workgroup path.
-constexpr int kWgMaxChunksPerThread = 12;
 constexpr int kWgMaxThreads = 1024;
+
+// Instantiated workgroup shapes (threads, 4-element groups per thread).  The
+// largest capacity, 1024 x 16 groups = 65,536 elements, bounds the blocks
+// held in registers; larger blocks take the two-pass path.
+#define VE_WG_SHAPES(X)                                                                         \
+    X(256, 1) X(256, 2) X(256, 4) X(256, 8) X(256, 12) X(256, 16) X(256, 24) X(256, 32)         \
+    X(512, 2) X(512, 4) X(512, 6) X(512, 8) X(512, 10) X(512, 12) X(512, 14) X(512, 16)         \
+    X(512, 20) X(512, 24)                                                                       \
+    X(1024, 2) X(1024, 4) X(1024, 6) X(1024, 8) X(1024, 10) X(1024, 12) X(1024, 14) X(1024, 16)
+constexpr int64_t kWgMaxGroups = 1024 * 16;
 // Entries of a work-prefix table staged in LDS (larger tables are searched
 // in global memory).
 constexpr int kLdsPrefixCap = 2048;
@@ -39,8 +51,8 @@ struct Seg {
     int32_t tiles;       // tiles per panel = cols / block_cols
     int32_t cls;         // SegClass
     int32_t group;       // small path: lanes per block (power of two <= 64)
-    int32_t max_chunks;  // chunks of a full block
-    int32_t pad_;
+    int32_t max_chunks;  // 16-element chunks of a full block (small path)
+    int32_t max_groups;  // 4-element groups of a full block (workgroup path)
 };
 
 // A contiguous copy (tensor >= 0) or zero fill (tensor == -1) of `len`
@@ -88,7 +100,7 @@ struct RunArgs {
 
 // Launchers (ve_kernels.hip).  Return the hipError_t of the launch.
 hipError_t launch_step_small(const StepArgs& a, int n_states, hipStream_t s);
-hipError_t launch_step_wg(const StepArgs& a, int n_states, int threads, int chunks_per_thread,
+hipError_t launch_step_wg(const StepArgs& a, int n_states, int threads, int groups_per_thread,
                           hipStream_t s);
 hipError_t launch_step_huge(const StepArgs& a, int n_states, hipStream_t s);
 // Copy-in: out = bucket; grad pointers from `grad_ptrs`.
@@ -98,7 +110,7 @@ hipError_t launch_runs_copy(const RunArgs& r, const uint16_t* const* grad_ptrs, 
 hipError_t launch_runs_pad(const RunArgs& r, const ve_shard_state* states, int n_states,
                            hipStream_t s);
 
-// (threads, chunks per thread) pairs instantiated for the workgroup path.
-bool wg_config_supported(int threads, int chunks_per_thread);
+// (threads, groups per thread) pairs instantiated for the workgroup path.
+bool wg_config_supported(int threads, int groups_per_thread);
 
 }  // namespace ve

@@ -2,7 +2,7 @@
 //
 // Per element the step streams 18 bytes through HBM (bf16 gradient read and
 // copy-in write, fp32 master read+write, two int8 codes read+write, bf16
-// parameter write) and does ~60 VALU operations, so it is bandwidth-bound;
+// parameter write) and does ~40 VALU operations, so it is bandwidth-bound;
 // nothing here is a dense contraction and no MFMA is used.
 //
 // The one non-local step is the block absmax: every quantisation block's new
@@ -21,10 +21,12 @@
 //
 // Block-size classes (decided per rank segment at plan load):
 //   small  <= 64 chunks of 16 elements: a group of G (power of two) lanes of
-//          one wave owns a block, 64/G blocks per wave (1-, 16-, 128-element
-//          blocks of ragged buckets);
-//   wg     one workgroup owns a block, CPT chunks per thread held in VGPRs
-//          (row blocks of 8K..46K elements, 128x128 tiles);
+//          one wave owns a block, one 16-element chunk per lane, 64/G blocks
+//          per wave (1-, 16-, 128-element blocks of ragged buckets);
+//   wg     one workgroup owns a block; lanes own 4-element groups so that
+//          every wave-wide access is one contiguous span (1 KB of fp32
+//          master, 512 B of bf16, 256 B of codes), GPT groups per thread
+//          held in VGPRs (row blocks of 8K..46K elements, 128x128 tiles);
 //   huge   one workgroup, two passes (inputs re-read) for blocks too large to
 //          hold on chip.
 // Runs (copy-in, padding zero-fill) are plain tiled copies.
@@ -98,72 +100,35 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// block and chunk geometry
-struct Geo {
-    int64_t e0;      // tensor element of the block's first element
-    int64_t stride;  // tensor elements between consecutive runs (rows of a tile)
-    int32_t run;     // contiguous elements per run
-    int32_t nruns;
-    int32_t cpr;     // chunks per run
-    int32_t nchunks;
-    int64_t blk;     // rank-local block index (scale slot)
-};
-
-__device__ __forceinline__ Geo block_geo(const Seg& sg, int64_t k) {
-    Geo g;
-    const int64_t q = k / sg.tiles;
-    const int64_t j = k - q * sg.tiles;
-    const int64_t r0 = (sg.panel0 + q) * sg.block_rows;
-    const int64_t rows_in = min(sg.block_rows, sg.rows - r0);
-    if (sg.tiles == 1) {  // whole-row blocks: one contiguous run
-        g.e0 = r0 * sg.cols;
-        g.run = (int32_t)(rows_in * sg.cols);
-        g.nruns = 1;
-        g.stride = 0;
-    } else {              // a tile: rows_in runs of block_cols, row stride cols
-        g.e0 = r0 * sg.cols + j * sg.block_cols;
-        g.run = (int32_t)sg.block_cols;
-        g.nruns = (int32_t)rows_in;
-        g.stride = sg.cols;
-    }
-    g.cpr = (g.run + kChunk - 1) / kChunk;
-    g.nchunks = g.nruns * g.cpr;
-    g.blk = sg.block0 + k;
-    return g;
-}
-
-struct ChunkPos {
-    int64_t e;  // tensor element of the chunk's first element
-    int64_t s;  // shard coordinate of the same element
-    int32_t n;  // valid elements (1..16), contiguous
-};
-
-__device__ __forceinline__ ChunkPos chunk_pos(const Geo& g, int64_t shard_base, int ci) {
-    int ri = 0, w = ci * kChunk;
-    if (g.nruns != 1) {
-        ri = ci / g.cpr;
-        w = (ci - ri * g.cpr) * kChunk;
-    }
-    ChunkPos c;
-    c.e = g.e0 + (int64_t)ri * g.stride + w;
-    c.s = shard_base + c.e;
-    c.n = min(kChunk, g.run - w);
-    return c;
-}
-
-// ---------------------------------------------------------------------------
-// per-chunk data movement and arithmetic
-struct In {
-    uint32_t g[8];  // 16 bf16 gradients
-    uint32_t m[4];  // 16 first-moment codes
-    uint32_t v[4];  // 16 second-moment codes
-};
-
+// global-memory access
 // Pointers read from the state table are generic; the buffers live in device
 // global memory, so address them as such (global_* instead of flat_* accesses).
 #define VE_GLOBAL __attribute__((address_space(1)))
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Vector accesses.  Every byte is touched once; where a wave-wide access
+// covers whole cache lines (lane-contiguous layouts) it carries a
+// non-temporal (streaming) hint.  Where lanes are strided (16-element
+// chunks), partial lines are merged in the L2 across accesses, which the
+// hint would defeat, so those stay plain.
+#ifndef VE_NONTEMPORAL
+#define VE_NONTEMPORAL 1
+#endif
+template <int CH>
+constexpr bool kStream = VE_NONTEMPORAL && CH == kWgChunk;
+
+template <bool NT, class V>
+__device__ __forceinline__ V ldv(const VE_GLOBAL V* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <bool NT, class V>
+__device__ __forceinline__ void stv(VE_GLOBAL V* p, V v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
 
 struct Ptrs {
     const VE_GLOBAL uint16_t* __restrict__ grad;
@@ -189,31 +154,113 @@ __device__ __forceinline__ Ptrs make_ptrs(const ve_shard_state& st, int tensor) 
     return p;
 }
 
-__device__ __forceinline__ bool vec_ok(const Ptrs& p, const ChunkPos& c) {
-    return p.aligned && c.n == kChunk && (c.s & 15) == 0 && (c.e & 7) == 0;
+// ---------------------------------------------------------------------------
+// block and chunk geometry
+struct Geo {
+    int64_t e0;      // tensor element of the block's first element
+    int64_t stride;  // tensor elements between consecutive runs (rows of a tile)
+    int32_t run;     // contiguous elements per run
+    int32_t nruns;
+    int32_t cpr;     // chunks per run
+    int32_t nchunks;
+    int64_t blk;     // rank-local block index (scale slot)
+};
+
+template <int CH>
+__device__ __forceinline__ Geo block_geo(const Seg& sg, int64_t k) {
+    Geo g;
+    const int64_t q = k / sg.tiles;
+    const int64_t j = k - q * sg.tiles;
+    const int64_t r0 = (sg.panel0 + q) * sg.block_rows;
+    const int64_t rows_in = min(sg.block_rows, sg.rows - r0);
+    if (sg.tiles == 1) {  // whole-row blocks: one contiguous run
+        g.e0 = r0 * sg.cols;
+        g.run = (int32_t)(rows_in * sg.cols);
+        g.nruns = 1;
+        g.stride = 0;
+    } else {              // a tile: rows_in runs of block_cols, row stride cols
+        g.e0 = r0 * sg.cols + j * sg.block_cols;
+        g.run = (int32_t)sg.block_cols;
+        g.nruns = (int32_t)rows_in;
+        g.stride = sg.cols;
+    }
+    g.cpr = (g.run + CH - 1) / CH;
+    g.nchunks = g.nruns * g.cpr;
+    g.blk = sg.block0 + k;
+    return g;
 }
+
+struct ChunkPos {
+    int64_t e;  // tensor element of the chunk's first element
+    int64_t s;  // shard coordinate of the same element
+    int32_t n;  // valid elements (1..CH), contiguous
+};
+
+template <int CH>
+__device__ __forceinline__ ChunkPos chunk_pos(const Geo& g, int64_t shard_base, int ci) {
+    int ri = 0, w = ci * CH;
+    if (g.nruns != 1) {
+        ri = ci / g.cpr;
+        w = (ci - ri * g.cpr) * CH;
+    }
+    ChunkPos c;
+    c.e = g.e0 + (int64_t)ri * g.stride + w;
+    c.s = shard_base + c.e;
+    c.n = min(CH, g.run - w);
+    return c;
+}
+
+// A chunk takes the vector path when it is full and every access is
+// naturally aligned (CH codes, CH/4 16-byte master vectors, CH bf16 values).
+template <int CH>
+__device__ __forceinline__ bool vec_ok(const Ptrs& p, const ChunkPos& c) {
+    constexpr int kGradAlign = CH >= 8 ? 8 : CH;  // elements: 16 B (CH 16) or 8 B (CH 4)
+    return p.aligned && c.n == CH && (c.s & (CH - 1)) == 0 && (c.e & (kGradAlign - 1)) == 0;
+}
+
+// ---------------------------------------------------------------------------
+// per-chunk data movement and arithmetic
+template <int CH>
+struct In {
+    uint32_t g[CH / 2];  // CH bf16 gradients
+    uint32_t m[CH / 4];  // CH first-moment codes
+    uint32_t v[CH / 4];  // CH second-moment codes
+};
 
 // Both access paths produce plain values and the registers are assigned
 // once afterwards (stores from two branches into one array would otherwise be
 // merged into a store through a selected address, which demotes the array to
 // scratch memory).
-__device__ __forceinline__ void load_in(In& x, const Ptrs& p, const ChunkPos& c, bool vec) {
-    u32x4 g0, g1, m, v;
+template <int CH>
+__device__ __forceinline__ void load_in(In<CH>& x, const Ptrs& p, const ChunkPos& c, bool vec) {
+    uint32_t gw[CH / 2], mw[CH / 4], vw[CH / 4];
     if (vec) {
-        g0 = *(const VE_GLOBAL u32x4*)(p.grad + c.e);
-        g1 = *(const VE_GLOBAL u32x4*)(p.grad + c.e + 8);
-        m = *(const VE_GLOBAL u32x4*)(p.m_q + c.s);
-        v = *(const VE_GLOBAL u32x4*)(p.v_q + c.s);
+        if constexpr (CH == 16) {
+            const u32x4 g0 = ldv<kStream<CH>>((const VE_GLOBAL u32x4*)(p.grad + c.e));
+            const u32x4 g1 = ldv<kStream<CH>>((const VE_GLOBAL u32x4*)(p.grad + c.e + 8));
+            const u32x4 m = ldv<kStream<CH>>((const VE_GLOBAL u32x4*)(p.m_q + c.s));
+            const u32x4 v = ldv<kStream<CH>>((const VE_GLOBAL u32x4*)(p.v_q + c.s));
+            gw[0] = g0.x; gw[1] = g0.y; gw[2] = g0.z; gw[3] = g0.w;
+            gw[4] = g1.x; gw[5] = g1.y; gw[6] = g1.z; gw[7] = g1.w;
+            mw[0] = m.x; mw[1] = m.y; mw[2] = m.z; mw[3] = m.w;
+            vw[0] = v.x; vw[1] = v.y; vw[2] = v.z; vw[3] = v.w;
+        } else {
+            static_assert(CH == 4, "chunks are 4 or 16 elements");
+            const u32x2 g = ldv<kStream<CH>>((const VE_GLOBAL u32x2*)(p.grad + c.e));
+            gw[0] = g.x;
+            gw[1] = g.y;
+            mw[0] = ldv<kStream<CH>>((const VE_GLOBAL uint32_t*)(p.m_q + c.s));
+            vw[0] = ldv<kStream<CH>>((const VE_GLOBAL uint32_t*)(p.v_q + c.s));
+        }
     } else {
-        uint32_t gw[8], mw[4], vw[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < CH / 2; ++i) {
             const uint32_t lo = (2 * i < c.n) ? p.grad[c.e + 2 * i] : 0u;
             const uint32_t hi = (2 * i + 1 < c.n) ? p.grad[c.e + 2 * i + 1] : 0u;
             gw[i] = lo | (hi << 16);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < CH / 4; ++i) {
             uint32_t a = 0, b = 0;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -225,32 +272,32 @@ __device__ __forceinline__ void load_in(In& x, const Ptrs& p, const ChunkPos& c,
             mw[i] = a;
             vw[i] = b;
         }
-        g0 = u32x4{gw[0], gw[1], gw[2], gw[3]};
-        g1 = u32x4{gw[4], gw[5], gw[6], gw[7]};
-        m = u32x4{mw[0], mw[1], mw[2], mw[3]};
-        v = u32x4{vw[0], vw[1], vw[2], vw[3]};
     }
-    x.g[0] = g0.x; x.g[1] = g0.y; x.g[2] = g0.z; x.g[3] = g0.w;
-    x.g[4] = g1.x; x.g[5] = g1.y; x.g[6] = g1.z; x.g[7] = g1.w;
-    x.m[0] = m.x; x.m[1] = m.y; x.m[2] = m.z; x.m[3] = m.w;
-    x.v[0] = v.x; x.v[1] = v.y; x.v[2] = v.z; x.v[3] = v.w;
+#pragma unroll
+    for (int i = 0; i < CH / 2; ++i) x.g[i] = gw[i];
+#pragma unroll
+    for (int i = 0; i < CH / 4; ++i) {
+        x.m[i] = mw[i];
+        x.v[i] = vw[i];
+    }
 }
 
-__device__ __forceinline__ void load_master(float (&mst)[16], const Ptrs& p, const ChunkPos& c, bool vec) {
-    f32x4 f[4];
+template <int CH>
+__device__ __forceinline__ void load_master(float (&mst)[CH], const Ptrs& p, const ChunkPos& c, bool vec) {
+    f32x4 f[CH / 4];
     if (vec) {
         const VE_GLOBAL f32x4* mp = (const VE_GLOBAL f32x4*)(p.master + c.s);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f[i] = mp[i];
+        for (int i = 0; i < CH / 4; ++i) f[i] = ldv<kStream<CH>>(mp + i);
     } else {
-        float t[16];
+        float t[CH];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) t[k] = (k < c.n) ? p.master[c.s + k] : 0.f;
+        for (int k = 0; k < CH; ++k) t[k] = (k < c.n) ? p.master[c.s + k] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f[i] = f32x4{t[4 * i], t[4 * i + 1], t[4 * i + 2], t[4 * i + 3]};
+        for (int i = 0; i < CH / 4; ++i) f[i] = f32x4{t[4 * i], t[4 * i + 1], t[4 * i + 2], t[4 * i + 3]};
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < CH / 4; ++i) {
         mst[4 * i] = f[i].x; mst[4 * i + 1] = f[i].y; mst[4 * i + 2] = f[i].z; mst[4 * i + 3] = f[i].w;
     }
 }
@@ -263,17 +310,19 @@ __device__ __forceinline__ void moments(float g, float cm, float cv, float sm, f
     v1 = __builtin_fmaf(sc.beta2, cv * sv, sc.omb2 * (g * g));
 }
 
-__device__ __forceinline__ float elem_g(const In& x, int i) {
+template <int CH>
+__device__ __forceinline__ float elem_g(const In<CH>& x, int i) {
     return (i & 1) ? bf_hi(x.g[i >> 1]) : bf_lo(x.g[i >> 1]);
 }
 
 // Phase 1 on one chunk: moments, AdamW update, writes of master, bf16 param
 // and the gradient copy; folds the chunk into the running absmax.
-__device__ __forceinline__ void phase1(const In& x, float (&mst)[16], const Ptrs& p, const ChunkPos& c,
+template <int CH>
+__device__ __forceinline__ void phase1(const In<CH>& x, float (&mst)[CH], const Ptrs& p, const ChunkPos& c,
                                        bool vec, float sm, float sv, const StepScalars& sc, float& am,
                                        float& av) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < CH; ++i) {
         float m1, v1;
         moments(elem_g(x, i), code_at(x.m[i >> 2], i & 3), code_at(x.v[i >> 2], i & 3), sm, sv, sc, m1, v1);
         am = fmaxf(am, fabsf(m1));
@@ -282,22 +331,27 @@ __device__ __forceinline__ void phase1(const In& x, float (&mst)[16], const Ptrs
         const float u = m1 * __builtin_amdgcn_rcpf(d);
         mst[i] = __builtin_fmaf(-sc.step_size, u, mst[i] * sc.decay);
     }
-    uint32_t pb[8];
+    uint32_t pb[CH / 2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pb[i] = pack_bf16x2(mst[2 * i], mst[2 * i + 1]);
+    for (int i = 0; i < CH / 2; ++i) pb[i] = pack_bf16x2(mst[2 * i], mst[2 * i + 1]);
     if (vec) {
         VE_GLOBAL f32x4* mp = (VE_GLOBAL f32x4*)(p.master + c.s);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mp[i] = f32x4{mst[4 * i], mst[4 * i + 1], mst[4 * i + 2], mst[4 * i + 3]};
-        VE_GLOBAL u32x4* pp = (VE_GLOBAL u32x4*)(p.param + c.s);
-        pp[0] = u32x4{pb[0], pb[1], pb[2], pb[3]};
-        pp[1] = u32x4{pb[4], pb[5], pb[6], pb[7]};
-        VE_GLOBAL u32x4* gp = (VE_GLOBAL u32x4*)(p.grad_shard + c.s);
-        gp[0] = u32x4{x.g[0], x.g[1], x.g[2], x.g[3]};
-        gp[1] = u32x4{x.g[4], x.g[5], x.g[6], x.g[7]};
+        for (int i = 0; i < CH / 4; ++i) stv<kStream<CH>>(mp + i, f32x4{mst[4 * i], mst[4 * i + 1], mst[4 * i + 2], mst[4 * i + 3]});
+        if constexpr (CH == 16) {
+            VE_GLOBAL u32x4* pp = (VE_GLOBAL u32x4*)(p.param + c.s);
+            stv<kStream<CH>>(pp, u32x4{pb[0], pb[1], pb[2], pb[3]});
+            stv<kStream<CH>>(pp + 1, u32x4{pb[4], pb[5], pb[6], pb[7]});
+            VE_GLOBAL u32x4* gp = (VE_GLOBAL u32x4*)(p.grad_shard + c.s);
+            stv<kStream<CH>>(gp, u32x4{x.g[0], x.g[1], x.g[2], x.g[3]});
+            stv<kStream<CH>>(gp + 1, u32x4{x.g[4], x.g[5], x.g[6], x.g[7]});
+        } else {
+            stv<kStream<CH>>((VE_GLOBAL u32x2*)(p.param + c.s), u32x2{pb[0], pb[1]});
+            stv<kStream<CH>>((VE_GLOBAL u32x2*)(p.grad_shard + c.s), u32x2{x.g[0], x.g[1]});
+        }
     } else {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < CH; ++k) {
             if (k < c.n) {
                 p.master[c.s + k] = mst[k];
                 p.param[c.s + k] = (uint16_t)(pb[k >> 1] >> (16 * (k & 1)));
@@ -315,22 +369,30 @@ __device__ __forceinline__ uint32_t quant_byte(float x, float inv) {
 
 // Phase 2 on one chunk: recompute the moments from the held inputs and write
 // their codes under the block's new scales.
-__device__ __forceinline__ void phase2(const In& x, const Ptrs& p, const ChunkPos& c, bool vec, float sm,
+template <int CH>
+__device__ __forceinline__ void phase2(const In<CH>& x, const Ptrs& p, const ChunkPos& c, bool vec, float sm,
                                        float sv, float im, float iv, const StepScalars& sc) {
-    uint32_t qm[4] = {0, 0, 0, 0}, qv[4] = {0, 0, 0, 0};
+    uint32_t qm[CH / 4], qv[CH / 4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < CH / 4; ++i) qm[i] = qv[i] = 0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
         float m1, v1;
         moments(elem_g(x, i), code_at(x.m[i >> 2], i & 3), code_at(x.v[i >> 2], i & 3), sm, sv, sc, m1, v1);
         qm[i >> 2] |= quant_byte(m1, im) << (8 * (i & 3));
         qv[i >> 2] |= quant_byte(v1, iv) << (8 * (i & 3));
     }
     if (vec) {
-        *(VE_GLOBAL u32x4*)(p.m_q + c.s) = u32x4{qm[0], qm[1], qm[2], qm[3]};
-        *(VE_GLOBAL u32x4*)(p.v_q + c.s) = u32x4{qv[0], qv[1], qv[2], qv[3]};
+        if constexpr (CH == 16) {
+            stv<kStream<CH>>((VE_GLOBAL u32x4*)(p.m_q + c.s), u32x4{qm[0], qm[1], qm[2], qm[3]});
+            stv<kStream<CH>>((VE_GLOBAL u32x4*)(p.v_q + c.s), u32x4{qv[0], qv[1], qv[2], qv[3]});
+        } else {
+            stv<kStream<CH>>((VE_GLOBAL uint32_t*)(p.m_q + c.s), qm[0]);
+            stv<kStream<CH>>((VE_GLOBAL uint32_t*)(p.v_q + c.s), qv[0]);
+        }
     } else {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < CH; ++k) {
             if (k < c.n) {
                 p.m_q[c.s + k] = (int8_t)(qm[k >> 2] >> (8 * (k & 3)));
                 p.v_q[c.s + k] = (int8_t)(qv[k >> 2] >> (8 * (k & 3)));
@@ -339,11 +401,12 @@ __device__ __forceinline__ void phase2(const In& x, const Ptrs& p, const ChunkPo
     }
 }
 
-__device__ __forceinline__ void make_opaque(In& x) {
+template <int CH>
+__device__ __forceinline__ void make_opaque(In<CH>& x) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) opaque(x.g[i]);
+    for (int i = 0; i < CH / 2; ++i) opaque(x.g[i]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < CH / 4; ++i) {
         opaque(x.m[i]);
         opaque(x.v[i]);
     }
@@ -375,6 +438,7 @@ __device__ __forceinline__ int find_item(const WorkList& wl, int64_t w, int64_t&
 // ---------------------------------------------------------------------------
 // kernels
 __global__ void __launch_bounds__(256) k_step_small(StepArgs a) {
+    constexpr int CH = kSmallChunk;
     const int lane = threadIdx.x & 63;
     const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     int64_t local;
@@ -392,16 +456,16 @@ __global__ void __launch_bounds__(256) k_step_small(StepArgs a) {
     ChunkPos cp;
     bool vec = false, has = false;
     float sm = 0.f, sv = 0.f, am = 0.f, av = 0.f;
-    In x;
+    In<CH> x;
     if (active) {
-        geo = block_geo(sg, k);
+        geo = block_geo<CH>(sg, k);
         has = li < geo.nchunks;
         if (has) {
             sm = st.m_scale[geo.blk];
             sv = st.v_scale[geo.blk];
-            float mst[16];
-            cp = chunk_pos(geo, sg.shard_base, li);
-            vec = vec_ok(p, cp);
+            float mst[CH];
+            cp = chunk_pos<CH>(geo, sg.shard_base, li);
+            vec = vec_ok<CH>(p, cp);
             load_in(x, p, cp, vec);
             load_master(mst, p, cp, vec);
             phase1(x, mst, p, cp, vec, sm, sv, a.sc, am, av);
@@ -423,37 +487,58 @@ __global__ void __launch_bounds__(256) k_step_small(StepArgs a) {
     }
 }
 
-template <int T, int CPT>
+#ifndef VE_MASTER_AHEAD
+#define VE_MASTER_AHEAD 2  // master loads issued this many groups ahead of their update
+#endif
+
+// One workgroup per block; thread tid owns groups tid, tid + T, ... of
+// kWgChunk elements, so wave instruction j covers 64 consecutive groups.
+//
+// Load order matters: vector loads and stores retire through one in-order
+// counter, so waiting for a load also waits for every store issued before
+// it.  All input loads are therefore issued first (they stay in registers),
+// and each group's master is loaded MA groups ahead of its update, i.e.
+// before the stores of the groups in between.
+template <int T, int GPT>
 __global__ void __launch_bounds__(T) k_step_wg(StepArgs a) {
+    constexpr int CH = kWgChunk;
+    constexpr int MA = VE_MASTER_AHEAD < GPT ? VE_MASTER_AHEAD : GPT;
     __shared__ float s_red[2][T / 64];
     const int tid = threadIdx.x;
     int64_t local;
     const int si = find_item(a.work, blockIdx.x, local);
     const ve_shard_state st = a.states[blockIdx.y];
     const Seg sg = a.segs[a.work.seg_idx[si]];
-    const Geo geo = block_geo(sg, local);
+    const Geo geo = block_geo<CH>(sg, local);
     const Ptrs p = make_ptrs(st, sg.tensor);
     const float sm = st.m_scale[geo.blk], sv = st.v_scale[geo.blk];
 
-    In x[CPT];
+    In<CH> x[GPT];
+    float mst[MA + 1][CH];  // ring of master values in flight
     float am = 0.f, av = 0.f;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {  // every input load first: they stay in VGPRs
+    for (int c = 0; c < GPT; ++c) {
         const int ci = tid + c * T;
         if (ci < geo.nchunks) {
-            const ChunkPos cp = chunk_pos(geo, sg.shard_base, ci);
-            load_in(x[c], p, cp, vec_ok(p, cp));
+            const ChunkPos cp = chunk_pos<CH>(geo, sg.shard_base, ci);
+            const bool vec = vec_ok<CH>(p, cp);
+            load_in(x[c], p, cp, vec);
+            if (c < MA) load_master(mst[c % (MA + 1)], p, cp, vec);
         }
     }
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {  // master streamed chunk by chunk
+    for (int c = 0; c < GPT; ++c) {
+        if (c + MA < GPT) {
+            const int cn = tid + (c + MA) * T;
+            if (cn < geo.nchunks) {
+                const ChunkPos cpn = chunk_pos<CH>(geo, sg.shard_base, cn);
+                load_master(mst[(c + MA) % (MA + 1)], p, cpn, vec_ok<CH>(p, cpn));
+            }
+        }
         const int ci = tid + c * T;
         if (ci < geo.nchunks) {
-            const ChunkPos cp = chunk_pos(geo, sg.shard_base, ci);
-            const bool vec = vec_ok(p, cp);
-            float mst[16];
-            load_master(mst, p, cp, vec);
-            phase1(x[c], mst, p, cp, vec, sm, sv, a.sc, am, av);
+            const ChunkPos cp = chunk_pos<CH>(geo, sg.shard_base, ci);
+            phase1(x[c], mst[c % (MA + 1)], p, cp, vec_ok<CH>(p, cp), sm, sv, a.sc, am, av);
         }
     }
     am = wave_max(am);
@@ -477,34 +562,35 @@ __global__ void __launch_bounds__(T) k_step_wg(StepArgs a) {
         st.v_scale[geo.blk] = av / 127.0f;
     }
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
+    for (int c = 0; c < GPT; ++c) {
         const int ci = tid + c * T;
         if (ci < geo.nchunks) {
             make_opaque(x[c]);
-            const ChunkPos cp = chunk_pos(geo, sg.shard_base, ci);
-            phase2(x[c], p, cp, vec_ok(p, cp), sm, sv, im, iv, a.sc);
+            const ChunkPos cp = chunk_pos<CH>(geo, sg.shard_base, ci);
+            phase2(x[c], p, cp, vec_ok<CH>(p, cp), sm, sv, im, iv, a.sc);
         }
     }
 }
 
 // Blocks too large for registers: two sweeps, the second re-reading inputs.
 __global__ void __launch_bounds__(256) k_step_huge(StepArgs a) {
+    constexpr int CH = kWgChunk;
     __shared__ float s_red[2][4];
     const int tid = threadIdx.x, T = blockDim.x;
     int64_t local;
     const int si = find_item(a.work, blockIdx.x, local);
     const ve_shard_state st = a.states[blockIdx.y];
     const Seg sg = a.segs[a.work.seg_idx[si]];
-    const Geo geo = block_geo(sg, local);
+    const Geo geo = block_geo<CH>(sg, local);
     const Ptrs p = make_ptrs(st, sg.tensor);
     const float sm = st.m_scale[geo.blk], sv = st.v_scale[geo.blk];
     float am = 0.f, av = 0.f;
     for (int ci = tid; ci < geo.nchunks; ci += T) {
-        In x;
-        const ChunkPos cp = chunk_pos(geo, sg.shard_base, ci);
-        load_in(x, p, cp, vec_ok(p, cp));
+        In<CH> x;
+        const ChunkPos cp = chunk_pos<CH>(geo, sg.shard_base, ci);
+        load_in(x, p, cp, vec_ok<CH>(p, cp));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < CH; ++i) {
             float m1, v1;
             moments(elem_g(x, i), code_at(x.m[i >> 2], i & 3), code_at(x.v[i >> 2], i & 3), sm, sv, a.sc, m1, v1);
             am = fmaxf(am, fabsf(m1));
@@ -523,10 +609,10 @@ __global__ void __launch_bounds__(256) k_step_huge(StepArgs a) {
     const float im = am > 0.f ? 127.0f / am : 0.f;
     const float iv = av > 0.f ? 127.0f / av : 0.f;
     for (int ci = tid; ci < geo.nchunks; ci += T) {
-        In x;
-        float mst[16];
-        const ChunkPos cp = chunk_pos(geo, sg.shard_base, ci);
-        const bool vec = vec_ok(p, cp);
+        In<CH> x;
+        float mst[CH];
+        const ChunkPos cp = chunk_pos<CH>(geo, sg.shard_base, ci);
+        const bool vec = vec_ok<CH>(p, cp);
         load_in(x, p, cp, vec);
         load_master(mst, p, cp, vec);
         float dm = 0.f, dv = 0.f;
@@ -543,6 +629,8 @@ __global__ void __launch_bounds__(256) k_step_huge(StepArgs a) {
 // mode 0: one output `out`; mode 1: grad_shard and param_shard of states[y].
 __global__ void __launch_bounds__(256) k_runs(RunArgs r, const uint16_t* const* grad_ptrs, uint16_t* out,
                                               const ve_shard_state* states, int mode) {
+    constexpr int V = 8;                        // bf16 per 16-byte vector
+    constexpr int PER = kRunTile / (256 * V);   // vectors per thread
     const int64_t tile = blockIdx.x;
     const int ri = r.tile_run[tile];
     const Run rn = r.runs[ri];
@@ -560,26 +648,23 @@ __global__ void __launch_bounds__(256) k_runs(RunArgs r, const uint16_t* const* 
     const VE_GLOBAL uint16_t* s = (const VE_GLOBAL uint16_t*)src;
     VE_GLOBAL uint16_t* d0 = (VE_GLOBAL uint16_t*)(o0 + rn.dst + t0);
     VE_GLOBAL uint16_t* d1 = o1 ? (VE_GLOBAL uint16_t*)(o1 + rn.dst + t0) : nullptr;
-    const int64_t i0 = (int64_t)threadIdx.x * kChunk;
-    if (i0 >= len) return;
-    if (aligned && i0 + kChunk <= len) {
-        u32x4 a = u32x4{0, 0, 0, 0}, b = a;
-        if (s) {
-            a = *(const VE_GLOBAL u32x4*)(s + i0);
-            b = *(const VE_GLOBAL u32x4*)(s + i0 + 8);
-        }
-        ((VE_GLOBAL u32x4*)(d0 + i0))[0] = a;
-        ((VE_GLOBAL u32x4*)(d0 + i0))[1] = b;
-        if (d1) {
-            ((VE_GLOBAL u32x4*)(d1 + i0))[0] = a;
-            ((VE_GLOBAL u32x4*)(d1 + i0))[1] = b;
-        }
-    } else {
-        const int64_t n = min((int64_t)kChunk, len - i0);
-        for (int64_t k = 0; k < n; ++k) {
-            const uint16_t v = s ? s[i0 + k] : (uint16_t)0;
-            d0[i0 + k] = v;
-            if (d1) d1[i0 + k] = v;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        // vector q*256 + tid: each wave-wide access is 1 KB contiguous
+        const int64_t i0 = ((int64_t)q * 256 + threadIdx.x) * V;
+        if (i0 >= len) break;
+        if (aligned && i0 + V <= len) {
+            u32x4 a = u32x4{0, 0, 0, 0};
+            if (s) a = ldv<VE_NONTEMPORAL>((const VE_GLOBAL u32x4*)(s + i0));
+            stv<VE_NONTEMPORAL>((VE_GLOBAL u32x4*)(d0 + i0), a);
+            if (d1) stv<VE_NONTEMPORAL>((VE_GLOBAL u32x4*)(d1 + i0), a);
+        } else {
+            const int64_t n = min((int64_t)V, len - i0);
+            for (int64_t k = 0; k < n; ++k) {
+                const uint16_t v = s ? s[i0 + k] : (uint16_t)0;
+                d0[i0 + k] = v;
+                if (d1) d1[i0 + k] = v;
+            }
         }
     }
 }
@@ -599,40 +684,25 @@ hipError_t launch_step_small(const StepArgs& a, int n_states, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int T, int CPT>
+template <int T, int GPT>
 static hipError_t launch_wg_t(const StepArgs& a, int n_states, hipStream_t s) {
-    hipLaunchKernelGGL((k_step_wg<T, CPT>), dim3(grid_x(a.work.total), n_states), dim3(T), lds_bytes(a.work), s, a);
+    hipLaunchKernelGGL((k_step_wg<T, GPT>), dim3(grid_x(a.work.total), n_states), dim3(T), lds_bytes(a.work), s, a);
     return hipGetLastError();
 }
 
-#define VE_WG_CASES(T)                                              \
-    switch (cpt) {                                                  \
-        case 1: return launch_wg_t<T, 1>(a, n_states, s);           \
-        case 2: return launch_wg_t<T, 2>(a, n_states, s);           \
-        case 3: return launch_wg_t<T, 3>(a, n_states, s);           \
-        case 4: return launch_wg_t<T, 4>(a, n_states, s);           \
-        case 5: return launch_wg_t<T, 5>(a, n_states, s);           \
-        case 6: return launch_wg_t<T, 6>(a, n_states, s);           \
-        case 7: return launch_wg_t<T, 7>(a, n_states, s);           \
-        case 8: return launch_wg_t<T, 8>(a, n_states, s);           \
-        case 9: return launch_wg_t<T, 9>(a, n_states, s);           \
-        case 10: return launch_wg_t<T, 10>(a, n_states, s);         \
-        case 11: return launch_wg_t<T, 11>(a, n_states, s);         \
-        case 12: return launch_wg_t<T, 12>(a, n_states, s);         \
-        default: return hipErrorInvalidValue;                       \
-    }
-
-bool wg_config_supported(int threads, int cpt) {
-    return (threads == 256 || threads == 512 || threads == 1024) && cpt >= 1 && cpt <= kWgMaxChunksPerThread;
+bool wg_config_supported(int threads, int gpt) {
+#define VE_WG_CASE(T, G) if (threads == T && gpt == G) return true;
+    VE_WG_SHAPES(VE_WG_CASE)
+#undef VE_WG_CASE
+    return false;
 }
 
-hipError_t launch_step_wg(const StepArgs& a, int n_states, int threads, int cpt, hipStream_t s) {
-    if (threads == 256) { VE_WG_CASES(256) }
-    if (threads == 512) { VE_WG_CASES(512) }
-    if (threads == 1024) { VE_WG_CASES(1024) }
+hipError_t launch_step_wg(const StepArgs& a, int n_states, int threads, int gpt, hipStream_t s) {
+#define VE_WG_CASE(T, G) if (threads == T && gpt == G) return launch_wg_t<T, G>(a, n_states, s);
+    VE_WG_SHAPES(VE_WG_CASE)
+#undef VE_WG_CASE
     return hipErrorInvalidValue;
 }
-#undef VE_WG_CASES
 
 hipError_t launch_step_huge(const StepArgs& a, int n_states, hipStream_t s) {
     hipLaunchKernelGGL(k_step_huge, dim3(grid_x(a.work.total), n_states), dim3(256), lds_bytes(a.work), s, a);
