@@ -266,20 +266,34 @@ RunArgs run_args(const ve_plan& P, const HostRuns& h) {
     return r;
 }
 
-WorkList work_list(const ve_plan& P, const HostWork& w) {
-    WorkList l;
-    l.seg_idx = P.dptr<int32_t>(w.off_idx);
-    l.prefix = P.dptr<int64_t>(w.off_pref);
-    l.n = (int32_t)w.seg_idx.size();
-    l.total = w.prefix.back();
-    return l;
+// Point the step arguments at one class's work list (small-block path).
+void set_work(StepArgs& a, const ve_plan& P, const HostWork& w) {
+    a.work.seg_idx = P.dptr<int32_t>(w.off_idx);
+    a.work.prefix = P.dptr<int64_t>(w.off_pref);
+    a.work.n = (int32_t)w.seg_idx.size();
+    a.work.total = w.prefix.back();
+    a.n_inline = 0;
+}
+
+// Copy segments [i0, i1) of a class's work list into the step arguments
+// (workgroup paths); returns the number of work items of the slice.
+int64_t set_inline(StepArgs& a, const RankTables& rt, const HostWork& w, size_t i0, size_t i1) {
+    a.n_inline = (int32_t)(i1 - i0);
+    for (size_t i = i0; i < i1; ++i) {
+        a.inl_segs[i - i0] = rt.segs[(size_t)w.seg_idx[i]];
+        a.inl_prefix[i - i0] = w.prefix[i] - w.prefix[i0];
+    }
+    a.inl_prefix[i1 - i0] = w.prefix[i1] - w.prefix[i0];
+    a.work.total = a.inl_prefix[i1 - i0];
+    return a.work.total;
 }
 
 // Workgroup path shape: threads and 4-element groups per thread for blocks
-// of up to `groups` groups.  Default: 512 threads (two workgroups per CU at
-// the usual register count) with the smallest instantiated groups-per-thread
-// that covers the block; 256 threads for small blocks, 1024 for the largest.
-// VE_WG_THREADS / VE_WG_GPT override it (launch-shape tuning).
+// of up to `groups` groups.  Measured on MI355X, 6..12 groups per thread
+// stream best (fewer leave the per-block prologue exposed, more add
+// per-thread serial work): take the largest workgroup that gives each thread
+// at least 6 groups, else 256 threads.  VE_WG_THREADS / VE_WG_GPT override
+// it (launch-shape tuning).
 void wg_shape(int32_t groups, int& threads, int& gpt) {
     const char* et = std::getenv("VE_WG_THREADS");
     const char* eg = std::getenv("VE_WG_GPT");
@@ -288,15 +302,25 @@ void wg_shape(int32_t groups, int& threads, int& gpt) {
         gpt = std::atoi(eg);
         if (wg_config_supported(threads, gpt) && (int64_t)threads * gpt >= groups) return;
     }
+    auto fit = [&](int t, int& g) {
+        for (g = (int)ceil_div(groups, t); g <= 32; ++g)
+            if (wg_config_supported(t, g)) return true;
+        return false;
+    };
+    for (int t : {1024, 512}) {
+        int g;
+        if (ceil_div(groups, t) >= 6 && fit(t, g)) {
+            threads = t;
+            gpt = g;
+            return;
+        }
+    }
     for (int t : {256, 512, 1024}) {
-        if (t == 256 && groups > 256 * 4) continue;
-        const int need = (int)ceil_div(groups, t);
-        for (int g = need; g <= 32; ++g) {
-            if (wg_config_supported(t, g)) {
-                threads = t;
-                gpt = g;
-                return;
-            }
+        int g;
+        if (fit(t, g)) {
+            threads = t;
+            gpt = g;
+            return;
         }
     }
     threads = 1024;  // unreachable for blocks classed kWg (groups <= kWgMaxGroups)
@@ -494,16 +518,23 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
     if (rt.wg.prefix.back() > 0) {
         int threads, gpt;
         wg_shape(rt.wg_max_groups, threads, gpt);
-        a.work = work_list(*plan, rt.wg);
-        if ((st = launch_status(launch_step_wg(a, n_states, threads, gpt, s), "workgroup step")) != VE_OK) return st;
+        for (size_t i0 = 0; i0 < rt.wg.seg_idx.size(); i0 += kInlineSegs) {
+            const size_t i1 = std::min(rt.wg.seg_idx.size(), i0 + (size_t)kInlineSegs);
+            if (set_inline(a, rt, rt.wg, i0, i1) == 0) continue;
+            if ((st = launch_status(launch_step_wg(a, n_states, threads, gpt, s), "workgroup step")) != VE_OK)
+                return st;
+        }
     }
     if (rt.small.prefix.back() > 0) {
-        a.work = work_list(*plan, rt.small);
+        set_work(a, *plan, rt.small);
         if ((st = launch_status(launch_step_small(a, n_states, s), "small-block step")) != VE_OK) return st;
     }
     if (rt.huge.prefix.back() > 0) {
-        a.work = work_list(*plan, rt.huge);
-        if ((st = launch_status(launch_step_huge(a, n_states, s), "large-block step")) != VE_OK) return st;
+        for (size_t i0 = 0; i0 < rt.huge.seg_idx.size(); i0 += kInlineSegs) {
+            const size_t i1 = std::min(rt.huge.seg_idx.size(), i0 + (size_t)kInlineSegs);
+            if (set_inline(a, rt, rt.huge, i0, i1) == 0) continue;
+            if ((st = launch_status(launch_step_huge(a, n_states, s), "large-block step")) != VE_OK) return st;
+        }
     }
     if (rt.pad.tile_prefix.back() > 0) {
         if ((st = launch_status(launch_runs_pad(run_args(*plan, rt.pad), states, n_states, s), "padding fill")) != VE_OK)

@@ -29,9 +29,11 @@ constexpr int kWgMaxThreads = 1024;
     X(512, 20) X(512, 24)                                                                       \
     X(1024, 2) X(1024, 4) X(1024, 6) X(1024, 8) X(1024, 10) X(1024, 12) X(1024, 14) X(1024, 16)
 constexpr int64_t kWgMaxGroups = 1024 * 16;
-// Entries of a work-prefix table staged in LDS (larger tables are searched
-// in global memory).
-constexpr int kLdsPrefixCap = 2048;
+// The workgroup-path kernels take their segment table in the kernel
+// arguments (read through the scalar cache), so a workgroup finds its block
+// without a dependent chain of memory loads; a class with more segments is
+// launched in slices of at most this many.
+constexpr int kInlineSegs = 16;
 // Elements per tile of the run copier (copy-in and padding fill).
 constexpr int kRunTile = 4096;
 
@@ -88,6 +90,9 @@ struct StepArgs {
     const Seg* segs;               // device, this rank's segments
     WorkList work;
     StepScalars sc;
+    int32_t n_inline;              // workgroup paths: segments given inline below
+    int64_t inl_prefix[kInlineSegs + 1];  // work-item prefix, inl_prefix[0] = 0
+    Seg inl_segs[kInlineSegs];
 };
 
 struct RunArgs {

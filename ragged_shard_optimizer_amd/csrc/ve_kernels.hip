@@ -130,6 +130,15 @@ __device__ __forceinline__ void stv(VE_GLOBAL V* p, V v) {
     else *p = v;
 }
 
+// Wave-uniform reads of device memory the reading workgroup alone may later
+// change (the gradient pointer table, a block's old scales) go through the
+// constant address space, i.e. scalar loads.
+#define VE_CONST __attribute__((address_space(4)))
+template <class T>
+__device__ __forceinline__ T sload(const T* p) {
+    return *(const VE_CONST T*)p;
+}
+
 struct Ptrs {
     const VE_GLOBAL uint16_t* __restrict__ grad;
     VE_GLOBAL uint16_t* __restrict__ grad_shard;
@@ -140,9 +149,10 @@ struct Ptrs {
     bool aligned;  // every base pointer 16-byte aligned
 };
 
+template <bool UNIFORM = false>
 __device__ __forceinline__ Ptrs make_ptrs(const ve_shard_state& st, int tensor) {
     Ptrs p;
-    const uint16_t* g = st.grad_ptrs[tensor];
+    const uint16_t* g = UNIFORM ? sload(st.grad_ptrs + tensor) : st.grad_ptrs[tensor];
     p.aligned = (((uintptr_t)g | (uintptr_t)st.grad_shard | (uintptr_t)st.master | (uintptr_t)st.m_q |
                   (uintptr_t)st.v_q | (uintptr_t)st.param_shard) & 15) == 0;
     p.grad = (const VE_GLOBAL uint16_t*)g;
@@ -413,26 +423,36 @@ __device__ __forceinline__ void make_opaque(In<CH>& x) {
 }
 
 // ---------------------------------------------------------------------------
-// work lookup: the segmented descriptor table of the rank's class, staged in
-// LDS when it fits.  Returns the list index i with prefix[i] <= w < prefix[i+1]
-// and the item's offset inside that segment.  Contains a barrier: call from
-// converged code with every thread of the workgroup.
-extern __shared__ int64_t s_pref[];  // dynamic: prefix table (n + 1 entries) when staged
+// work lookup: which segment holds work item w (a block, or a wave of small
+// blocks), and the item's offset inside that segment.  w is wave-uniform, so
+// every load here is a scalar (or read-first-lane) load.
 
-__device__ __forceinline__ int find_item(const WorkList& wl, int64_t w, int64_t& local) {
-    const bool staged = wl.n <= kLdsPrefixCap;
-    if (staged) {
-        for (int i = threadIdx.x; i <= wl.n; i += blockDim.x) s_pref[i] = wl.prefix[i];
-    }
-    __syncthreads();
-    const int64_t* pref = staged ? s_pref : wl.prefix;
-    int lo = 0, hi = wl.n - 1;  // largest i with pref[i] <= w
+// Workgroup paths: the slice of segments handled by this launch is in the
+// kernel arguments.
+__device__ __forceinline__ Seg find_inline(const StepArgs& a, int64_t w, int64_t& local) {
+    int i = 0;
+#pragma unroll
+    for (int j = 1; j < kInlineSegs; ++j)
+        if (j < a.n_inline && a.inl_prefix[j] <= w) i = j;
+    local = w - a.inl_prefix[i];
+    return a.inl_segs[i];
+}
+
+// Small-block path: binary search in the segmented descriptor table in
+// device memory (classes can hold hundreds of segments).
+__device__ __forceinline__ Seg find_global(const StepArgs& a, int64_t w, int64_t& local) {
+    int lo = 0, hi = a.work.n - 1;  // largest i with prefix[i] <= w
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (pref[mid] <= w) lo = mid; else hi = mid - 1;
+        if (a.work.prefix[mid] <= w) lo = mid; else hi = mid - 1;
     }
-    local = w - pref[lo];
-    return lo;
+    local = w - a.work.prefix[lo];
+    const int32_t* src = reinterpret_cast<const int32_t*>(a.segs + a.work.seg_idx[lo]);
+    Seg sg;
+    int32_t* dst = reinterpret_cast<int32_t*>(&sg);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(Seg) / 4); ++i) dst[i] = __builtin_amdgcn_readfirstlane(src[i]);
+    return sg;
 }
 
 // ---------------------------------------------------------------------------
@@ -440,12 +460,12 @@ __device__ __forceinline__ int find_item(const WorkList& wl, int64_t w, int64_t&
 __global__ void __launch_bounds__(256) k_step_small(StepArgs a) {
     constexpr int CH = kSmallChunk;
     const int lane = threadIdx.x & 63;
-    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+    if (gw >= a.work.total) return;  // whole waves; the kernel has no barrier
     int64_t local;
-    const int si = find_item(a.work, min(gw, a.work.total - 1), local);
-    if (gw >= a.work.total) return;  // whole waves only; no barrier follows
+    const Seg sg = find_global(a, gw, local);
     const ve_shard_state st = a.states[blockIdx.y];
-    const Seg sg = a.segs[a.work.seg_idx[si]];
     const int G = sg.group;
     const int64_t k = local * (64 / G) + lane / G;
     const int li = lane & (G - 1);
@@ -461,8 +481,8 @@ __global__ void __launch_bounds__(256) k_step_small(StepArgs a) {
         geo = block_geo<CH>(sg, k);
         has = li < geo.nchunks;
         if (has) {
-            sm = st.m_scale[geo.blk];
-            sv = st.v_scale[geo.blk];
+            sm = ((const VE_GLOBAL float*)st.m_scale)[geo.blk];
+            sv = ((const VE_GLOBAL float*)st.v_scale)[geo.blk];
             float mst[CH];
             cp = chunk_pos<CH>(geo, sg.shard_base, li);
             vec = vec_ok<CH>(p, cp);
@@ -477,8 +497,8 @@ __global__ void __launch_bounds__(256) k_step_small(StepArgs a) {
         const float im = am > 0.f ? 127.0f / am : 0.f;
         const float iv = av > 0.f ? 127.0f / av : 0.f;
         if (li == 0) {
-            st.m_scale[geo.blk] = am / 127.0f;
-            st.v_scale[geo.blk] = av / 127.0f;
+            ((VE_GLOBAL float*)st.m_scale)[geo.blk] = am / 127.0f;
+            ((VE_GLOBAL float*)st.v_scale)[geo.blk] = av / 127.0f;
         }
         if (has) {
             make_opaque(x);
@@ -487,8 +507,11 @@ __global__ void __launch_bounds__(256) k_step_small(StepArgs a) {
     }
 }
 
+#ifndef VE_WG_ROTATE
+#define VE_WG_ROTATE 1
+#endif
 #ifndef VE_MASTER_AHEAD
-#define VE_MASTER_AHEAD 2  // master loads issued this many groups ahead of their update
+#define VE_MASTER_AHEAD 0  // 0: per shape (4 groups ahead, 8 from 12 groups per thread)
 #endif
 
 // One workgroup per block; thread tid owns groups tid, tid + T, ... of
@@ -502,23 +525,29 @@ __global__ void __launch_bounds__(256) k_step_small(StepArgs a) {
 template <int T, int GPT>
 __global__ void __launch_bounds__(T) k_step_wg(StepArgs a) {
     constexpr int CH = kWgChunk;
-    constexpr int MA = VE_MASTER_AHEAD < GPT ? VE_MASTER_AHEAD : GPT;
+    constexpr int MA0 = VE_MASTER_AHEAD > 0 ? VE_MASTER_AHEAD : (GPT >= 12 ? 8 : 4);
+    constexpr int MA = MA0 < GPT ? MA0 : GPT;
     __shared__ float s_red[2][T / 64];
     const int tid = threadIdx.x;
     int64_t local;
-    const int si = find_item(a.work, blockIdx.x, local);
+    const Seg sg = find_inline(a, blockIdx.x, local);
     const ve_shard_state st = a.states[blockIdx.y];
-    const Seg sg = a.segs[a.work.seg_idx[si]];
     const Geo geo = block_geo<CH>(sg, local);
-    const Ptrs p = make_ptrs(st, sg.tensor);
-    const float sm = st.m_scale[geo.blk], sv = st.v_scale[geo.blk];
+    const Ptrs p = make_ptrs<true>(st, sg.tensor);
+    const float sm = sload(st.m_scale + geo.blk), sv = sload(st.v_scale + geo.blk);
 
     In<CH> x[GPT];
     float mst[MA + 1][CH];  // ring of master values in flight
     float am = 0.f, av = 0.f;
+    // Register slot c holds group tid + ((c + rot) mod GPT) * T: neighbouring
+    // workgroups start their sweeps at different offsets of their blocks, so
+    // the sweep fronts of the resident blocks (whose starts are a multiple of
+    // the block size apart) do not all address the same memory channels.
+    const int rot = VE_WG_ROTATE ? (int)(blockIdx.x % GPT) : 0;
+    auto slot_chunk = [&](int c) { return tid + ((c + rot) % GPT) * T; };
 #pragma unroll
     for (int c = 0; c < GPT; ++c) {
-        const int ci = tid + c * T;
+        const int ci = slot_chunk(c);
         if (ci < geo.nchunks) {
             const ChunkPos cp = chunk_pos<CH>(geo, sg.shard_base, ci);
             const bool vec = vec_ok<CH>(p, cp);
@@ -529,13 +558,13 @@ __global__ void __launch_bounds__(T) k_step_wg(StepArgs a) {
 #pragma unroll
     for (int c = 0; c < GPT; ++c) {
         if (c + MA < GPT) {
-            const int cn = tid + (c + MA) * T;
+            const int cn = slot_chunk(c + MA);
             if (cn < geo.nchunks) {
                 const ChunkPos cpn = chunk_pos<CH>(geo, sg.shard_base, cn);
                 load_master(mst[(c + MA) % (MA + 1)], p, cpn, vec_ok<CH>(p, cpn));
             }
         }
-        const int ci = tid + c * T;
+        const int ci = slot_chunk(c);
         if (ci < geo.nchunks) {
             const ChunkPos cp = chunk_pos<CH>(geo, sg.shard_base, ci);
             phase1(x[c], mst[c % (MA + 1)], p, cp, vec_ok<CH>(p, cp), sm, sv, a.sc, am, av);
@@ -558,12 +587,12 @@ __global__ void __launch_bounds__(T) k_step_wg(StepArgs a) {
     const float im = am > 0.f ? 127.0f / am : 0.f;
     const float iv = av > 0.f ? 127.0f / av : 0.f;
     if (tid == 0) {
-        st.m_scale[geo.blk] = am / 127.0f;
-        st.v_scale[geo.blk] = av / 127.0f;
+        ((VE_GLOBAL float*)st.m_scale)[geo.blk] = am / 127.0f;
+        ((VE_GLOBAL float*)st.v_scale)[geo.blk] = av / 127.0f;
     }
 #pragma unroll
     for (int c = 0; c < GPT; ++c) {
-        const int ci = tid + c * T;
+        const int ci = slot_chunk(c);
         if (ci < geo.nchunks) {
             make_opaque(x[c]);
             const ChunkPos cp = chunk_pos<CH>(geo, sg.shard_base, ci);
@@ -578,12 +607,11 @@ __global__ void __launch_bounds__(256) k_step_huge(StepArgs a) {
     __shared__ float s_red[2][4];
     const int tid = threadIdx.x, T = blockDim.x;
     int64_t local;
-    const int si = find_item(a.work, blockIdx.x, local);
+    const Seg sg = find_inline(a, blockIdx.x, local);
     const ve_shard_state st = a.states[blockIdx.y];
-    const Seg sg = a.segs[a.work.seg_idx[si]];
     const Geo geo = block_geo<CH>(sg, local);
-    const Ptrs p = make_ptrs(st, sg.tensor);
-    const float sm = st.m_scale[geo.blk], sv = st.v_scale[geo.blk];
+    const Ptrs p = make_ptrs<true>(st, sg.tensor);
+    const float sm = sload(st.m_scale + geo.blk), sv = sload(st.v_scale + geo.blk);
     float am = 0.f, av = 0.f;
     for (int ci = tid; ci < geo.nchunks; ci += T) {
         In<CH> x;
@@ -620,8 +648,8 @@ __global__ void __launch_bounds__(256) k_step_huge(StepArgs a) {
         phase2(x, p, cp, vec, sm, sv, im, iv, a.sc);
     }
     if (tid == 0) {
-        st.m_scale[geo.blk] = am / 127.0f;
-        st.v_scale[geo.blk] = av / 127.0f;
+        ((VE_GLOBAL float*)st.m_scale)[geo.blk] = am / 127.0f;
+        ((VE_GLOBAL float*)st.v_scale)[geo.blk] = av / 127.0f;
     }
 }
 
@@ -674,19 +702,16 @@ __global__ void __launch_bounds__(256) k_runs(RunArgs r, const uint16_t* const* 
 // ---------------------------------------------------------------------------
 // launchers
 static inline unsigned grid_x(int64_t n) { return (unsigned)n; }
-static inline size_t lds_bytes(const WorkList& w) {
-    return w.n <= kLdsPrefixCap ? sizeof(int64_t) * (size_t)(w.n + 1) : 0;
-}
 
 hipError_t launch_step_small(const StepArgs& a, int n_states, hipStream_t s) {
     const int64_t wgs = (a.work.total + 3) / 4;
-    hipLaunchKernelGGL(k_step_small, dim3(grid_x(wgs), n_states), dim3(256), lds_bytes(a.work), s, a);
+    hipLaunchKernelGGL(k_step_small, dim3(grid_x(wgs), n_states), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 template <int T, int GPT>
 static hipError_t launch_wg_t(const StepArgs& a, int n_states, hipStream_t s) {
-    hipLaunchKernelGGL((k_step_wg<T, GPT>), dim3(grid_x(a.work.total), n_states), dim3(T), lds_bytes(a.work), s, a);
+    hipLaunchKernelGGL((k_step_wg<T, GPT>), dim3(grid_x(a.work.total), n_states), dim3(T), 0, s, a);
     return hipGetLastError();
 }
 
@@ -705,7 +730,7 @@ hipError_t launch_step_wg(const StepArgs& a, int n_states, int threads, int gpt,
 }
 
 hipError_t launch_step_huge(const StepArgs& a, int n_states, hipStream_t s) {
-    hipLaunchKernelGGL(k_step_huge, dim3(grid_x(a.work.total), n_states), dim3(256), lds_bytes(a.work), s, a);
+    hipLaunchKernelGGL(k_step_huge, dim3(grid_x(a.work.total), n_states), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
