@@ -204,7 +204,10 @@ def main():
         "ms_per_step_wall": round(ms_wall, 5),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None if traffic is None else round(traffic / (ms / 1e3) / 1e9, 2)},
+                     # measured HBM bytes per launch (rocprofv3 counters on these kernel sources)
+                     # over the same launch time, comparable with "achieved"
+                     "traffic": None if traffic is None else round(traffic / (ms / 1e3) / 1e9, 2),
+                     "traffic_bytes_per_launch": None if traffic is None else round(traffic)},
     }
     del states, table, buckets
     torch.cuda.empty_cache()
