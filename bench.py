@@ -28,31 +28,50 @@ METRIC = "fused shard-step HBM GB/s and params/s on 1 GPU; % of HBM peak"
 BYTES_PER_ELEM = 18   # grad read 2 + grad-slice write 2 + master r/w 8 + codes r/w 4 + bf16 param write 2
 BYTES_PER_BLOCK = 16  # two fp32 scales read + written
 BYTES_PER_PAD = 4     # two bf16 zero writes
+# DBuffer group operations: algorithmic bytes per tensor element (padding: one bf16 write)
+GROUP_BYTES = {"zero": 2, "scale": 4, "accumulate": 6}
+GROUP_PAD_BYTES = 2
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+STEP_SOURCES = ("ve_kernels.hip", "ve_device.h", "ve_internal.h", "ve_host.cpp")
+GROUP_SOURCES = ("ve_group.hip", "ve_device.h", "ve_internal.h", "ve_host.cpp")
+
+
+def kernel_source_hash(files=STEP_SOURCES):
     h = hashlib.sha256()
-    for f in ("ve_kernels.hip", "ve_internal.h", "ve_host.cpp"):
+    for f in files:
         with open(os.path.join(ROOT, "ragged_shard_optimizer_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"shard_step_{workload}_traffic.json")
+def _profile(name, files):
+    """A committed rocprofv3 counter summary, if it was taken on the current
+    kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         d = json.load(fh)
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    if d.get("kernel_source_hash") != kernel_source_hash(files):
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the step kernel from the committed counters."""
+    d = _profile(f"shard_step_{workload}_traffic.json", STEP_SOURCES)
+    return None if d is None else d.get("hbm_bytes_per_launch")
+
+
+def measured_group_traffic(workload):
+    """{op: HBM bytes per launch} of the group kernels from the committed counters."""
+    d = _profile(f"dbuffer_group_{workload}_traffic.json", GROUP_SOURCES)
+    return None if d is None else d.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(cfg, lay, rank, budget_s=12.0):
@@ -94,6 +113,40 @@ def cpu_baseline(cfg, lay, rank, budget_s=12.0):
                       f"buckets stepped in turn), {el:.1f} s wall, single thread"}
 
 
+def time_group_ops(torch, ve, plan, rank, states, lay, valid, steps, warmup, traffic=None):
+    """Each DBuffer group operation over every bucket's rank chunk (the
+    states' gradient slices) in one launch: HIP events on the launch stream,
+    algorithmic bytes per launch over the mean launch time."""
+    stream = torch.cuda.current_stream()
+    bufs = [st["grad_shard"] for st in states]
+    gts = [st["grad_table"] for st in states]
+    S, nbk = lay.shard, len(states)
+    out = {}
+    for name, op, alpha in (("zero", ve.GROUP_ZERO, 0.0), ("scale", ve.GROUP_SCALE, 0.999),
+                            ("accumulate", ve.GROUP_ACCUMULATE, 1.0)):
+        table = ve.group_table(plan, rank, bufs, gts if op == ve.GROUP_ACCUMULATE else None)
+        for _ in range(warmup):
+            plan.group_op(rank, op, alpha, table, stream)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            plan.group_op(rank, op, alpha, table, stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+        per_elem = GROUP_BYTES[name]
+        alg = nbk * (S * per_elem if name == "zero" else per_elem * valid + GROUP_PAD_BYTES * (S - valid))
+        gbs = alg / (ms / 1e3) / 1e9
+        t = None if not traffic or name not in traffic else traffic[name] / (ms / 1e3) / 1e9
+        out[name] = {"ms": round(ms, 5), "alg_bytes": alg, "achieved": round(gbs, 2),
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if t is None else round(t, 2)}
+        log(f"[bench] group {name}: {ms:.4f} ms, {gbs:.1f} GB/s")
+    return {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s", "buckets": nbk,
+            "bytes_per_elem": GROUP_BYTES, "bytes_per_pad": GROUP_PAD_BYTES, "ops": out}
+
+
 def copy_ceiling(torch, dev, gib, reps=10):
     """A plain device-to-device copy (torch's copy kernel) of ``gib`` GiB:
     read + write bytes over its time -- the practical streaming ceiling."""
@@ -122,6 +175,7 @@ def main():
     ap.add_argument("--workload", default="llama", choices=["llama", "gptoss", "deepseek", "adversarial"])
     ap.add_argument("--buckets", type=int, default=None, help="override the number of buckets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-group-ops", action="store_true", help="skip timing the DBuffer group operations")
     ap.add_argument("--copy-gib", type=float, default=2.0,
                     help="size of the plain device copy that measures the copy ceiling (0: skip)")
     args = ap.parse_args()
@@ -209,6 +263,9 @@ def main():
                      "traffic": None if traffic is None else round(traffic / (ms / 1e3) / 1e9, 2),
                      "traffic_bytes_per_launch": None if traffic is None else round(traffic)},
     }
+    if not args.no_group_ops:
+        out["group_ops"] = time_group_ops(torch, ve, plan, rank, states, lay, valid, 10, 2,
+                                          measured_group_traffic(args.workload))
     del states, table, buckets
     torch.cuda.empty_cache()
     if args.copy_gib > 0:

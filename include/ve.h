@@ -12,7 +12,11 @@
  *      RaggedShard quantisation block, so no rank needs another rank's data
  *      (talk notes, "1. RaggedShard": sync-free block-wise quantisation;
  *      "Case study: 8-bit Adam and distributed Muon");
- *   3. write-back of the bf16 parameter shard for the next all-gather.
+ *   3. write-back of the bf16 parameter shard for the next all-gather;
+ *
+ * and the DBuffer's other group operations (zero, scale, accumulate) over a
+ * rank chunk or a whole bucket, and the structure-aware planner that
+ * produces bucket layouts (host only).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -148,6 +152,63 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
  * *elem_end = 0 and VE_OK. */
 ve_status ve_dbuffer_slice(const ve_plan* plan, int32_t rank, int32_t tensor,
                            int64_t* shard_offset, int64_t* elem_start, int64_t* elem_end);
+
+/* DBuffer group operations: one operation applied to every tensor of a
+ * chunk (or of the whole bucket) in one launch, the way the DBuffer fuses
+ * identical operations such as add, scale and zero across its tensors
+ * (talk notes, "3. DBuffer"; Dutch summary, "C. Distributed Buffer"). */
+typedef enum {
+    VE_GROUP_ZERO = 0,       /* x = 0 on every element, padding included */
+    VE_GROUP_SCALE = 1,      /* x = alpha * x on tensor elements (e.g. averaging) */
+    VE_GROUP_ACCUMULATE = 2  /* x = x + alpha * g on tensor elements (gradient accumulation) */
+} ve_group_op;
+
+/* One bucket operand of a group operation.  Both members are device pointers. */
+typedef struct {
+    uint16_t* bucket;                 /* bf16 [S] (rank >= 0) or [fsdp_size*S] (rank == -1), in/out */
+    const uint16_t* const* grad_ptrs; /* VE_GROUP_ACCUMULATE: device array as in ve_shard_state
+                                         (tensor k's element e at grad_ptrs[k][e]; entries of
+                                         tensors without a piece in the range may be NULL);
+                                         ignored by the other operations (may be NULL) */
+} ve_group_operand;
+
+/* Apply `op` to n_operands buckets that share this plan (operands is a
+ * DEVICE array [n_operands]; one launch).  rank >= 0: each bucket is rank's
+ * chunk, bf16 [S]; rank == -1: the whole bucket, bf16 [fsdp_size*S].
+ * Arithmetic per tensor element, in fp32: the bf16 operands are widened,
+ * one IEEE operation is applied (scale: the product alpha*x; accumulate: the
+ * fused multiply-add fma(alpha, g, x), one rounding) and the result is
+ * stored as bf16, rounded to nearest even.  Padding is written 0 by every
+ * operation.  NaN inputs give NaN outputs (payload unspecified).  Buckets
+ * must not overlap each other or the gradients.  Errors: unknown op, rank
+ * out of [-1, fsdp_size), n_operands < 0 or a NULL operands array with
+ * n_operands > 0 give VE_ERR_INVALID_ARG; n_operands == 0 is a no-op. */
+ve_status ve_dbuffer_group_op(const ve_plan* plan, int32_t rank, int32_t op, float alpha,
+                              const ve_group_operand* operands, int32_t n_operands, void* stream);
+
+/* Structure-aware bucket planner (talk notes, "2. Structure-aware planning
+ * algorithm"; Dutch summary, "2B"; Korean summary, "2.2").  Host only: no
+ * device is touched.  Reads rows, cols and block_rows of the host array
+ * specs[n_tensors] (block_cols and offset are ignored on input) and writes
+ * every tensor's offset and *shard_elems = S; the result passes
+ * ve_plan_load's checks for fsdp_size.
+ *   Order: by shard unit (min(block_rows, rows) * cols elements), largest
+ *   first, ties in input order.  Placement: each tensor at the smallest
+ *   multiple of `align` after the previous tensor at which every chunk
+ *   boundary inside it falls on one of its unit boundaries; padding only
+ *   between tensors.  S: the smallest multiple of `align` for which the
+ *   ordered tensors fit in fsdp_size chunks; for this order no smaller S
+ *   admits a valid placement.
+ *   *lower_bound (may be NULL): the smallest S any layout, in any order,
+ *   could have: at least total/fsdp_size rounded up to `align`, and a
+ *   multiple of the unit of every tensor longer than 2S (such a tensor
+ *   crosses two chunk boundaries wherever it lies).
+ * Errors: NULL specs or shard_elems, n_tensors < 1, fsdp_size < 1, align
+ * outside [1, 2^20] or a non-positive shape or block: VE_ERR_INVALID_ARG;
+ * a bucket beyond 2^52 / fsdp_size elements: VE_ERR_UNSUPPORTED.  On error
+ * the outputs are not written. */
+ve_status ve_plan_layout(ve_tensor_spec* specs, int32_t n_tensors, int32_t fsdp_size, int64_t align,
+                         int64_t* shard_elems, int64_t* lower_bound);
 
 /* Thread-local message of this thread's last failing call ("" if none). */
 const char* ve_last_error(void);

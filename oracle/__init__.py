@@ -62,6 +62,11 @@ def lib():
         L.ora_slice.argtypes = [P, C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int, P, P, P]
         L.ora_copy_in.restype = None
         L.ora_copy_in.argtypes = [P, C.c_int, C.c_int, C.c_int64, C.c_int64, P, P, P]
+        L.ora_group_op.argtypes = [P, C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int, C.c_float, P, P, P]
+        L.ora_plan_min_shard.restype = C.c_int64
+        L.ora_plan_min_shard.argtypes = [P, P, P, C.c_int, C.c_int64, C.c_int64, C.c_int64]
+        L.ora_plan_min_shard_any_order.restype = C.c_int64
+        L.ora_plan_min_shard_any_order.argtypes = [P, P, C.c_int, C.c_int64, C.c_int64, C.c_int64]
         L.ora_quantize.restype = None
         L.ora_quantize.argtypes = [P, C.c_int64, P, P]
         L.ora_shard_step.argtypes = [P, C.c_int, C.c_int, C.c_int64, C.c_int64, P, P,
@@ -148,6 +153,48 @@ def copy_in(spec, m: int, S: int, rank: int, grads, bases=None) -> np.ndarray:
     out = np.empty(m * S if rank < 0 else S, dtype=np.uint16)
     lib().ora_copy_in(arr, n, m, S, rank, ptrs, _ptr(base), _ptr(out))
     return out
+
+
+GROUP_ZERO, GROUP_SCALE, GROUP_ACCUMULATE = 0, 1, 2
+
+
+def group_op(spec, m: int, S: int, rank: int, op: int, alpha: float, bucket: np.ndarray, grads=None,
+             bases=None) -> np.ndarray:
+    """DBuffer group operation on ``bucket`` (uint16 bf16 bits, length S for
+    ``rank`` >= 0, m*S for ``rank`` = -1), updated in place.  ``op`` is
+    GROUP_ZERO, GROUP_SCALE or GROUP_ACCUMULATE; ``alpha`` is rounded to fp32
+    first; ``grads`` (accumulate only) are the per-parameter bf16 gradients,
+    as for ``copy_in``."""
+    arr, n = _specs(spec)
+    if grads is None:
+        grads = [None] * n
+    ptrs, base, keep = _grad_table(grads, bases, n)
+    if bucket.dtype != np.uint16 or not bucket.flags.c_contiguous:
+        raise TypeError("bucket: need contiguous uint16")
+    rc = lib().ora_group_op(arr, n, m, S, rank, int(op), float(np.float32(alpha)), ptrs, _ptr(base),
+                            _ptr(bucket))
+    if rc != 0:
+        raise OracleError(lib().ora_last_error().decode())
+    return bucket
+
+
+def plan_min_shard(sizes, units, m: int, align: int, s_max: int, order=None) -> int:
+    """Exhaustive search: the smallest S (multiple of ``align``, <= s_max) at
+    which tensors of ``sizes`` elements and shard ``units`` fit in m chunks,
+    in ``order`` (default: as given), or over every order when ``order`` is
+    "any" (at most 8 tensors).  0 if no S up to s_max works.  Tiny inputs
+    only: the search is exponential."""
+    n = np.ascontiguousarray(sizes, dtype=np.int64)
+    u = np.ascontiguousarray(units, dtype=np.int64)
+    if n.shape != u.shape or n.ndim != 1 or len(n) < 1:
+        raise ValueError("sizes and units: equal-length 1-D arrays")
+    if isinstance(order, str) and order == "any":
+        r = lib().ora_plan_min_shard_any_order(_ptr(n), _ptr(u), len(n), m, align, s_max)
+        if r < 0:
+            raise OracleError(lib().ora_last_error().decode())
+        return int(r)
+    o = np.arange(len(n), dtype=np.intc) if order is None else np.ascontiguousarray(order, dtype=np.intc)
+    return int(lib().ora_plan_min_shard(_ptr(n), _ptr(u), _ptr(o), len(n), m, align, s_max))
 
 
 def shard_step(spec, m: int, S: int, rank: int, grads, state: dict, hp: dict, t: int,

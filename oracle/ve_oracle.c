@@ -33,7 +33,16 @@
  *
  *  - Write-back of the parameter shard as bf16 for the next all-gather.
  *
- * Arithmetic: every update is carried out in double precision.  Stored
+ *  - Bucket planning: the smallest chunk length S at which the tensors fit
+ *    (in a given order, or in any order) by exhaustive search over offsets.
+ *
+ *  - DBuffer group operations (zero, scale, accumulate) applied to every
+ *    tensor of a chunk or of the whole bucket at once (talk notes
+ *    "3. DBuffer"; Dutch summary "C"), in fp32 as described at
+ *    ora_group_op.
+ *
+ * Arithmetic: every update of the shard step is carried out in double
+ * precision.  Stored
  * results take their storage type: fp32 master, fp32 scales, bf16 param
  * (round-to-nearest-even of the stored fp32 master).  The int8 codes are
  * integers decided by floating point, so that decision is taken in the
@@ -216,6 +225,120 @@ void ora_quantize(const float* x, int64_t n, int8_t* q, float* scale) {
         if (y < -127.0f) y = -127.0f;
         q[i] = (int8_t)y;
     }
+}
+
+/* ---- DBuffer group operations ---------------------------------------------- */
+/* One operation over every tensor of rank r's chunk (r = -1: the whole
+ * bucket), the way the DBuffer applies an identical operation to all of its
+ * tensors at once (talk notes "3. DBuffer"; Dutch summary "C": add, scale
+ * and zero fused across tensors):
+ *   op 0 zero:       every element of the chunk, padding included, becomes 0;
+ *   op 1 scale:      x = alpha * x on tensor elements (gradient averaging);
+ *   op 2 accumulate: x = x + alpha * g on tensor elements, g the
+ *                    per-parameter gradient (gradient accumulation);
+ * and padding becomes 0 for every op.  The pages fix no precision; the
+ * reading taken is that of elementwise arithmetic on bf16 tensors in a
+ * PyTorch system: the operands are widened to fp32, the operation is one
+ * IEEE fp32 operation (a product, or a fused multiply-add with a single
+ * rounding), and the result is rounded to bf16 to nearest-even. */
+int ora_group_op(const ora_tensor* t, int n, int m, int64_t S, int64_t r, int op, float alpha,
+                 const uint16_t* const* grads, const int64_t* grad_base, uint16_t* bucket) {
+    if (op < 0 || op > 2) return fail("unknown group op %d", op);
+    if (r < -1 || r >= m) return fail("rank %lld out of range [-1, %d)", (long long)r, m);
+    const int64_t len = r < 0 ? (int64_t)m * S : S;
+    const int64_t c0 = r < 0 ? 0 : r * S;
+    char* covered = (char*)calloc((size_t)len, 1);
+    if (!covered) return fail("out of host memory");
+    for (int k = 0; k < n; ++k) {
+        int64_t lo = 0, hi = t[k].rows * t[k].cols;
+        if (r >= 0 && !piece(&t[k], S, r, &lo, &hi)) continue;
+        for (int64_t e = lo; e < hi; ++e) {
+            const int64_t pos = t[k].offset + e - c0;
+            covered[pos] = 1;
+            const float x = bf16_to_f32(bucket[pos]);
+            if (op == 0) {
+                bucket[pos] = 0;
+            } else if (op == 1) {
+                bucket[pos] = f32_to_bf16(alpha * x);
+            } else {
+                const float g = bf16_to_f32(grads[k][e - grad_base[k]]);
+                bucket[pos] = f32_to_bf16(fmaf(alpha, g, x));
+            }
+        }
+    }
+    for (int64_t j = 0; j < len; ++j)
+        if (!covered[j]) bucket[j] = 0;
+    free(covered);
+    return 0;
+}
+
+/* ---- bucket planning by exhaustive search ----------------------------------- */
+/* A layout of tensors (n_k elements, shard unit u_k elements) in a bucket of
+ * m chunks of S elements is valid when every offset is a multiple of `align`,
+ * the tensors do not overlap and end by m*S, and every chunk boundary j*S
+ * strictly inside tensor k lies a multiple of u_k from its first element
+ * (talk notes "1. RaggedShard" and "2. Structure-aware planning";
+ * padding only between tensors).  The search below tries every offset of
+ * every tensor, so it only serves tiny buckets. */
+static int boundaries_ok(int64_t o, int64_t n, int64_t u, int64_t m, int64_t S) {
+    for (int64_t j = 1; j < m; ++j) {
+        const int64_t b = j * S;
+        if (b > o && b < o + n && (b - o) % u != 0) return 0;
+    }
+    return 1;
+}
+
+/* Can tensors order[i..cnt) be placed at or after `cursor`, in this order? */
+static int place_from(const int64_t* n, const int64_t* u, const int* order, int i, int cnt, int64_t cursor,
+                      int64_t m, int64_t S, int64_t align, int64_t rest) {
+    if (i == cnt) return 1;
+    const int k = order[i];
+    int64_t o = (cursor + align - 1) / align * align;
+    for (; o + rest <= m * S; o += align) {
+        if (!boundaries_ok(o, n[k], u[k], m, S)) continue;
+        if (place_from(n, u, order, i + 1, cnt, o + n[k], m, S, align, rest - n[k])) return 1;
+    }
+    return 0;
+}
+
+/* Smallest S (a multiple of align, at most s_max) for which the tensors fit
+ * in the given order; 0 if none does. */
+int64_t ora_plan_min_shard(const int64_t* n, const int64_t* u, const int* order, int cnt, int64_t m,
+                           int64_t align, int64_t s_max) {
+    int64_t total = 0;
+    for (int i = 0; i < cnt; ++i) total += n[i];
+    for (int64_t S = align; S <= s_max; S += align) {
+        if (m * S < total) continue;
+        if (place_from(n, u, order, 0, cnt, 0, m, S, align, total)) return S;
+    }
+    return 0;
+}
+
+static int next_permutation(int* a, int cnt) {
+    int i = cnt - 2;
+    while (i >= 0 && a[i] >= a[i + 1]) --i;
+    if (i < 0) return 0;
+    int j = cnt - 1;
+    while (a[j] <= a[i]) --j;
+    int t = a[i]; a[i] = a[j]; a[j] = t;
+    for (int l = i + 1, r = cnt - 1; l < r; ++l, --r) { t = a[l]; a[l] = a[r]; a[r] = t; }
+    return 1;
+}
+
+/* Smallest S over every order of the tensors (cnt <= 8). */
+int64_t ora_plan_min_shard_any_order(const int64_t* n, const int64_t* u, int cnt, int64_t m, int64_t align,
+                                     int64_t s_max) {
+    if (cnt < 1 || cnt > 8) return fail("any-order search needs 1..8 tensors"), -1;
+    int order[8];
+    for (int i = 0; i < cnt; ++i) order[i] = i;
+    int64_t best = 0;
+    do {
+        const int64_t lim = best ? best - align : s_max;
+        if (lim < align) break;
+        const int64_t S = ora_plan_min_shard(n, u, order, cnt, m, align, lim);
+        if (S) best = S;
+    } while (next_permutation(order, cnt));
+    return best;
 }
 
 /* ---- the shard step --------------------------------------------------------- */

@@ -7,8 +7,10 @@ been built (``python -m ragged_shard_optimizer_amd.build``); there is no
 fallback implementation.
 
 Names follow the C ABI: ``plan_load`` / ``Plan.query`` / ``Plan.slice`` /
-``Plan.copy_in`` / ``Plan.step`` wrap ``ve_plan_load``, ``ve_plan_query``,
-``ve_dbuffer_slice``, ``ve_dbuffer_copy_in`` and ``ve_shard_adam8bit_step``.
+``Plan.copy_in`` / ``Plan.step`` / ``Plan.group_op`` / ``plan_layout`` wrap
+``ve_plan_load``, ``ve_plan_query``, ``ve_dbuffer_slice``,
+``ve_dbuffer_copy_in``, ``ve_shard_adam8bit_step``, ``ve_dbuffer_group_op``
+and ``ve_plan_layout``.
 """
 
 from __future__ import annotations
@@ -27,7 +29,11 @@ _STATUS = {0: "VE_OK", 1: "VE_ERR_INVALID_ARG", 2: "VE_ERR_LAYOUT", 3: "VE_ERR_O
 
 # every symbol include/ve.h declares
 EXPORTS = ("ve_plan_load", "ve_plan_free", "ve_plan_query", "ve_dbuffer_copy_in",
-           "ve_shard_adam8bit_step", "ve_dbuffer_slice", "ve_last_error")
+           "ve_shard_adam8bit_step", "ve_dbuffer_slice", "ve_dbuffer_group_op", "ve_plan_layout",
+           "ve_last_error")
+
+# ve_group_op
+GROUP_ZERO, GROUP_SCALE, GROUP_ACCUMULATE = 0, 1, 2
 
 
 class VeError(RuntimeError):
@@ -67,6 +73,8 @@ def lib() -> C.CDLL:
         L.ve_dbuffer_copy_in.argtypes = [P, C.c_int32, P, P, P]
         L.ve_shard_adam8bit_step.argtypes = [P, C.c_int32, P, C.c_int32, P, C.c_int64, P]
         L.ve_dbuffer_slice.argtypes = [P, C.c_int32, C.c_int32, P, P, P]
+        L.ve_dbuffer_group_op.argtypes = [P, C.c_int32, C.c_int32, C.c_float, P, C.c_int32, P]
+        L.ve_plan_layout.argtypes = [P, C.c_int32, C.c_int32, C.c_int64, P, P]
         for name in EXPORTS[:-1]:
             getattr(L, name).restype = C.c_int
         _lib = L
@@ -158,6 +166,36 @@ class Plan:
                                             len(states), C.byref(hp), int(step), _stream_handle(stream)))
 
 
+    def group_op(self, rank: int, op: int, alpha: float, table, stream=None):
+        """``ve_dbuffer_group_op`` over a :class:`GroupTable` built for the
+        same ``rank``."""
+        if table.rank != rank or table.plan is not self:
+            raise ValueError("group table was built for another plan or rank")
+        if op == GROUP_ACCUMULATE and not table.has_grads:
+            raise ValueError("accumulate needs a gradient table for every bucket")
+        _check(lib().ve_dbuffer_group_op(self._h, int(rank), int(op), float(alpha),
+                                         C.c_void_p(table.table.data_ptr()), len(table),
+                                         _stream_handle(stream)))
+
+
+def plan_layout(shapes, fsdp_size: int, align: int = 16):
+    """``ve_plan_layout``: ``shapes`` is an int array ``[n, >=3]`` of (rows,
+    cols, block_rows[, block_cols]); returns ``(specs, S, lower_bound)`` with
+    ``specs`` int64 ``[n, 5]`` (rows, cols, block_rows, block_cols, offset),
+    ready for :class:`Plan`."""
+    sh = np.asarray(shapes, dtype=np.int64)
+    if sh.ndim != 2 or sh.shape[1] < 3 or len(sh) < 1:
+        raise ValueError("shapes: need an [n, >=3] array of (rows, cols, block_rows[, block_cols])")
+    arr = (TensorSpec * len(sh))()
+    for i, row in enumerate(sh):
+        bc = int(row[3]) if sh.shape[1] > 3 else int(row[1])
+        arr[i] = TensorSpec(int(row[0]), int(row[1]), int(row[2]), bc, 0)
+    S, lb = C.c_int64(), C.c_int64()
+    _check(lib().ve_plan_layout(arr, len(sh), int(fsdp_size), int(align), C.byref(S), C.byref(lb)))
+    specs = np.array([[a.rows, a.cols, a.block_rows, a.block_cols, a.offset] for a in arr], dtype=np.int64)
+    return specs, S.value, lb.value
+
+
 def plan_load(specs, fsdp_size, shard_elems, device=0) -> Plan:
     return Plan(specs, fsdp_size, shard_elems, device)
 
@@ -243,6 +281,49 @@ def state_table(plan: Plan, rank: int, states, device=None) -> StateTable:
     if device is None:
         device = states[0]["master"].device
     return StateTable(plan, rank, states, device)
+
+
+class GroupTable:
+    """Device array of ``ve_group_operand`` records: one bf16 bucket (rank
+    chunk of S elements, or the whole bucket for rank -1) per entry, with an
+    optional gradient table (needed by accumulate)."""
+
+    def __init__(self, plan: Plan, rank: int, buckets, grad_tables, device):
+        import torch
+        need = plan.shard_elems * (plan.fsdp_size if rank < 0 else 1)
+        if grad_tables is None:
+            grad_tables = [None] * len(buckets)
+        if len(grad_tables) != len(buckets):
+            raise ValueError("one gradient table per bucket")
+        rows = []
+        for b, gt in zip(buckets, grad_tables):
+            _require_buffer(b, need, 2, "bucket")
+            if gt is not None:
+                if len(gt.grads) != plan.n_tensors:
+                    raise ValueError("grad table length != number of tensors in the plan")
+                for k in range(plan.n_tensors):
+                    sl = plan.slice(rank, k)
+                    g = gt.grads[k]
+                    if sl is not None and (g is None or g.numel() < sl[2]):
+                        raise ValueError(f"tensor {k} has elements in the range but its gradient is "
+                                         "missing or short")
+            rows.append([b.data_ptr(), 0 if gt is None else gt.table.data_ptr()])
+        self.plan, self.rank = plan, int(rank)
+        self.has_grads = all(gt is not None for gt in grad_tables)
+        self.keep = (list(buckets), list(grad_tables))
+        self.table = torch.tensor(rows if rows else [[0, 0]], dtype=torch.int64, device=device).reshape(-1)
+        self.n = len(rows)
+
+    def __len__(self):
+        return self.n
+
+
+def group_table(plan: Plan, rank: int, buckets, grad_tables=None, device=None) -> GroupTable:
+    """``buckets``: contiguous 16-bit device tensors; ``grad_tables``: one
+    GradTable per bucket (accumulate) or None."""
+    if device is None:
+        device = buckets[0].device
+    return GroupTable(plan, rank, buckets, grad_tables, device)
 
 
 def new_state(plan: Plan, rank: int, grad_table: GradTable, master, device=None) -> dict:

@@ -26,10 +26,10 @@
 using namespace ve;
 
 namespace {
-
 thread_local std::string g_err;
+}  // namespace
 
-ve_status fail(ve_status st, const char* fmt, ...) {
+ve_status ve::fail(ve_status st, const char* fmt, ...) {
     char buf[512];
     va_list ap;
     va_start(ap, fmt);
@@ -38,6 +38,8 @@ ve_status fail(ve_status st, const char* fmt, ...) {
     g_err = buf;
     return st;
 }
+
+namespace {
 
 // host-side copies of one work list / run table, with byte offsets into the
 // single device allocation filled in at upload
@@ -473,11 +475,33 @@ ve_status ve_dbuffer_copy_in(const ve_plan* plan, int32_t rank, const uint16_t* 
     for (const Run& r : h.runs) needs_grads |= r.tensor >= 0;
     if (needs_grads && !grad_ptrs) return fail(VE_ERR_INVALID_ARG, "grad_ptrs is NULL");
     if (h.tile_prefix.back() == 0) return VE_OK;
-    if (h.tile_prefix.back() > INT32_MAX) return fail(VE_ERR_UNSUPPORTED, "copy of more than 2^31 tiles");
+    if (h.tile_prefix.back() > kMaxRunTiles)
+        return fail(VE_ERR_UNSUPPORTED, "%lld tiles exceed one launch", (long long)h.tile_prefix.back());
     DeviceGuard g(plan->device);
     if (!g.ok) return fail(VE_ERR_DEVICE, "hipSetDevice(%d) failed", plan->device);
     (void)hipGetLastError();
     return launch_status(launch_runs_copy(run_args(*plan, h), grad_ptrs, bucket, (hipStream_t)stream), "copy-in");
+}
+
+ve_status ve_dbuffer_group_op(const ve_plan* plan, int32_t rank, int32_t op, float alpha,
+                              const ve_group_operand* operands, int32_t n_operands, void* stream) {
+    if (!plan) return fail(VE_ERR_INVALID_ARG, "plan is NULL");
+    if (rank < -1 || rank >= plan->m) return fail(VE_ERR_INVALID_ARG, "rank %d outside [-1, %d)", rank, plan->m);
+    if (op != VE_GROUP_ZERO && op != VE_GROUP_SCALE && op != VE_GROUP_ACCUMULATE)
+        return fail(VE_ERR_INVALID_ARG, "unknown group op %d", op);
+    if (n_operands < 0 || n_operands > 65535)
+        return fail(VE_ERR_INVALID_ARG, "n_operands %d outside [0, 65535]", n_operands);
+    if (n_operands > 0 && !operands) return fail(VE_ERR_INVALID_ARG, "operands is NULL");
+    if (!plan->dev) return fail(VE_ERR_INVALID_ARG, "host-only plan (device -1) cannot launch kernels");
+    const HostRuns& h = rank < 0 ? plan->whole : plan->ranks[(size_t)rank].copy;
+    if (n_operands == 0 || h.tile_prefix.back() == 0) return VE_OK;
+    if (h.tile_prefix.back() > kMaxRunTiles)
+        return fail(VE_ERR_UNSUPPORTED, "%lld tiles exceed one launch", (long long)h.tile_prefix.back());
+    DeviceGuard g(plan->device);
+    if (!g.ok) return fail(VE_ERR_DEVICE, "hipSetDevice(%d) failed", plan->device);
+    (void)hipGetLastError();
+    return launch_status(launch_group(run_args(*plan, h), op, alpha, operands, n_operands, (hipStream_t)stream),
+                         "group op");
 }
 
 ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_shard_state* states, int32_t n_states,
@@ -494,8 +518,11 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
         return fail(VE_ERR_INVALID_ARG, "lr / eps / weight_decay must be finite and eps > 0");
     if (!plan->dev) return fail(VE_ERR_INVALID_ARG, "host-only plan (device -1) cannot launch kernels");
     const RankTables& rt = plan->ranks[(size_t)rank];
-    for (const HostWork* w : {&rt.small, &rt.wg, &rt.huge})
-        if (w->prefix.back() > INT32_MAX) return fail(VE_ERR_UNSUPPORTED, "more than 2^31 work items on rank %d", rank);
+    int threads = 256, gpt = 1;
+    if (rt.wg.prefix.back() > 0) wg_shape(rt.wg_max_groups, threads, gpt);
+    if ((rt.small.prefix.back() + 3) / 4 * 256 > kMaxGridItems || rt.wg.prefix.back() * threads > kMaxGridItems ||
+        rt.huge.prefix.back() * 256 > kMaxGridItems || rt.pad.tile_prefix.back() > kMaxRunTiles)
+        return fail(VE_ERR_UNSUPPORTED, "rank %d has more blocks than one launch covers", rank);
 
     StepArgs a{};
     a.states = states;
@@ -516,8 +543,6 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
     hipStream_t s = (hipStream_t)stream;
     ve_status st;
     if (rt.wg.prefix.back() > 0) {
-        int threads, gpt;
-        wg_shape(rt.wg_max_groups, threads, gpt);
         for (size_t i0 = 0; i0 < rt.wg.seg_idx.size(); i0 += kInlineSegs) {
             const size_t i1 = std::min(rt.wg.seg_idx.size(), i0 + (size_t)kInlineSegs);
             if (set_inline(a, rt, rt.wg, i0, i1) == 0) continue;

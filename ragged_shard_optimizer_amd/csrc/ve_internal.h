@@ -36,6 +36,9 @@ constexpr int64_t kWgMaxGroups = 1024 * 16;
 constexpr int kInlineSegs = 16;
 // Elements per tile of the run copier (copy-in and padding fill).
 constexpr int kRunTile = 4096;
+// A dispatch's grid is at most 2^32 - 1 work-items per dimension.
+constexpr int64_t kMaxGridItems = 0xFFFFFFFFll;
+constexpr int64_t kMaxRunTiles = kMaxGridItems / 256;  // run kernels: 256 threads per tile
 
 enum SegClass : int32_t { kSmall = 0, kWg = 1, kHuge = 2 };
 
@@ -114,6 +117,14 @@ hipError_t launch_runs_copy(const RunArgs& r, const uint16_t* const* grad_ptrs, 
 // Padding fill of the step: zero grad_shard and param_shard of every state.
 hipError_t launch_runs_pad(const RunArgs& r, const ve_shard_state* states, int n_states,
                            hipStream_t s);
+
+// Record the thread-local message ve_last_error() returns; returns `st`.
+ve_status fail(ve_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// DBuffer group operation `op` (a ve_group_op) over the run tiles, for
+// ops[0 .. n_ops) (ve_group.hip).
+hipError_t launch_group(const RunArgs& r, int op, float alpha, const ve_group_operand* ops, int n_ops,
+                        hipStream_t s);
 
 // (threads, groups per thread) pairs instantiated for the workgroup path.
 bool wg_config_supported(int threads, int groups_per_thread);

@@ -40,6 +40,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ve_device.h"
 #include "ve_internal.h"
 
 namespace ve {
@@ -47,17 +48,8 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // scalar helpers
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float code_at(uint32_t w, int b) {
     return (float)((int32_t)(w << (24 - 8 * b)) >> 24);  // sign-extended byte b
-}
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    f32x2 v = {a, b};
-    bf16x2 h = __builtin_convertvector(v, bf16x2);  // v_cvt_pk_bf16_f32, RNE
-    return __builtin_bit_cast(uint32_t, h);
 }
 
 // Keep the compiler from proving a value equal to an earlier one (forces the
@@ -100,35 +92,14 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// global-memory access
-// Pointers read from the state table are generic; the buffers live in device
-// global memory, so address them as such (global_* instead of flat_* accesses).
-#define VE_GLOBAL __attribute__((address_space(1)))
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+// global-memory access (vector types and ldv/stv in ve_device.h)
 
-// Vector accesses.  Every byte is touched once; where a wave-wide access
-// covers whole cache lines (lane-contiguous layouts) it carries a
-// non-temporal (streaming) hint.  Where lanes are strided (16-element
-// chunks), partial lines are merged in the L2 across accesses, which the
-// hint would defeat, so those stay plain.
-#ifndef VE_NONTEMPORAL
-#define VE_NONTEMPORAL 1
-#endif
+// Every byte is touched once; where a wave-wide access covers whole cache
+// lines (lane-contiguous layouts) it carries a non-temporal (streaming) hint.
+// Where lanes are strided (16-element chunks), partial lines are merged in
+// the L2 across accesses, which the hint would defeat, so those stay plain.
 template <int CH>
 constexpr bool kStream = VE_NONTEMPORAL && CH == kWgChunk;
-
-template <bool NT, class V>
-__device__ __forceinline__ V ldv(const VE_GLOBAL V* p) {
-    if constexpr (NT) return __builtin_nontemporal_load(p);
-    else return *p;
-}
-template <bool NT, class V>
-__device__ __forceinline__ void stv(VE_GLOBAL V* p, V v) {
-    if constexpr (NT) __builtin_nontemporal_store(v, p);
-    else *p = v;
-}
 
 // Wave-uniform reads of device memory the reading workgroup alone may later
 // change (the gradient pointer table, a block's old scales) go through the

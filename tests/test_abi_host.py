@@ -117,6 +117,24 @@ def test_step_argument_checks():
                               C.byref(C.c_int64())) == ve.VE_ERR_INVALID_ARG
 
 
+def test_group_op_argument_checks():
+    # host-only plan: every call is refused before anything reaches a device
+    p = ve.Plan(np.array([[4, 8, 1, 8, 0]]), 2, 16, device=-1)
+    L = ve.lib()
+    ops = C.c_void_p(16)   # never dereferenced: every call below is refused first
+    assert L.ve_dbuffer_group_op(None, 0, ve.GROUP_ZERO, 1.0, ops, 1, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_dbuffer_group_op(p.handle, 2, ve.GROUP_ZERO, 1.0, ops, 1, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_dbuffer_group_op(p.handle, -2, ve.GROUP_ZERO, 1.0, ops, 1, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_dbuffer_group_op(p.handle, 0, 3, 1.0, ops, 1, None) == ve.VE_ERR_INVALID_ARG
+    assert "unknown group op" in ve.lib().ve_last_error().decode()
+    assert L.ve_dbuffer_group_op(p.handle, 0, -1, 1.0, ops, 1, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_dbuffer_group_op(p.handle, 0, ve.GROUP_SCALE, 1.0, ops, -1, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_dbuffer_group_op(p.handle, 0, ve.GROUP_SCALE, 1.0, ops, 65536, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_dbuffer_group_op(p.handle, 0, ve.GROUP_SCALE, 1.0, None, 1, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_dbuffer_group_op(p.handle, -1, ve.GROUP_ACCUMULATE, 1.0, ops, 1, None) == ve.VE_ERR_INVALID_ARG
+    assert "host-only" in ve.lib().ve_last_error().decode()
+
+
 def test_tensor_spanning_many_ranks_and_unsorted_specs():
     # specs in any order; a 1-D tensor crossing several chunks of 128-element units
     specs = np.array([[2048, 1, 128, 1, 256], [100, 1, 1, 1, 0], [37, 2, 1, 2, 112]])

@@ -137,3 +137,64 @@ def test_adversarial_whole_bucket_copy_in():
     for r in (0, lay.largest_rank(), lay.fsdp - 1):
         want = oracle.copy_in(lay.spec_array(), lay.fsdp, lay.shard, r, host)
         assert np.array_equal(got[r * lay.shard:(r + 1) * lay.shard], want)
+
+
+def _bf16_noise(n, seed):
+    import torch
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return torch.randn(n, generator=g, device=DEV).to(torch.bfloat16).view(torch.int16)
+
+
+@pytest.mark.parametrize("name", ["llama", "gptoss", "deepseek", "adversarial"])
+def test_full_size_group_ops(name):
+    """Accumulate and scale over every bucket's rank chunk in one launch (the
+    shape the benchmark times); sampled buckets compared whole with the
+    oracle, bit for bit."""
+    import torch
+    import ragged_shard_optimizer_amd as ve
+    cfg, lay = layout_of(name)
+    rank = lay.largest_rank()
+    spec, m, S = lay.spec_array(), lay.fsdp, lay.shard
+    plan = ve.Plan(spec, m, S, device=0)
+    buckets = device_buckets(cfg, lay, rank, DEV)
+    gts = [ve.grad_pointer_table(g, DEV) for g, _ in buckets]
+    bufs = [_bf16_noise(S, 1000 + b) for b in range(len(buckets))]
+    sample_b = sorted({0, len(buckets) // 2, len(buckets) - 1})
+    pieces = list(lay.chunk_intervals(rank))
+    for op, alpha in ((oracle.GROUP_ACCUMULATE, 0.5), (oracle.GROUP_SCALE, 1.0 / 3.0)):
+        pre = {b: bufs[b].cpu().numpy().view(np.uint16).copy() for b in sample_b}
+        table = ve.group_table(plan, rank, bufs, gts if op == oracle.GROUP_ACCUMULATE else None)
+        _say(f"[gpu] full-size group op {op} {name}: rank {rank}, {len(bufs)} buckets, S={S}")
+        plan.group_op(rank, op, alpha, table)
+        torch.cuda.synchronize()
+        for b in sample_b:
+            grads, bases = None, None
+            if op == oracle.GROUP_ACCUMULATE:
+                grads, bases = [None] * len(lay.tensors), [0] * len(lay.tensors)
+                for k, lo, hi, _dst in pieces:
+                    grads[k] = buckets[b][0][k][lo:hi].cpu().numpy().view(np.uint16)
+                    bases[k] = lo
+            want = oracle.group_op(spec, m, S, rank, op, alpha, pre[b], grads=grads, bases=bases)
+            got = bufs[b].cpu().numpy().view(np.uint16)
+            bad = np.nonzero(got != want)[0]
+            assert bad.size == 0, (name, op, b, bad[:5])
+    del bufs, gts, buckets
+    torch.cuda.empty_cache()
+
+
+def test_adversarial_whole_bucket_group_scale():
+    """Scale of the whole adversarial bucket (10,000 tensors, ~727 M
+    elements) against the oracle, bit for bit."""
+    import torch
+    import ragged_shard_optimizer_amd as ve
+    cfg, lay = layout_of("adversarial")
+    spec, m, S = lay.spec_array(), lay.fsdp, lay.shard
+    plan = ve.Plan(spec, m, S, device=0)
+    buf = _bf16_noise(lay.bucket_elems, 77)
+    pre = buf.cpu().numpy().view(np.uint16).copy()
+    _say(f"[gpu] whole-bucket group scale: {lay.bucket_elems} elements")
+    plan.group_op(-1, oracle.GROUP_SCALE, -0.75, ve.group_table(plan, -1, [buf]))
+    torch.cuda.synchronize()
+    want = oracle.group_op(spec, m, S, -1, oracle.GROUP_SCALE, -0.75, pre)
+    assert np.array_equal(buf.cpu().numpy().view(np.uint16), want)
