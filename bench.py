@@ -147,6 +147,40 @@ def time_group_ops(torch, ve, plan, rank, states, lay, valid, steps, warmup, tra
             "bytes_per_elem": GROUP_BYTES, "bytes_per_pad": GROUP_PAD_BYTES, "ops": out}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def time_muon(torch, ve, dev, rows=8192, cols=28672, steps=3, warmup=1):
+    """Muon's Newton-Schulz iteration (5 steps) on one gathered matrix of the
+    LLaMA-3-70B MLP shape, HIP events on the launch stream; flops counted the
+    minimal way (symmetric products at half cost)."""
+    from oracle import muon
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    G = torch.randn(rows, cols, generator=g, device=dev).to(torch.bfloat16).view(torch.int16)
+    out = torch.empty_like(G)
+    ws = torch.empty(ve.muon_workspace_bytes(rows, cols), dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        ve.muon_newton_schulz(G, out, 5, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        ve.muon_newton_schulz(G, out, 5, workspace=ws, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    flops = muon.flops(rows, cols)
+    tf = flops / (ms / 1e3) / 1e12
+    log(f"[bench] muon newton-schulz {rows}x{cols}: {ms:.3f} ms, {tf:.1f} TFLOP/s")
+    del G, out, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"Muon Newton-Schulz, 5 steps, one {rows}x{cols} bf16 matrix (LLaMA-3-70B MLP)",
+            "bound": "mfma", "ms": round(ms, 4), "flops": flops, "achieved": round(tf, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def copy_ceiling(torch, dev, gib, reps=10):
     """A plain device-to-device copy (torch's copy kernel) of ``gib`` GiB:
     read + write bytes over its time -- the practical streaming ceiling."""
@@ -176,6 +210,7 @@ def main():
     ap.add_argument("--buckets", type=int, default=None, help="override the number of buckets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-group-ops", action="store_true", help="skip timing the DBuffer group operations")
+    ap.add_argument("--no-muon", action="store_true", help="skip timing Muon's Newton-Schulz iteration")
     ap.add_argument("--copy-gib", type=float, default=2.0,
                     help="size of the plain device copy that measures the copy ceiling (0: skip)")
     args = ap.parse_args()
@@ -268,6 +303,8 @@ def main():
                                           measured_group_traffic(args.workload))
     del states, table, buckets
     torch.cuda.empty_cache()
+    if not args.no_muon:
+        out["muon"] = time_muon(torch, ve, dev)
     if args.copy_gib > 0:
         out["copy_ceiling"] = copy_ceiling(torch, dev, args.copy_gib)
         out["copy_ceiling_frac"] = round(gbs / out["copy_ceiling"]["gbs"], 4)

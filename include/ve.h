@@ -15,8 +15,9 @@
  *   3. write-back of the bf16 parameter shard for the next all-gather;
  *
  * and the DBuffer's other group operations (zero, scale, accumulate) over a
- * rank chunk or a whole bucket, and the structure-aware planner that
- * produces bucket layouts (host only).
+ * rank chunk or a whole bucket, the structure-aware planner that produces
+ * bucket layouts (host only), and Muon's Newton-Schulz iteration on one
+ * gathered matrix (MFMA).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -209,6 +210,43 @@ ve_status ve_dbuffer_group_op(const ve_plan* plan, int32_t rank, int32_t op, flo
  * the outputs are not written. */
 ve_status ve_plan_layout(ve_tensor_spec* specs, int32_t n_tensors, int32_t fsdp_size, int64_t align,
                          int64_t* shard_elems, int64_t* lower_bound);
+
+/* Muon's Newton-Schulz orthogonalisation of one gathered 2-D matrix, the
+ * dense work of the root rank in distributed Muon (talk notes, "Case study:
+ * 8-bit Adam and distributed Muon": the full matrix is gathered on one rank,
+ * iterated and redistributed; Dutch summary, "Muon-optimalisator").  The
+ * iteration is the published Muon quintic: X0 = G / (|G|_F + eps) in the
+ * wide orientation (a tall G is transposed), then `steps` times
+ * A = X X^T, B = b A + c A A, X = a X + B X with (a, b, c) =
+ * (3.4445, -4.7750, 2.0315); the result is returned in G's orientation.
+ * Precision: X, A and B are bf16; products accumulate in fp32 on the MFMA
+ * units; each stored result is rounded once from fp32 to bf16 (nearest
+ * even); the Frobenius norm is accumulated in fp64 and 1/(|G|_F + eps) is
+ * rounded to fp32.
+ *   G, out: device, bf16 rows x cols row-major (out may not alias G or the
+ *   workspace).  steps in [0, 64] (0: out = bf16(G / (|G|_F + eps))).
+ *   workspace: device, 256-byte aligned, at least ve_muon_workspace_bytes
+ *   bytes, owned by the caller; its contents are scratch.
+ * Errors: NULL pointers, a non-positive shape, steps outside [0, 64], eps
+ * negative or not finite, a short or misaligned workspace:
+ * VE_ERR_INVALID_ARG; a matrix beyond one launch: VE_ERR_UNSUPPORTED;
+ * launch failures: VE_ERR_DEVICE. */
+ve_status ve_muon_workspace_bytes(int64_t rows, int64_t cols, int64_t* bytes);
+ve_status ve_muon_newton_schulz(const uint16_t* G, uint16_t* out, int64_t rows, int64_t cols, int32_t steps,
+                                float eps, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* The product kernel the iteration runs on: C = bf16(alpha * P Q^T + beta * D)
+ * with P (M x K), Q (N x K), D and C (M x N) and CT = C^T (N x M), all bf16
+ * row-major device arrays with leading dimensions ld* (>= the row length).
+ * D may be NULL (beta ignored); C or CT may be NULL, not both.  fp32
+ * accumulation on the MFMA units, one rounding to bf16.  symmetric != 0
+ * declares P Q^T symmetric (M == N, C required, D symmetric if given): only
+ * the output tiles on or above the diagonal are computed, each mirrored.
+ * Errors: NULL P or Q, no output, a non-positive size, a short leading
+ * dimension, symmetric without M == N and C: VE_ERR_INVALID_ARG. */
+ve_status ve_gemm_bf16_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, const uint16_t* D,
+                          int64_t ldd, uint16_t* C, int64_t ldc, uint16_t* CT, int64_t ldct, int64_t M, int64_t N,
+                          int64_t K, float alpha, float beta, int32_t symmetric, void* stream);
 
 /* Thread-local message of this thread's last failing call ("" if none). */
 const char* ve_last_error(void);

@@ -30,7 +30,7 @@ _STATUS = {0: "VE_OK", 1: "VE_ERR_INVALID_ARG", 2: "VE_ERR_LAYOUT", 3: "VE_ERR_O
 # every symbol include/ve.h declares
 EXPORTS = ("ve_plan_load", "ve_plan_free", "ve_plan_query", "ve_dbuffer_copy_in",
            "ve_shard_adam8bit_step", "ve_dbuffer_slice", "ve_dbuffer_group_op", "ve_plan_layout",
-           "ve_last_error")
+           "ve_muon_workspace_bytes", "ve_muon_newton_schulz", "ve_gemm_bf16_nt", "ve_last_error")
 
 # ve_group_op
 GROUP_ZERO, GROUP_SCALE, GROUP_ACCUMULATE = 0, 1, 2
@@ -75,6 +75,10 @@ def lib() -> C.CDLL:
         L.ve_dbuffer_slice.argtypes = [P, C.c_int32, C.c_int32, P, P, P]
         L.ve_dbuffer_group_op.argtypes = [P, C.c_int32, C.c_int32, C.c_float, P, C.c_int32, P]
         L.ve_plan_layout.argtypes = [P, C.c_int32, C.c_int32, C.c_int64, P, P]
+        L.ve_muon_workspace_bytes.argtypes = [C.c_int64, C.c_int64, P]
+        L.ve_muon_newton_schulz.argtypes = [P, P, C.c_int64, C.c_int64, C.c_int32, C.c_float, P, C.c_int64, P]
+        L.ve_gemm_bf16_nt.argtypes = [P, C.c_int64, P, C.c_int64, P, C.c_int64, P, C.c_int64, P, C.c_int64,
+                                      C.c_int64, C.c_int64, C.c_int64, C.c_float, C.c_float, C.c_int32, P]
         for name in EXPORTS[:-1]:
             getattr(L, name).restype = C.c_int
         _lib = L
@@ -194,6 +198,55 @@ def plan_layout(shapes, fsdp_size: int, align: int = 16):
     _check(lib().ve_plan_layout(arr, len(sh), int(fsdp_size), int(align), C.byref(S), C.byref(lb)))
     specs = np.array([[a.rows, a.cols, a.block_rows, a.block_cols, a.offset] for a in arr], dtype=np.int64)
     return specs, S.value, lb.value
+
+
+def muon_workspace_bytes(rows: int, cols: int) -> int:
+    n = C.c_int64()
+    _check(lib().ve_muon_workspace_bytes(int(rows), int(cols), C.byref(n)))
+    return n.value
+
+
+def _ptr_of(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def muon_newton_schulz(G, out, steps: int = 5, eps: float = 1e-7, workspace=None, stream=None):
+    """``ve_muon_newton_schulz``: ``G`` and ``out`` contiguous 2-D 16-bit
+    (bf16 bits) device tensors of the same shape; ``workspace`` a uint8
+    device tensor of at least :func:`muon_workspace_bytes` bytes (allocated
+    here if None)."""
+    import torch
+    if G.dim() != 2 or tuple(out.shape) != tuple(G.shape):
+        raise ValueError("G and out: 2-D tensors of the same shape")
+    rows, cols = G.shape
+    _require_buffer(G, rows * cols, 2, "G")
+    _require_buffer(out, rows * cols, 2, "out")
+    need = muon_workspace_bytes(rows, cols)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=G.device)
+    _require_buffer(workspace, need, 1, "workspace")
+    _check(lib().ve_muon_newton_schulz(_ptr_of(G), _ptr_of(out), rows, cols, int(steps), float(eps),
+                                       _ptr_of(workspace), workspace.numel(), _stream_handle(stream)))
+    return out
+
+
+def gemm_bf16_nt(P, Q, C=None, CT=None, D=None, alpha: float = 1.0, beta: float = 0.0, symmetric: bool = False,
+                 stream=None):
+    """``ve_gemm_bf16_nt`` on contiguous 2-D 16-bit device tensors:
+    C = bf16(alpha P Q^T + beta D), CT = C^T."""
+    M, K = P.shape
+    N, K2 = Q.shape
+    if K2 != K:
+        raise ValueError("P and Q must share the contraction length")
+    for t, shape, name in ((C, (M, N), "C"), (CT, (N, M), "CT"), (D, (M, N), "D")):
+        if t is not None:
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name}: shape {tuple(t.shape)} != {shape}")
+            _require_buffer(t, shape[0] * shape[1], 2, name)
+    _require_buffer(P, M * K, 2, "P")
+    _require_buffer(Q, N * K, 2, "Q")
+    _check(lib().ve_gemm_bf16_nt(_ptr_of(P), K, _ptr_of(Q), K, _ptr_of(D), N, _ptr_of(C), N, _ptr_of(CT), M,
+                                 M, N, K, float(alpha), float(beta), int(bool(symmetric)), _stream_handle(stream)))
 
 
 def plan_load(specs, fsdp_size, shard_elems, device=0) -> Plan:

@@ -1,0 +1,424 @@
+// ve_muon.hip -- Muon's Newton-Schulz orthogonalisation of one gathered 2-D
+// matrix on the MFMA units.
+//
+// Distributed Muon gathers each full 2-D update matrix on one root rank,
+// runs the Newton-Schulz iteration there and redistributes the result
+// (veScale-FSDP talk notes, "Case study: 8-bit Adam and distributed Muon";
+// Dutch summary, "Muon-optimalisator").  This file is the root rank's dense
+// work.  The iteration is the published Muon quintic (Jordan et al., 2024):
+//
+//   X0 = G / (|G|_F + eps), transposed to the wide orientation (m <= n);
+//   repeat: A = X X^T;  B = b A + c A A;  X <- a X + B X;
+//   (a, b, c) = (3.4445, -4.7750, 2.0315).
+//
+// Precision: X, A, B are stored as bf16; products accumulate in fp32 on the
+// MFMA units; every epilogue is fp32 and rounds once to bf16 (nearest even).
+// The Frobenius norm is accumulated in fp64.
+//
+// All three products are "NT" (C = P Q^T, both operands with contiguous
+// contraction index): X X^T directly; A A = A A^T since A is symmetric; and
+// B X = B (X^T)^T, which reads X^T -- so the step that produces X also
+// writes X^T from its epilogue.  X X^T and A A are symmetric: only tiles on
+// or above the diagonal are computed and each is mirrored.
+//
+// Product kernel (gfx950): 256 threads = 4 waves as 2 x 2, a 128 x 128 output
+// tile per workgroup, each wave 64 x 64 = 2 x 2 MFMA 32x32x16 bf16 tiles in
+// fp32 accumulators.  The contraction runs in steps of 64 through LDS, double
+// buffered: the next step's global loads are issued before the current
+// step's MFMAs, one barrier per step.  LDS rows are padded by 16 bytes so
+// that the 16-byte fragment reads of 16 consecutive rows hit distinct banks.
+//
+// MFMA 32x32x16 bf16 operand layout (lane l = 0..63): A fragment = 8
+// consecutive k of row l%32 starting at k = 8*(l/32); B fragment = the same
+// for column l%32; accumulator register r of lane l holds row
+// 8*(r/4) + 4*(l/32) + r%4, column l%32.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "ve_device.h"
+#include "ve_muon.h"
+
+namespace ve {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// A product configuration: workgroup tile BM x BN, contraction step BK,
+// each wave a WM x WN tile of (WM/32) x (WN/32) MFMA 32x32 blocks.
+template <int BM_, int BN_, int BK_, int WM_, int WN_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+    static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+    static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+    static constexpr int TM = WM / 32, TN = WN / 32;
+    static constexpr int LDK = BK + 8;             // padded LDS row (bf16): 16 rows hit distinct banks
+    static constexpr int VPR = BK / 8;             // 16-byte vectors per operand row of one step
+    static constexpr int PV = BM * VPR / THREADS;  // staged vectors per thread
+    static constexpr int QV = BN * VPR / THREADS;
+    static constexpr int LDC = BN + 4;             // fp32 output rows (padded)
+    static constexpr int OP_BYTES = 2 * (BM + BN) * LDK * 2;
+    static constexpr int C_BYTES = WM * LDC * 4;   // one wave-row pass of the output tile
+    static constexpr int SMEM = OP_BYTES > C_BYTES ? OP_BYTES : C_BYTES;
+    static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0 && BK % 16 == 0, "shape");
+    static_assert(PV * THREADS == BM * VPR && QV * THREADS == BN * VPR, "staging must divide evenly");
+    static_assert((WM * BN / 8) % THREADS == 0, "epilogue must divide evenly");
+};
+
+// The configurations compiled in; VE_GEMM_CFG (environment) selects one for tuning.
+#define VE_GEMM_CFGS(X) \
+    X(0, 128, 128, 64, 64, 64) \
+    X(1, 256, 128, 64, 128, 64) \
+    X(2, 256, 256, 64, 128, 64) \
+    X(3, 256, 256, 32, 128, 64) \
+    X(4, 256, 128, 64, 64, 64) \
+    X(5, 128, 128, 32, 64, 64)
+
+constexpr int kNormBlocks = 1024;    // partial sums of the Frobenius norm
+constexpr int kCUs = 256;           // MI355X compute units
+
+__device__ __forceinline__ uint16_t to_bf16(float x) { return (uint16_t)pack_bf16x2(x, 0.f); }
+__device__ __forceinline__ float from_bf16(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// 8 consecutive bf16 of row `r` starting at column `k` of a row-major matrix
+// with `rows` x `cols` valid elements and leading dimension `ld`; zeros
+// outside.  VEC: rows are 16-byte aligned and cols is a multiple of 8, so
+// every in-range group of 8 is one 16-byte access.
+template <bool VEC>
+__device__ __forceinline__ u32x4 load8(const uint16_t* base, int64_t ld, int64_t rows, int64_t cols, int64_t r,
+                                       int64_t k) {
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (r >= rows || k >= cols) return v;
+    const VE_GLOBAL uint16_t* p = (const VE_GLOBAL uint16_t*)(base + r * ld + k);
+    if constexpr (VEC) {
+        return *(const VE_GLOBAL u32x4*)p;
+    } else {
+        uint16_t e[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) e[t] = (k + t < cols) ? p[t] : (uint16_t)0;
+        v.x = e[0] | ((uint32_t)e[1] << 16);
+        v.y = e[2] | ((uint32_t)e[3] << 16);
+        v.z = e[4] | ((uint32_t)e[5] << 16);
+        v.w = e[6] | ((uint32_t)e[7] << 16);
+        return v;
+    }
+}
+
+// 8 bf16 <-> a 16-byte vector
+__device__ __forceinline__ u32x4 pack8(const float* v) {
+    return u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+}
+
+template <class CF, bool HAS_D, bool HAS_C, bool HAS_CT, bool VEC>
+__global__ void __launch_bounds__(CF::THREADS) k_gemm_nt(GemmArgs g) {
+    constexpr int BM = CF::BM, BN = CF::BN, BK = CF::BK, WM = CF::WM, WN = CF::WN, TM = CF::TM, TN = CF::TN;
+    constexpr int LDK = CF::LDK, LDC = CF::LDC, NT = CF::THREADS, VPR = CF::VPR;
+    const int tile = blockIdx.x;
+    const int ti = tile / g.tiles_n, tj = tile % g.tiles_n;
+    if (g.symmetric && ti > tj) return;
+    const int64_t i0 = (int64_t)ti * BM, j0 = (int64_t)tj * BN;
+    // operand tiles (2 buffers each), reused for the fp32 output afterwards
+    __shared__ __attribute__((aligned(16))) unsigned char smem[CF::SMEM];
+    uint16_t* sP = (uint16_t*)smem;                   // [2][BM * LDK]
+    uint16_t* sQ = sP + 2 * BM * LDK;                 // [2][BN * LDK]
+    float* sC = (float*)smem;                         // [WM][LDC], one wave row at a time
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave / CF::WAVES_N, wc = wave % CF::WAVES_N;
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+    // global -> register staging: vector v = tid + NT*q covers row v/VPR, k-vector v%VPR
+    u32x4 rp[CF::PV], rq[CF::QV];
+    auto gload = [&](int64_t k0) {
+#pragma unroll
+        for (int q = 0; q < CF::PV; ++q) {
+            const int v = tid + NT * q;
+            rp[q] = load8<VEC>(g.P, g.ldp, g.M, g.K, i0 + v / VPR, k0 + (v % VPR) * 8);
+        }
+#pragma unroll
+        for (int q = 0; q < CF::QV; ++q) {
+            const int v = tid + NT * q;
+            rq[q] = load8<VEC>(g.Q, g.ldq, g.N, g.K, j0 + v / VPR, k0 + (v % VPR) * 8);
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < CF::PV; ++q) {
+            const int v = tid + NT * q;
+            *(u32x4*)&sP[buf * BM * LDK + (v / VPR) * LDK + (v % VPR) * 8] = rp[q];
+        }
+#pragma unroll
+        for (int q = 0; q < CF::QV; ++q) {
+            const int v = tid + NT * q;
+            *(u32x4*)&sQ[buf * BN * LDK + (v / VPR) * LDK + (v % VPR) * 8] = rq[q];
+        }
+    };
+
+    const int64_t nk = (g.K + BK - 1) / BK;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    const int frow = lane & 31, fk = (lane >> 5) * 8;
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        const int cur = (int)(kt & 1);
+        if (kt + 1 < nk) gload((kt + 1) * BK);
+        const uint16_t* cp = sP + cur * BM * LDK + (wr * WM + frow) * LDK + fk;
+        const uint16_t* cq = sQ + cur * BN * LDK + (wc * WN + frow) * LDK + fk;
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            bf16x8 fa[TM], fb[TN];
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+                fa[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)&cp[t * 32 * LDK + kk * 16]);
+#pragma unroll
+            for (int t = 0; t < TN; ++t)
+                fb[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)&cq[t * 32 * LDK + kk * 16]);
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int b = 0; b < TN; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+        }
+        if (kt + 1 < nk) sstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue, one wave row (WM rows of the tile) at a time through LDS:
+    //   1. alpha * acc into the fp32 staging rows (the operand buffers are dead);
+    //   2. row-major: v = bf16(stage + beta * D), C written as 16-byte runs of a
+    //      row; the rounded value goes back to the stage for the transpose;
+    //   3. transposed: C^T (or the mirrored tile of a symmetric C) written as
+    //      16-byte runs of its rows, lanes on consecutive columns of the stage
+    //      so the LDS reads are conflict-free.
+    const bool mirror = g.symmetric && ti < tj;
+    const bool transpose = HAS_CT || mirror;
+    uint16_t* T = HAS_CT ? g.CT : g.C;
+    const int64_t ldt = HAS_CT ? g.ldct : g.ldc;
+    const bool vec_t = HAS_CT ? g.vec_ct : g.vec_c;
+    const int64_t ncols = min((int64_t)BN, g.N - j0);
+#pragma unroll 1
+    for (int pass = 0; pass < CF::WAVES_M; ++pass) {
+        const int64_t r0 = i0 + (int64_t)pass * WM;                  // first tile row of this pass
+        const int64_t mrows = min((int64_t)WM, g.M - r0);
+        if (wr == pass) {
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int b = 0; b < TN; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = a * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                        const int col = wc * WN + b * 32 + (lane & 31);
+                        sC[row * LDC + col] = g.alpha * acc[a][b][r];
+                    }
+        }
+        __syncthreads();
+        if (mrows > 0) {
+#pragma unroll 2
+            for (int q = 0; q < (WM * BN / 8) / NT; ++q) {
+                const int id = tid + NT * q;
+                const int row = id / (BN / 8), c8 = (id % (BN / 8)) * 8;
+                if (row >= mrows || c8 >= ncols) continue;
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = sC[row * LDC + c8 + e];
+                const int64_t i = r0 + row, j = j0 + c8;
+                const bool full = c8 + 8 <= ncols;
+                if (HAS_D) {
+                    if (full && g.vec_d) {
+                        const u32x4 d = *(const VE_GLOBAL u32x4*)(g.D + i * g.ldd + j);
+                        const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            v[e] = __builtin_fmaf(g.beta, (e & 1) ? bf_hi(dw[e >> 1]) : bf_lo(dw[e >> 1]), v[e]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (c8 + e < ncols) v[e] = __builtin_fmaf(g.beta, from_bf16(g.D[i * g.ldd + j + e]), v[e]);
+                    }
+                }
+                const u32x4 h = pack8(v);
+                const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+                if (HAS_C) {
+                    if (full && g.vec_c) {
+                        *(VE_GLOBAL u32x4*)(g.C + i * g.ldc + j) = h;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (c8 + e < ncols) g.C[i * g.ldc + j + e] = (uint16_t)(hw[e >> 1] >> (16 * (e & 1)));
+                    }
+                }
+                if (transpose) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        sC[row * LDC + c8 + e] = (e & 1) ? bf_hi(hw[e >> 1]) : bf_lo(hw[e >> 1]);
+                }
+            }
+            if (transpose) {
+                __syncthreads();
+#pragma unroll 2
+                for (int q = 0; q < (WM * BN / 8) / NT; ++q) {
+                    const int id = tid + NT * q;
+                    const int col = id % BN, r8 = (id / BN) * 8;
+                    if (col >= ncols || r8 >= mrows) continue;
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = sC[(r8 + e) * LDC + col];
+                    const u32x4 h = pack8(v);               // exact: the values are bf16 already
+                    const int64_t j = j0 + col, i = r0 + r8;
+                    if (r8 + 8 <= mrows && vec_t) {
+                        *(VE_GLOBAL u32x4*)(T + j * ldt + i) = h;
+                    } else {
+                        const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (r8 + e < mrows) T[j * ldt + i + e] = (uint16_t)(hw[e >> 1] >> (16 * (e & 1)));
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Partial sums of squares of n bf16 values, in fp64, one per workgroup.
+__global__ void __launch_bounds__(256) k_sumsq(const uint16_t* x, int64_t n, double* partial) {
+    double s = 0.0;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const double v = (double)from_bf16(x[i]);
+        s = __builtin_fma(v, v, s);
+    }
+    __shared__ double red[256];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
+}
+
+// s = fp32(1 / (sqrt(sum of the partials) + eps)), one workgroup.
+__global__ void __launch_bounds__(256) k_norm_scale(const double* partial, int nparts, float eps, float* scale) {
+    __shared__ double red[256];
+    double s = 0.0;
+    for (int i = threadIdx.x; i < nparts; i += 256) s += partial[i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *scale = (float)(1.0 / (__builtin_sqrt(red[0]) + (double)eps));
+}
+
+// X0 = bf16(fp32(G * s)), written straight (rows x cols, to `straight`) and/or
+// transposed (cols x rows, to `transposed`).  64 x 64 tiles through LDS so
+// both writes are coalesced.
+__global__ void __launch_bounds__(256) k_normalize(const uint16_t* G, int64_t rows, int64_t cols, const float* scale_p,
+                                                   uint16_t* straight, uint16_t* transposed, int tiles_c) {
+    __shared__ uint16_t tileT[64][66];
+    const float scale = *scale_p;
+    const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * 64, c0 = (int64_t)(blockIdx.x % tiles_c) * 64;
+    const int tc = threadIdx.x & 63, tr = threadIdx.x >> 6;
+    for (int rr = tr; rr < 64; rr += 4) {
+        const int64_t r = r0 + rr, c = c0 + tc;
+        uint16_t h = 0;
+        if (r < rows && c < cols) {
+            h = to_bf16(from_bf16(G[r * cols + c]) * scale);
+            if (straight) straight[r * cols + c] = h;
+        }
+        tileT[tc][rr] = h;
+    }
+    if (!transposed) return;
+    __syncthreads();
+    for (int cc = tr; cc < 64; cc += 4) {
+        const int64_t c = c0 + cc, r = r0 + tc;
+        if (c < cols && r < rows) transposed[c * rows + r] = tileT[cc][tc];
+    }
+}
+
+template <class CF, bool HAS_D, bool HAS_C, bool HAS_CT>
+hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s) {
+    const int64_t tiles = (int64_t)((g.M + CF::BM - 1) / CF::BM) * g.tiles_n;
+    if (g.vec_p && g.vec_q && g.K % 8 == 0)
+        hipLaunchKernelGGL((k_gemm_nt<CF, HAS_D, HAS_C, HAS_CT, true>), dim3((unsigned)tiles), dim3(CF::THREADS), 0, s, g);
+    else
+        hipLaunchKernelGGL((k_gemm_nt<CF, HAS_D, HAS_C, HAS_CT, false>), dim3((unsigned)tiles), dim3(CF::THREADS), 0, s,
+                           g);
+    return hipGetLastError();
+}
+
+template <class CF>
+hipError_t launch_gemm_cfg(GemmArgs g, hipStream_t s) {
+    g.tiles_n = (int)((g.N + CF::BN - 1) / CF::BN);
+    const bool d = g.D != nullptr, c = g.C != nullptr, ct = g.CT != nullptr;
+    if (d && c && ct) return launch_gemm_t<CF, true, true, true>(g, s);
+    if (d && c) return launch_gemm_t<CF, true, true, false>(g, s);
+    if (d && ct) return launch_gemm_t<CF, true, false, true>(g, s);
+    if (c && ct) return launch_gemm_t<CF, false, true, true>(g, s);
+    if (c) return launch_gemm_t<CF, false, true, false>(g, s);
+    if (ct) return launch_gemm_t<CF, false, false, true>(g, s);
+    return hipErrorInvalidValue;
+}
+
+// VE_GEMM_CFG (environment) pins one configuration for tuning; otherwise
+// large tiles are used when they still give every CU several tiles.
+int gemm_cfg_override() {
+    static const int idx = [] {
+        const char* e = getenv("VE_GEMM_CFG");
+        return e ? atoi(e) : -1;
+    }();
+    return idx;
+}
+
+int gemm_cfg_auto(const GemmArgs& g) {
+    const int64_t tm = (g.M + 255) / 256, tn = (g.N + 255) / 256;
+    const int64_t active = g.symmetric ? tm * (tm + 1) / 2 : tm * tn;
+    return active >= 4 * kCUs ? 2 : 0;
+}
+
+}  // namespace
+
+int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127) / 128); }
+int norm_blocks() { return kNormBlocks; }
+
+hipError_t launch_gemm_nt(GemmArgs g, hipStream_t s) {
+    const int cfg = gemm_cfg_override();
+    switch (cfg >= 0 ? cfg : gemm_cfg_auto(g)) {
+#define VE_GEMM_CASE(ID, BM, BN, BK, WM, WN) \
+        case ID: return launch_gemm_cfg<Cfg<BM, BN, BK, WM, WN>>(g, s);
+        VE_GEMM_CFGS(VE_GEMM_CASE)
+#undef VE_GEMM_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_sumsq(const uint16_t* x, int64_t n, double* partial, hipStream_t s) {
+    hipLaunchKernelGGL(k_sumsq, dim3(kNormBlocks), dim3(256), 0, s, x, n, partial);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_scale(const double* partial, float eps, float* scale, hipStream_t s) {
+    hipLaunchKernelGGL(k_norm_scale, dim3(1), dim3(256), 0, s, partial, kNormBlocks, eps, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_normalize(const uint16_t* G, int64_t rows, int64_t cols, const float* scale, uint16_t* straight,
+                            uint16_t* transposed, hipStream_t s) {
+    const int tiles_c = (int)((cols + 63) / 64);
+    const int64_t tiles = ((rows + 63) / 64) * tiles_c;
+    hipLaunchKernelGGL(k_normalize, dim3((unsigned)tiles), dim3(256), 0, s, G, rows, cols, scale, straight,
+                       transposed, tiles_c);
+    return hipGetLastError();
+}
+
+}  // namespace ve

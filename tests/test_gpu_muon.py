@@ -1,0 +1,270 @@
+"""GPU parity of Muon's Newton-Schulz path: the MFMA product kernel
+(``ve_gemm_bf16_nt``) and the whole iteration (``ve_muon_newton_schulz``)
+against the oracle (oracle/muon.py) on seeded inputs.
+
+Gates (tests/muon_common.py): a product, and one Newton-Schulz step, must lie
+within a rigorous elementwise bound of the oracle (fp32 accumulation error
+plus one bf16 ulp, propagated through the stages).  Over five steps that
+bound is too loose to use (it compounds the absolute values), so the five-
+step result is compared in relative Frobenius norm with a first-order
+allowance: the GPU and the oracle round at the same points and differ where
+the accumulation order flips a rounding, about one bf16 ulp on a small share
+of the entries per stage; the iteration amplifies such a perturbation at most
+by max |p'(s)| over the singular values (about 3.8 on [0, 1.2]) per step.
+Five steps of three stages with a 2^-8 relative perturbation each, amplified
+that way, stay below 2^-8 * 3 * (1 + 3.8 + ...) applied to the share of
+flipped entries; the gate is 3 % of |X|_F.  Full-size products are checked
+on sampled output elements, each computed exactly on the host.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import muon
+from muon_common import U, product_bound, ns_one_step_bound, ulp_bf16
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _ve():
+    import ragged_shard_optimizer_amd as ve
+    return ve
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _bf16_host(shape, seed, scale=1.0):
+    x = np.random.default_rng(seed).standard_normal(shape) * scale
+    return muon.f64_to_bf16_bits(x)
+
+
+def _dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV)
+
+
+def _host(t):
+    return muon.bf16_bits_to_f64(t.cpu().numpy().view(np.uint16))
+
+
+def _empty(shape, fill=-1):
+    import torch
+    return torch.full(shape, fill, dtype=torch.int16, device=DEV)
+
+
+# ---------------------------------------------------------------------------
+# the product kernel
+PRODUCT_CASES = [
+    # M, N, K, alpha, beta, with D
+    (128, 128, 64, 1.0, 0.0, False),
+    (256, 384, 512, 1.0, 0.0, False),
+    (200, 300, 136, 0.7, -1.3, True),       # ragged tiles, K tail within a step
+    (37, 53, 29, 1.5, 0.25, True),          # K % 8 != 0: the 2-byte operand path
+    (1, 1, 1, 1.0, 0.0, False),
+    (130, 7, 1000, -2.0, 3.4445, True),
+    (64, 2880, 2880, 1.0, 3.4445, True),    # GPT-OSS expert width
+]
+
+
+@pytest.mark.parametrize("M,N,K,alpha,beta,has_d", PRODUCT_CASES)
+def test_product_parity(M, N, K, alpha, beta, has_d):
+    import torch
+    ve = _ve()
+    Pb, Qb = _bf16_host((M, K), 1 + M), _bf16_host((N, K), 2 + N)
+    Db = _bf16_host((M, N), 3) if has_d else None
+    P, Q = muon.bf16_bits_to_f64(Pb), muon.bf16_bits_to_f64(Qb)
+    D = muon.bf16_bits_to_f64(Db) if has_d else None
+    C, CT = _empty((M, N)), _empty((N, M))
+    _say(f"[gpu] product M={M} N={N} K={K}")
+    ve.gemm_bf16_nt(_dev(Pb), _dev(Qb), C=C, CT=CT, D=_dev(Db) if has_d else None, alpha=alpha, beta=beta)
+    torch.cuda.synchronize()
+    want = muon.gemm_nt(P, Q, D, alpha, beta)
+    got = _host(C)
+    bound = product_bound(P, Q, D, alpha, beta, C=want)
+    bad = np.abs(got - want) > bound
+    assert not bad.any(), (int(bad.sum()), np.argwhere(bad)[:3])
+    # the transposed output is the same values, bit for bit
+    assert np.array_equal(C.cpu().numpy().T, CT.cpu().numpy())
+
+
+@pytest.mark.parametrize("n,K", [(128, 256), (384, 200), (300, 64), (45, 77)])
+def test_product_symmetric_tiles(n, K):
+    """X X^T with only the upper tiles computed: exactly symmetric, and
+    within the bound of the oracle everywhere."""
+    import torch
+    ve = _ve()
+    Xb = _bf16_host((n, K), 7)
+    X = muon.bf16_bits_to_f64(Xb)
+    Xd = _dev(Xb)
+    C = _empty((n, n))
+    ve.gemm_bf16_nt(Xd, Xd, C=C, symmetric=True)
+    torch.cuda.synchronize()
+    got = _host(C)
+    assert np.array_equal(got, got.T)
+    want = muon.gemm_nt(X, X)
+    assert (np.abs(got - want) <= product_bound(X, X, C=want)).all()
+    # with an addend, as in B = c A A + b A
+    Ab = muon.f64_to_bf16_bits(want)
+    A = muon.bf16_bits_to_f64(Ab)
+    Ad = _dev(Ab)
+    B = _empty((n, n))
+    ve.gemm_bf16_nt(Ad, Ad, C=B, D=Ad, alpha=2.0315, beta=-4.7750, symmetric=True)
+    torch.cuda.synchronize()
+    gotB = _host(B)
+    assert np.array_equal(gotB, gotB.T)
+    wantB = muon.gemm_nt(A, A, A, 2.0315, -4.7750)
+    assert (np.abs(gotB - wantB) <= product_bound(A, A, A, 2.0315, -4.7750, C=wantB)).all()
+
+
+def test_product_rejects_bad_arguments():
+    import ctypes as C
+    ve = _ve()
+    L = ve.lib()
+    p = C.c_void_p(256)   # never dereferenced: each call is refused first
+    assert L.ve_gemm_bf16_nt(None, 8, p, 8, None, 0, p, 8, None, 0, 8, 8, 8, 1.0, 0.0, 0, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_gemm_bf16_nt(p, 8, p, 8, None, 0, None, 0, None, 0, 8, 8, 8, 1.0, 0.0, 0, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_gemm_bf16_nt(p, 4, p, 8, None, 0, p, 8, None, 0, 8, 8, 8, 1.0, 0.0, 0, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_gemm_bf16_nt(p, 8, p, 8, None, 0, p, 8, None, 0, 8, 4, 8, 1.0, 0.0, 1, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_gemm_bf16_nt(p, 8, p, 8, None, 0, p, 8, None, 0, 0, 8, 8, 1.0, 0.0, 0, None) == ve.VE_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# the iteration
+def _run_ns(Gb, steps):
+    import torch
+    ve = _ve()
+    G = _dev(Gb)
+    out = _empty(Gb.shape)
+    ve.muon_newton_schulz(G, out, steps=steps)
+    torch.cuda.synchronize()
+    return _host(out)
+
+
+@pytest.mark.parametrize("shape", [(64, 160), (160, 64), (96, 96), (37, 100), (1, 50), (50, 1)])
+def test_normalisation(shape):
+    Gb = _bf16_host(shape, 11, scale=3.0)
+    G = muon.bf16_bits_to_f64(Gb)
+    _say(f"[gpu] newton-schulz steps=0 {shape}")
+    got = _run_ns(Gb, 0)
+    want = muon.newton_schulz(G, steps=0)
+    assert np.all(np.abs(got - want) <= U * np.abs(want) + ulp_bf16(want))
+
+
+@pytest.mark.parametrize("shape", [(64, 160), (160, 64), (128, 128), (37, 100), (100, 37), (200, 520)])
+def test_one_step_within_propagated_bound(shape):
+    Gb = _bf16_host(shape, 12)
+    G = muon.bf16_bits_to_f64(Gb)
+    _say(f"[gpu] newton-schulz steps=1 {shape}")
+    got = _run_ns(Gb, 1)
+    trace = []
+    want = muon.newton_schulz(G, steps=1, trace=trace)
+    X0 = muon.newton_schulz(G, steps=0)
+    if shape[0] > shape[1]:
+        X0 = X0.T
+    (A, B, X1), = trace[0]
+    dX0 = U * np.abs(X0) + ulp_bf16(X0)
+    bound = ns_one_step_bound(X0, A, B, X1, dX0)
+    if shape[0] > shape[1]:
+        bound = bound.T
+    bad = np.abs(got - want) > bound
+    assert not bad.any(), (int(bad.sum()), float(np.abs(got - want).max()))
+
+
+@pytest.mark.parametrize("shape", [(256, 512), (512, 256), (300, 300), (128, 1000)])
+def test_five_steps(shape):
+    Gb = _bf16_host(shape, 13)
+    G = muon.bf16_bits_to_f64(Gb)
+    _say(f"[gpu] newton-schulz steps=5 {shape}")
+    got = _run_ns(Gb, 5)
+    want = muon.newton_schulz(G, steps=5)
+    rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+    assert rel <= 0.03, rel
+    # the structure of the result: the singular values follow the quintic map
+    exact = muon.newton_schulz(G, steps=5, rounding=False)
+    s_got = np.linalg.svd(got, compute_uv=False)
+    s_ex = np.linalg.svd(exact, compute_uv=False)
+    assert np.abs(s_got - s_ex).max() <= 0.05
+
+
+def test_repeat_calls_are_deterministic():
+    import torch
+    ve = _ve()
+    Gb = _bf16_host((192, 640), 14)
+    G = _dev(Gb)
+    outs = []
+    ws = torch.empty(ve.muon_workspace_bytes(192, 640), dtype=torch.uint8, device=DEV)
+    for _ in range(3):
+        out = _empty((192, 640))
+        ve.muon_newton_schulz(G, out, steps=5, workspace=ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+def test_newton_schulz_rejects_bad_arguments():
+    import ctypes as C
+    import torch
+    ve = _ve()
+    L = ve.lib()
+    G = _empty((8, 8), 0)
+    out = _empty((8, 8), 0)
+    need = ve.muon_workspace_bytes(8, 8)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device=DEV)
+    g, o, w = C.c_void_p(G.data_ptr()), C.c_void_p(out.data_ptr()), C.c_void_p(ws.data_ptr())
+    assert L.ve_muon_newton_schulz(None, o, 8, 8, 5, 1e-7, w, need, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_muon_newton_schulz(g, o, 0, 8, 5, 1e-7, w, need, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_muon_newton_schulz(g, o, 8, 8, -1, 1e-7, w, need, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_muon_newton_schulz(g, o, 8, 8, 5, -1.0, w, need, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_muon_newton_schulz(g, o, 8, 8, 5, 1e-7, w, need - 1, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_muon_newton_schulz(g, o, 8, 8, 5, 1e-7, C.c_void_p(ws.data_ptr() + 16), need, None) \
+        == ve.VE_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# full size: the three products of one step at a real matrix's shapes,
+# sampled output elements computed exactly on the host
+FULL = [("llama_mlp", 8192, 28672), ("deepseek_expert", 2048, 7168), ("gptoss_expert", 2880, 5760)]
+
+
+@pytest.mark.parametrize("name,m,n", FULL)
+def test_full_size_products_sampled(name, m, n):
+    import torch
+    ve = _ve()
+    g = torch.Generator(device=DEV)
+    g.manual_seed(m * 7 + n)
+    # X with rows of norm ~ 1/sqrt(m) (as after normalisation), A and B of the
+    # magnitudes a step produces
+    X = (torch.randn(m, n, generator=g, device=DEV) / np.sqrt(m * n) * 4).to(torch.bfloat16).view(torch.int16)
+    XT = X.view(torch.bfloat16).t().contiguous().view(torch.int16)
+    A = _empty((m, m))
+    _say(f"[gpu] full-size products {name}: {m} x {n}")
+    ve.gemm_bf16_nt(X, X, C=A, symmetric=True)
+    B = _empty((m, m))
+    ve.gemm_bf16_nt(A, A, C=B, D=A, alpha=2.0315, beta=-4.7750, symmetric=True)
+    Y, YT = _empty((m, n)), _empty((n, m))
+    ve.gemm_bf16_nt(B, XT, C=Y, CT=YT, D=X, alpha=1.0, beta=3.4445)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    Xh, Ah, Bh = _host(X), _host(A), _host(B)
+    Yh = _host(Y)
+    assert torch.equal(Y.view(torch.bfloat16).t().contiguous().view(torch.int16), YT)
+    for (P, Q, D, alpha, beta, C) in ((Xh, Xh, None, 1.0, 0.0, Ah), (Ah, Ah, Ah, 2.0315, -4.7750, Bh),
+                                      (Bh, Xh.T, Xh, 1.0, 3.4445, Yh)):
+        rows = rng.integers(0, C.shape[0], 64)
+        cols = rng.integers(0, C.shape[1], 64)
+        Pr, Qc = P[rows], Q[cols]
+        Dr = None if D is None else D[rows, cols][:, None]
+        for t in range(len(rows)):
+            want = muon.gemm_nt(Pr[t:t + 1], Qc[t:t + 1], None if Dr is None else Dr[t:t + 1], alpha, beta)
+            bd = product_bound(Pr[t:t + 1], Qc[t:t + 1], None if Dr is None else Dr[t:t + 1], alpha, beta, C=want)
+            assert abs(C[rows[t], cols[t]] - want[0, 0]) <= bd[0, 0], (name, rows[t], cols[t])
+    del X, XT, A, B, Y, YT
+    torch.cuda.empty_cache()
