@@ -25,6 +25,7 @@ struct GemmArgs {
     int32_t symmetric;
     int32_t tiles_n;                 // set by the launcher
     bool vec_p, vec_q, vec_d, vec_c, vec_ct;  // rows allow 16-byte accesses
+    bool xcd_remap;                  // set by the launcher: XCD-aware tile order
 };
 hipError_t launch_gemm_nt(GemmArgs g, hipStream_t s);
 int64_t gemm_tiles(int64_t M, int64_t N);

@@ -106,6 +106,37 @@ __device__ __forceinline__ u32x4 load8(const uint16_t* base, int64_t ld, int64_t
     }
 }
 
+// Output tile of this workgroup.  Workgroups are dispatched round-robin over
+// the 8 XCDs, each with its own L2; with g.xcd_remap each XCD is given a
+// contiguous slice of the tile sequence.  A full product walks groups of 8
+// tile rows column by column, so the operand panels a slice touches are few
+// and stay in its L2.  A symmetric product launches only the tiles on or
+// above the diagonal, row by row, so every slice carries the same work.
+__device__ __forceinline__ void tile_of(const GemmArgs& g, int& ti, int& tj) {
+    const int nb = gridDim.x;
+    int bid = blockIdx.x;
+    if (g.xcd_remap && nb % 8 == 0) bid = (bid % 8) * (nb / 8) + bid / 8;
+    if (g.symmetric) {
+        // row t of the upper triangle holds tiles_n - t tiles
+        int t = 0, rem = bid;
+        while (rem >= g.tiles_n - t) {
+            rem -= g.tiles_n - t;
+            ++t;
+        }
+        ti = t;
+        tj = t + rem;
+        return;
+    }
+    constexpr int kGroup = 8;
+    const int tiles_m = nb / g.tiles_n;
+    const int per_group = kGroup * g.tiles_n;
+    const int first = (bid / per_group) * kGroup;
+    const int gm = min(tiles_m - first, kGroup);
+    const int r = bid % per_group;
+    ti = first + r % gm;
+    tj = r / gm;
+}
+
 // 8 bf16 <-> a 16-byte vector
 __device__ __forceinline__ u32x4 pack8(const float* v) {
     return u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
@@ -115,9 +146,8 @@ template <class CF, bool HAS_D, bool HAS_C, bool HAS_CT, bool VEC>
 __global__ void __launch_bounds__(CF::THREADS) k_gemm_nt(GemmArgs g) {
     constexpr int BM = CF::BM, BN = CF::BN, BK = CF::BK, WM = CF::WM, WN = CF::WN, TM = CF::TM, TN = CF::TN;
     constexpr int LDK = CF::LDK, LDC = CF::LDC, NT = CF::THREADS, VPR = CF::VPR;
-    const int tile = blockIdx.x;
-    const int ti = tile / g.tiles_n, tj = tile % g.tiles_n;
-    if (g.symmetric && ti > tj) return;
+    int ti, tj;
+    tile_of(g, ti, tj);
     const int64_t i0 = (int64_t)ti * BM, j0 = (int64_t)tj * BN;
     // operand tiles (2 buffers each), reused for the fp32 output afterwards
     __shared__ __attribute__((aligned(16))) unsigned char smem[CF::SMEM];
@@ -192,8 +222,9 @@ __global__ void __launch_bounds__(CF::THREADS) k_gemm_nt(GemmArgs g) {
     }
 
     // epilogue, one wave row (WM rows of the tile) at a time through LDS:
-    //   1. alpha * acc into the fp32 staging rows (the operand buffers are dead);
-    //   2. row-major: v = bf16(stage + beta * D), C written as 16-byte runs of a
+    //   1. the accumulators into the fp32 staging rows (the operand buffers are
+    //      dead; stored straight from the accumulator registers);
+    //   2. row-major: v = bf16(alpha * stage + beta * D), C written as 16-byte runs of a
     //      row; the rounded value goes back to the stage for the transpose;
     //   3. transposed: C^T (or the mirrored tile of a symmetric C) written as
     //      16-byte runs of its rows, lanes on consecutive columns of the stage
@@ -217,7 +248,7 @@ __global__ void __launch_bounds__(CF::THREADS) k_gemm_nt(GemmArgs g) {
                     for (int r = 0; r < 16; ++r) {
                         const int row = a * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                         const int col = wc * WN + b * 32 + (lane & 31);
-                        sC[row * LDC + col] = g.alpha * acc[a][b][r];
+                        sC[row * LDC + col] = acc[a][b][r];
                     }
         }
         __syncthreads();
@@ -229,7 +260,7 @@ __global__ void __launch_bounds__(CF::THREADS) k_gemm_nt(GemmArgs g) {
                 if (row >= mrows || c8 >= ncols) continue;
                 float v[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = sC[row * LDC + c8 + e];
+                for (int e = 0; e < 8; ++e) v[e] = g.alpha * sC[row * LDC + c8 + e];
                 const int64_t i = r0 + row, j = j0 + c8;
                 const bool full = c8 + 8 <= ncols;
                 if (HAS_D) {
@@ -273,6 +304,255 @@ __global__ void __launch_bounds__(CF::THREADS) k_gemm_nt(GemmArgs g) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = sC[(r8 + e) * LDC + col];
                     const u32x4 h = pack8(v);               // exact: the values are bf16 already
+                    const int64_t j = j0 + col, i = r0 + r8;
+                    if (r8 + 8 <= mrows && vec_t) {
+                        *(VE_GLOBAL u32x4*)(T + j * ldt + i) = h;
+                    } else {
+                        const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (r8 + e < mrows) T[j * ldt + i + e] = (uint16_t)(hw[e >> 1] >> (16 * (e & 1)));
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Large-tile product with direct global -> LDS loads (gfx950
+// global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS base
+// + 16 * lane).  256 x 256 output tile; waves of WM x WN (WM/32 x WN/32 MFMA
+// 32x32 blocks); contraction steps of BK in a ring of STAGES LDS stages, so
+// the loads for step k + STAGES - 1 are in flight while step k computes and
+// each step waits only for the oldest outstanding stage.  Operand rows are
+// BK * 2 bytes with no padding; the 16-byte chunks of row r are stored
+// XOR-swizzled (chunk c at slot c ^ s(r)) so that the fragment reads of
+// consecutive rows spread over the banks.  Each DMA instruction of a wave
+// fills 1 KiB of whole rows.  Requires K % BK == 0 and 16-byte operand rows;
+// rows past M or N read a clamped valid row (their outputs are never stored).
+// instruction classes for __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+
+// s_waitcnt operand: wait until at most n vector-memory operations are
+// outstanding (expcnt and lgkmcnt left unconstrained).
+constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
+
+template <int WM_, int WN_, int BK_, int STAGES_>
+struct DmaCfg {
+    static constexpr int BM = 256, BN = 256, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_;
+    static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, WAVES = WAVES_M * WAVES_N;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int TM = WM / 32, TN = WN / 32;
+    static constexpr int CHUNKS = BK / 8;                      // 16-byte chunks per operand row
+    static constexpr int ROWS_PER_DMA = 1024 / (BK * 2);       // rows one wave instruction fills
+    static constexpr int DMA_PER_OP = BM / ROWS_PER_DMA / WAVES;  // instructions per operand per thread
+    static constexpr int STAGE_ELEMS = (BM + BN) * BK;
+    static constexpr int OP_BYTES = STAGES * STAGE_ELEMS * 2;
+    static constexpr int PASS_ROWS = 64;
+    static constexpr int LDC = BN + 4;
+    static constexpr int SMEM = OP_BYTES > PASS_ROWS * LDC * 4 ? OP_BYTES : PASS_ROWS * LDC * 4;
+    static_assert(DMA_PER_OP * ROWS_PER_DMA * WAVES == BM, "DMA rows must divide evenly");
+    static_assert(SMEM <= 160 * 1024, "LDS");
+    // swizzle: rows sharing a bank line get distinct slots
+    __device__ static __forceinline__ int swz(int r) {
+        if constexpr (CHUNKS == 8) return (r & 7) ^ ((r >> 3) & 1);
+        else return (r >> 1) & 3;
+    }
+};
+
+#define VE_DMA_CFGS(X) \
+    X(6, 128, 128, 64, 2) \
+    X(7, 128, 128, 32, 3) \
+    X(8, 128, 128, 32, 4) \
+    X(9, 128, 64, 64, 2) \
+    X(10, 128, 64, 32, 3) \
+    X(11, 128, 64, 32, 4)
+
+template <class CF, bool HAS_D, bool HAS_C, bool HAS_CT>
+__global__ void __launch_bounds__(CF::THREADS) k_gemm_nt_dma(GemmArgs g) {
+    constexpr int BM = CF::BM, BN = CF::BN, BK = CF::BK, WM = CF::WM, WN = CF::WN, TM = CF::TM, TN = CF::TN;
+    constexpr int NT = CF::THREADS, LDC = CF::LDC, S = CF::STAGES, SE = CF::STAGE_ELEMS;
+    int ti, tj;
+    tile_of(g, ti, tj);
+    const int64_t i0 = (int64_t)ti * BM, j0 = (int64_t)tj * BN;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[CF::SMEM];
+    uint16_t* ops = (uint16_t*)smem;                  // stage s: P rows [BM * BK], then Q rows [BN * BK]
+    float* sC = (float*)smem;                         // [PASS_ROWS][LDC]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave / CF::WAVES_N, wc = wave % CF::WAVES_N;
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+    // DMA: instruction q of wave w fills rows [(WAVES q + w) R, +R) of an
+    // operand (R = rows per KiB); lane l writes slot l % CHUNKS of row
+    // l / CHUNKS, i.e. logical chunk (l % CHUNKS) ^ s(row)
+    const int lrow = lane / CF::CHUNKS, lslot = lane % CF::CHUNKS;
+    auto dma_op = [&](const uint16_t* base, int64_t ld, int64_t rows, int64_t r0, uint16_t* dst, int64_t k0) {
+#pragma unroll
+        for (int q = 0; q < CF::DMA_PER_OP; ++q) {
+            const int blk = CF::WAVES * q + wave;
+            const int row = blk * CF::ROWS_PER_DMA + lrow;
+            const int64_t gr = min(r0 + row, rows - 1);
+            const uint16_t* src = base + gr * ld + k0 + 8 * (lslot ^ CF::swz(row));
+            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                             (void __attribute__((address_space(3)))*)(dst + blk * CF::ROWS_PER_DMA * BK),
+                                             16, 0, 0);
+        }
+    };
+    auto dma_step = [&](int64_t kt) {
+        uint16_t* st = ops + (int)(kt % S) * SE;
+        dma_op(g.P, g.ldp, g.M, i0, st, kt * BK);
+        dma_op(g.Q, g.ldq, g.N, j0, st + BM * BK, kt * BK);
+    };
+
+    const int64_t nk = g.K / BK;
+    // prologue: stages 0 .. S-2 in flight
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p)
+        if (p < nk) dma_step(p);
+    const int frow = lane & 31, fhalf = lane >> 5;
+    const int fs = CF::swz(lane & 15);                // rows t*32 + frow share frow's swizzle
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        // step kt's stage is complete when at most the S-2 younger stages are outstanding
+        if (kt + S - 2 < nk) {
+            constexpr int younger = (S - 2) * 2 * CF::DMA_PER_OP;
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(younger));
+        } else {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        }
+        // every wave has its own loads of this stage complete; a bare barrier
+        // (no memory fence, which would wait for the younger stages too) and
+        // compiler-level clobbers so no LDS access moves across it
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kt + S - 1 < nk) dma_step(kt + S - 1);     // into the stage consumed at step kt - 1
+        const uint16_t* st = ops + (int)(kt % S) * SE;
+        const uint16_t* cp = st + (wr * WM + frow) * BK;
+        const uint16_t* cq = st + BM * BK + (wc * WN + frow) * BK;
+        // fragments double-buffered over the 16-deep sub-steps: the reads for
+        // sub-step kk+1 are issued before the MFMAs of kk, so the LDS latency
+        // hides behind TM*TN MFMAs
+        bf16x8 fa[2][TM], fb[2][TN];
+        auto frag = [&](int buf, int kk) {
+            const int slot = ((2 * kk + fhalf) ^ fs) * 8;
+#pragma unroll
+            for (int t = 0; t < TM; ++t) fa[buf][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)&cp[t * 32 * BK + slot]);
+#pragma unroll
+            for (int t = 0; t < TN; ++t) fb[buf][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)&cq[t * 32 * BK + slot]);
+        };
+        frag(0, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, TM + TN, 0);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            if (kk + 1 < BK / 16) frag((kk + 1) & 1, kk + 1);
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int b = 0; b < TN; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][a], fb[kk & 1][b], acc[a][b], 0, 0, 0);
+            // schedule: one MFMA, then one read of the next sub-step, ...
+            if (kk + 1 < BK / 16) {
+#pragma unroll
+                for (int i = 0; i < TM + TN; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, TM * TN - (TM + TN), 0);
+            } else {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, TM * TN, 0);
+            }
+        }
+    }
+    __syncthreads();
+
+    // epilogue in passes of 64 tile rows, the same three phases as the
+    // register-staged kernel
+    const bool mirror = g.symmetric && ti < tj;
+    const bool transpose = HAS_CT || mirror;
+    uint16_t* T = HAS_CT ? g.CT : g.C;
+    const int64_t ldt = HAS_CT ? g.ldct : g.ldc;
+    const bool vec_t = HAS_CT ? g.vec_ct : g.vec_c;
+    const int64_t ncols = min((int64_t)BN, g.N - j0);
+    constexpr int PR = CF::PASS_ROWS;
+#pragma unroll
+    for (int pass = 0; pass < BM / PR; ++pass) {   // unrolled: accumulator indices stay compile-time
+        const int64_t r0 = i0 + (int64_t)pass * PR;
+        const int64_t mrows = min((int64_t)PR, g.M - r0);
+        if (wr == pass / (WM / PR)) {
+            constexpr int per = PR / 32;
+            const int a0 = (pass % (WM / PR)) * per;
+#pragma unroll
+            for (int aa = 0; aa < per; ++aa)
+#pragma unroll
+                for (int b = 0; b < TN; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = aa * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                        const int col = wc * WN + b * 32 + (lane & 31);
+                        sC[row * LDC + col] = acc[a0 + aa][b][r];
+                    }
+        }
+        __syncthreads();
+        if (mrows > 0) {
+#pragma unroll 2
+            for (int q = 0; q < (PR * BN / 8) / NT; ++q) {
+                const int id = tid + NT * q;
+                const int row = id / (BN / 8), c8 = (id % (BN / 8)) * 8;
+                if (row >= mrows || c8 >= ncols) continue;
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = g.alpha * sC[row * LDC + c8 + e];
+                const int64_t i = r0 + row, j = j0 + c8;
+                const bool full = c8 + 8 <= ncols;
+                if (HAS_D) {
+                    if (full && g.vec_d) {
+                        const u32x4 d = *(const VE_GLOBAL u32x4*)(g.D + i * g.ldd + j);
+                        const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            v[e] = __builtin_fmaf(g.beta, (e & 1) ? bf_hi(dw[e >> 1]) : bf_lo(dw[e >> 1]), v[e]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (c8 + e < ncols) v[e] = __builtin_fmaf(g.beta, from_bf16(g.D[i * g.ldd + j + e]), v[e]);
+                    }
+                }
+                const u32x4 h = pack8(v);
+                const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+                if (HAS_C) {
+                    if (full && g.vec_c) {
+                        *(VE_GLOBAL u32x4*)(g.C + i * g.ldc + j) = h;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (c8 + e < ncols) g.C[i * g.ldc + j + e] = (uint16_t)(hw[e >> 1] >> (16 * (e & 1)));
+                    }
+                }
+                if (transpose) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        sC[row * LDC + c8 + e] = (e & 1) ? bf_hi(hw[e >> 1]) : bf_lo(hw[e >> 1]);
+                }
+            }
+            if (transpose) {
+                __syncthreads();
+#pragma unroll 2
+                for (int q = 0; q < (PR * BN / 8) / NT; ++q) {
+                    const int id = tid + NT * q;
+                    const int col = id % BN, r8 = (id / BN) * 8;
+                    if (col >= ncols || r8 >= mrows) continue;
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = sC[(r8 + e) * LDC + col];
+                    const u32x4 h = pack8(v);
                     const int64_t j = j0 + col, i = r0 + r8;
                     if (r8 + 8 <= mrows && vec_t) {
                         *(VE_GLOBAL u32x4*)(T + j * ldt + i) = h;
@@ -346,9 +626,15 @@ __global__ void __launch_bounds__(256) k_normalize(const uint16_t* G, int64_t ro
     }
 }
 
+// workgroups of a launch: every tile, or the upper triangle of a symmetric product
+int64_t launch_tiles(const GemmArgs& g, int bm) {
+    const int64_t tm = (g.M + bm - 1) / bm;
+    return g.symmetric ? (int64_t)g.tiles_n * (g.tiles_n + 1) / 2 : tm * g.tiles_n;
+}
+
 template <class CF, bool HAS_D, bool HAS_C, bool HAS_CT>
 hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s) {
-    const int64_t tiles = (int64_t)((g.M + CF::BM - 1) / CF::BM) * g.tiles_n;
+    const int64_t tiles = launch_tiles(g, CF::BM);
     if (g.vec_p && g.vec_q && g.K % 8 == 0)
         hipLaunchKernelGGL((k_gemm_nt<CF, HAS_D, HAS_C, HAS_CT, true>), dim3((unsigned)tiles), dim3(CF::THREADS), 0, s, g);
     else
@@ -356,6 +642,29 @@ hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s) {
                            g);
     return hipGetLastError();
 }
+
+template <class CF, bool HAS_D, bool HAS_C, bool HAS_CT>
+hipError_t launch_dma_t(const GemmArgs& g, hipStream_t s) {
+    const int64_t tiles = launch_tiles(g, CF::BM);
+    hipLaunchKernelGGL((k_gemm_nt_dma<CF, HAS_D, HAS_C, HAS_CT>), dim3((unsigned)tiles), dim3(CF::THREADS), 0, s, g);
+    return hipGetLastError();
+}
+
+template <class CF>
+hipError_t launch_gemm_dma(GemmArgs g, hipStream_t s) {
+    g.tiles_n = (int)((g.N + CF::BN - 1) / CF::BN);
+    const bool d = g.D != nullptr, c = g.C != nullptr, ct = g.CT != nullptr;
+    if (d && c && ct) return launch_dma_t<CF, true, true, true>(g, s);
+    if (d && c) return launch_dma_t<CF, true, true, false>(g, s);
+    if (d && ct) return launch_dma_t<CF, true, false, true>(g, s);
+    if (c && ct) return launch_dma_t<CF, false, true, true>(g, s);
+    if (c) return launch_dma_t<CF, false, true, false>(g, s);
+    if (ct) return launch_dma_t<CF, false, false, true>(g, s);
+    return hipErrorInvalidValue;
+}
+
+template <class CF>
+bool dma_ok(const GemmArgs& g) { return g.vec_p && g.vec_q && g.K % CF::BK == 0; }
 
 template <class CF>
 hipError_t launch_gemm_cfg(GemmArgs g, hipStream_t s) {
@@ -380,10 +689,15 @@ int gemm_cfg_override() {
     return idx;
 }
 
+// The direct-to-LDS kernel with 8 waves of 128 x 64 where it applies (K a
+// multiple of 64, 16-byte operand rows) and the product has at least two
+// rounds of 256 x 256 tiles; else the register-staged 256 x 256 or 128 x 128
+// kernel by the same rule.
 int gemm_cfg_auto(const GemmArgs& g) {
     const int64_t tm = (g.M + 255) / 256, tn = (g.N + 255) / 256;
     const int64_t active = g.symmetric ? tm * (tm + 1) / 2 : tm * tn;
-    return active >= 4 * kCUs ? 2 : 0;
+    if (active < 2 * kCUs) return 0;
+    return (g.vec_p && g.vec_q && g.K % 64 == 0) ? 9 : 2;
 }
 
 }  // namespace
@@ -392,12 +706,23 @@ int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127)
 int norm_blocks() { return kNormBlocks; }
 
 hipError_t launch_gemm_nt(GemmArgs g, hipStream_t s) {
+    static const bool remap = [] {
+        const char* e = getenv("VE_GEMM_XCD");
+        return e ? atoi(e) != 0 : true;
+    }();
+    g.xcd_remap = remap;
     const int cfg = gemm_cfg_override();
     switch (cfg >= 0 ? cfg : gemm_cfg_auto(g)) {
 #define VE_GEMM_CASE(ID, BM, BN, BK, WM, WN) \
         case ID: return launch_gemm_cfg<Cfg<BM, BN, BK, WM, WN>>(g, s);
         VE_GEMM_CFGS(VE_GEMM_CASE)
 #undef VE_GEMM_CASE
+#define VE_DMA_CASE(ID, WM, WN, BK, ST)                                                    \
+        case ID:                                                                           \
+            return dma_ok<DmaCfg<WM, WN, BK, ST>>(g) ? launch_gemm_dma<DmaCfg<WM, WN, BK, ST>>(g, s) \
+                                                     : launch_gemm_cfg<Cfg<256, 256, 64, 128, 64>>(g, s);
+        VE_DMA_CFGS(VE_DMA_CASE)
+#undef VE_DMA_CASE
         default: return hipErrorInvalidValue;
     }
 }
