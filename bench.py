@@ -176,9 +176,34 @@ def time_muon(torch, ve, dev, rows=8192, cols=28672, steps=3, warmup=1):
     log(f"[bench] muon newton-schulz {rows}x{cols}: {ms:.3f} ms, {tf:.1f} TFLOP/s")
     del G, out, ws
     torch.cuda.empty_cache()
+    # context: the same iteration in torch (hipBLASLt products with the scalars
+    # fused into addmm), timed the same way
+    m, n = min(rows, cols), max(rows, cols)
+    X = torch.randn(m, n, device=dev, dtype=torch.bfloat16, generator=g) / (m * n) ** 0.5
+    a_, b_, c_ = muon.NS_COEFFS
+
+    def torch_ns(X):
+        for _ in range(5):
+            A = X @ X.t()
+            B = torch.addmm(A, A, A, beta=b_, alpha=c_)
+            X = torch.addmm(X, B, X, beta=a_)
+        return X
+    torch_ns(X)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        torch_ns(X)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    tms = t0.elapsed_time(t1) / steps
+    log(f"[bench] torch addmm iteration for comparison: {tms:.3f} ms")
+    del X
+    torch.cuda.empty_cache()
     return {"workload": f"Muon Newton-Schulz, 5 steps, one {rows}x{cols} bf16 matrix (LLaMA-3-70B MLP)",
             "bound": "mfma", "ms": round(ms, 4), "flops": flops, "achieved": round(tf, 1),
-            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "torch_addmm_ms": round(tms, 4)}
 
 
 def copy_ceiling(torch, dev, gib, reps=10):
