@@ -268,3 +268,37 @@ def test_full_size_products_sampled(name, m, n):
             assert abs(C[rows[t], cols[t]] - want[0, 0]) <= bd[0, 0], (name, rows[t], cols[t])
     del X, XT, A, B, Y, YT
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("M,N,K,sym", [(7000, 7040, 1024, False), (8000, 8000, 1024, True), (6000, 9000, 2880, False)])
+def test_large_ragged_products_sampled(M, N, K, sym):
+    """Products large enough for the direct-to-LDS kernel, with ragged tile
+    edges (rows past M or N read clamped rows whose outputs are dropped) and a
+    partial last tile of a symmetric product: sampled elements within the
+    bound, C^T equal to C, the symmetric result exactly symmetric."""
+    import torch
+    ve = _ve()
+    g = torch.Generator(device=DEV)
+    g.manual_seed(M + N + K)
+    P = torch.randn(M, K, generator=g, device=DEV).to(torch.bfloat16).view(torch.int16)
+    Q = P if sym else torch.randn(N, K, generator=g, device=DEV).to(torch.bfloat16).view(torch.int16)
+    D = torch.randn(M, N, generator=g, device=DEV).to(torch.bfloat16).view(torch.int16)
+    if sym:
+        D = (D.view(torch.bfloat16) + D.view(torch.bfloat16).t()).contiguous().view(torch.int16)
+    C = _empty((M, N))
+    CT = None if sym else _empty((N, M))
+    _say(f"[gpu] large product M={M} N={N} K={K} symmetric={sym}")
+    ve.gemm_bf16_nt(P, Q, C=C, CT=CT, D=D, alpha=0.75, beta=-0.5, symmetric=sym)
+    torch.cuda.synchronize()
+    if sym:
+        assert torch.equal(C, C.view(torch.bfloat16).t().contiguous().view(torch.int16))
+    else:
+        assert torch.equal(C.view(torch.bfloat16).t().contiguous().view(torch.int16), CT)
+    Ph, Qh, Dh, Ch = _host(P), _host(Q), _host(D), _host(C)
+    rng = np.random.default_rng(1)
+    rows = np.concatenate([rng.integers(0, M, 200), [M - 1, M - 1, 0]])
+    cols = np.concatenate([rng.integers(0, N, 200), [N - 1, 0, N - 1]])
+    for i, j in zip(rows, cols):
+        want = muon.gemm_nt(Ph[i:i + 1], Qh[j:j + 1], Dh[i:i + 1, j:j + 1], 0.75, -0.5)
+        bd = product_bound(Ph[i:i + 1], Qh[j:j + 1], Dh[i:i + 1, j:j + 1], 0.75, -0.5, C=want)
+        assert abs(Ch[i, j] - want[0, 0]) <= bd[0, 0], (i, j, Ch[i, j], want[0, 0])
