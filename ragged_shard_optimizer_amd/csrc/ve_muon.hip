@@ -70,11 +70,7 @@ struct Cfg {
 // The configurations compiled in; VE_GEMM_CFG (environment) selects one for tuning.
 #define VE_GEMM_CFGS(X) \
     X(0, 128, 128, 64, 64, 64) \
-    X(1, 256, 128, 64, 128, 64) \
-    X(2, 256, 256, 64, 128, 64) \
-    X(3, 256, 256, 32, 128, 64) \
-    X(4, 256, 128, 64, 64, 64) \
-    X(5, 128, 128, 32, 64, 64)
+    X(2, 256, 256, 64, 128, 64)
 
 constexpr int kNormBlocks = 1024;    // partial sums of the Frobenius norm
 constexpr int kCUs = 256;           // MI355X compute units
@@ -363,11 +359,7 @@ struct DmaCfg {
 
 #define VE_DMA_CFGS(X) \
     X(6, 128, 128, 64, 2) \
-    X(7, 128, 128, 32, 3) \
-    X(8, 128, 128, 32, 4) \
-    X(9, 128, 64, 64, 2) \
-    X(10, 128, 64, 32, 3) \
-    X(11, 128, 64, 32, 4)
+    X(9, 128, 64, 64, 2)
 
 template <class CF, bool HAS_D, bool HAS_C, bool HAS_CT>
 __global__ void __launch_bounds__(CF::THREADS) k_gemm_nt_dma(GemmArgs g) {
@@ -465,9 +457,13 @@ __global__ void __launch_bounds__(CF::THREADS) k_gemm_nt_dma(GemmArgs g) {
                     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
                 }
-                __builtin_amdgcn_sched_group_barrier(kSchedMfma, TM * TN - (TM + TN), 0);
+            }
+            constexpr int kRestMid = TM * TN - (TM + TN), kRestLast = TM * TN;
+            static_assert(kRestMid >= 0, "sub-step too small for the interleave");
+            if (kk + 1 < BK / 16) {
+                if constexpr (kRestMid > 0) __builtin_amdgcn_sched_group_barrier(kSchedMfma, kRestMid, 0);
             } else {
-                __builtin_amdgcn_sched_group_barrier(kSchedMfma, TM * TN, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, kRestLast, 0);
             }
         }
     }

@@ -145,3 +145,35 @@ def test_tensor_spanning_many_ranks_and_unsorted_specs():
         assert p.query(r)[:2] == (nv, nb)
         for k in range(3):
             assert p.slice(r, k) == oracle.slice_(specs, 6, 384, r, k)
+
+
+def test_muon_workspace_and_argument_checks():
+    # sizing is pure host arithmetic: X, X^T twice (m*n each), A and B (m*m), norm partials
+    ve_ = ve
+    m, n = 8192, 28672
+    got = ve_.muon_workspace_bytes(m, n)
+    assert got >= 2 * 2 * (m * n * 2) + 2 * (m * m * 2)
+    assert ve_.muon_workspace_bytes(n, m) == got            # orientation does not matter
+    L = ve_.lib()
+    b = C.c_int64()
+    assert L.ve_muon_workspace_bytes(0, 5, C.byref(b)) == ve_.VE_ERR_INVALID_ARG
+    assert L.ve_muon_workspace_bytes(5, 5, None) == ve_.VE_ERR_INVALID_ARG
+    assert L.ve_muon_workspace_bytes(1 << 31, 1 << 31, C.byref(b)) == ve_.VE_ERR_UNSUPPORTED
+    # every rejection below happens before any device call
+    p = C.c_void_p(256)
+    need = ve_.muon_workspace_bytes(8, 8)
+    ns = L.ve_muon_newton_schulz
+    assert ns(None, p, 8, 8, 5, 1e-7, p, need, None) == ve_.VE_ERR_INVALID_ARG
+    assert ns(p, p, 0, 8, 5, 1e-7, p, need, None) == ve_.VE_ERR_INVALID_ARG
+    assert ns(p, p, 8, 8, 65, 1e-7, p, need, None) == ve_.VE_ERR_INVALID_ARG
+    assert ns(p, p, 8, 8, 5, float("nan"), p, need, None) == ve_.VE_ERR_INVALID_ARG
+    assert ns(p, p, 8, 8, 5, 1e-7, p, need - 1, None) == ve_.VE_ERR_INVALID_ARG
+    assert "workspace" in ve_.lib().ve_last_error().decode()
+    assert ns(p, p, 8, 8, 5, 1e-7, C.c_void_p(272), need, None) == ve_.VE_ERR_INVALID_ARG
+    assert "aligned" in ve_.lib().ve_last_error().decode()
+    gm = L.ve_gemm_bf16_nt
+    assert gm(None, 8, p, 8, None, 0, p, 8, None, 0, 8, 8, 8, 1.0, 0.0, 0, None) == ve_.VE_ERR_INVALID_ARG
+    assert gm(p, 8, p, 8, None, 0, None, 0, None, 0, 8, 8, 8, 1.0, 0.0, 0, None) == ve_.VE_ERR_INVALID_ARG
+    assert gm(p, 4, p, 8, None, 0, p, 8, None, 0, 8, 8, 8, 1.0, 0.0, 0, None) == ve_.VE_ERR_INVALID_ARG
+    assert gm(p, 8, p, 8, None, 0, p, 8, None, 0, 8, 4, 8, 1.0, 0.0, 1, None) == ve_.VE_ERR_INVALID_ARG
+    assert gm(p, 8, p, 8, p, 4, p, 8, None, 0, 8, 8, 8, 1.0, 0.5, 0, None) == ve_.VE_ERR_INVALID_ARG
