@@ -206,6 +206,38 @@ def time_muon(torch, ve, dev, rows=8192, cols=28672, steps=3, warmup=1):
             "torch_addmm_ms": round(tms, 4)}
 
 
+def time_planner(ve, sizes=(64, 256, 1024)):
+    """The structure-aware planner (host) on the models the pages evaluate it
+    on: whole-model padding and planning time per FSDP size, each distinct
+    bucket planned once."""
+    import numpy as np
+    from synth.models import MODELS, PLANNER_GRANULARITIES
+    out = {}
+    for name, fn in MODELS.items():
+        for g in PLANNER_GRANULARITIES:
+            buckets = fn(g)
+            for m in sizes:
+                t0 = time.perf_counter()
+                cache, pad, alloc, lb_pad, lb_alloc = {}, 0, 0, 0, 0
+                for b in buckets:
+                    sh = np.array([[t.rows, t.cols, t.block_rows] for t in b], dtype=np.int64)
+                    key = sh.tobytes()
+                    if key not in cache:
+                        _, S, lb = ve.plan_layout(sh, m)
+                        cache[key] = (S, lb)
+                    S, lb = cache[key]
+                    total = int((sh[:, 0] * sh[:, 1]).sum())
+                    pad += m * S - total
+                    alloc += m * S
+                    lb_pad += m * lb - total
+                    lb_alloc += m * lb
+                out[f"{name} rows/unit {g} fsdp {m}"] = {
+                    "padding_pct": round(100 * pad / alloc, 4), "lower_bound_pct": round(100 * lb_pad / lb_alloc, 4),
+                    "seconds": round(time.perf_counter() - t0, 4)}
+    log(f"[bench] planner: {len(out)} model/granularity/FSDP cases")
+    return out
+
+
 def copy_ceiling(torch, dev, gib, reps=10):
     """A plain device-to-device copy (torch's copy kernel) of ``gib`` GiB:
     read + write bytes over its time -- the practical streaming ceiling."""
@@ -236,6 +268,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-group-ops", action="store_true", help="skip timing the DBuffer group operations")
     ap.add_argument("--no-muon", action="store_true", help="skip timing Muon's Newton-Schulz iteration")
+    ap.add_argument("--no-planner", action="store_true", help="skip the bucket planner's padding / time report")
     ap.add_argument("--copy-gib", type=float, default=2.0,
                     help="size of the plain device copy that measures the copy ceiling (0: skip)")
     args = ap.parse_args()
@@ -330,6 +363,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_muon:
         out["muon"] = time_muon(torch, ve, dev)
+    if not args.no_planner:
+        out["planner"] = time_planner(ve)
     if args.copy_gib > 0:
         out["copy_ceiling"] = copy_ceiling(torch, dev, args.copy_gib)
         out["copy_ceiling_frac"] = round(gbs / out["copy_ceiling"]["gbs"], 4)
