@@ -291,11 +291,17 @@ int64_t set_inline(StepArgs& a, const RankTables& rt, const HostWork& w, size_t 
 }
 
 // Workgroup path shape: threads and 4-element groups per thread for blocks
-// of up to `groups` groups.  Measured on MI355X, 6..12 groups per thread
-// stream best (fewer leave the per-block prologue exposed, more add
-// per-thread serial work): take the largest workgroup that gives each thread
-// at least 6 groups, else 256 threads.  VE_WG_THREADS / VE_WG_GPT override
-// it (launch-shape tuning).
+// of up to `groups` groups.  Measured on MI355X over the model workloads
+// (one launch per rank, all blocks of a class share the shape):
+//   2,049 .. 4,096 groups (128x128 tiles): 1024 threads x 4 (two resident
+//     workgroups per CU) beat 512 x 8 by ~2%;
+//   4,097 .. 12,288 groups (row blocks of 16K..48K elements): 512 threads
+//     with 16 (up to 8,192 groups), 20 or 24 groups each beat 1024 threads
+//     by 1-2%, even with idle lanes in the last slot;
+//   larger: 1024 threads x 14 / 16;
+//   up to 2,048 groups: the largest workgroup that gives each thread at
+//     least 6 groups (fewer leave the per-block prologue exposed), else 256.
+// VE_WG_THREADS / VE_WG_GPT override it (launch-shape tuning).
 void wg_shape(int32_t groups, int& threads, int& gpt) {
     const char* et = std::getenv("VE_WG_THREADS");
     const char* eg = std::getenv("VE_WG_GPT");
@@ -304,22 +310,36 @@ void wg_shape(int32_t groups, int& threads, int& gpt) {
         gpt = std::atoi(eg);
         if (wg_config_supported(threads, gpt) && (int64_t)threads * gpt >= groups) return;
     }
-    auto fit = [&](int t, int& g) {
-        for (g = (int)ceil_div(groups, t); g <= 32; ++g)
+    auto fit = [&](int t, int min_g, int& g) {
+        for (g = std::max(min_g, (int)ceil_div(groups, t)); g <= 32; ++g)
             if (wg_config_supported(t, g)) return true;
         return false;
     };
+    int g = 0;
+    if (groups > 2048 && groups <= 4096 && fit(1024, 1, g)) {
+        threads = 1024;
+        gpt = g;
+        return;
+    }
+    if (groups > 4096 && groups <= 12288 && fit(512, 16, g)) {
+        threads = 512;
+        gpt = g;
+        return;
+    }
+    if (groups > 12288 && fit(1024, 1, g)) {
+        threads = 1024;
+        gpt = g;
+        return;
+    }
     for (int t : {1024, 512}) {
-        int g;
-        if (ceil_div(groups, t) >= 6 && fit(t, g)) {
+        if (ceil_div(groups, t) >= 6 && fit(t, 1, g)) {
             threads = t;
             gpt = g;
             return;
         }
     }
     for (int t : {256, 512, 1024}) {
-        int g;
-        if (fit(t, g)) {
+        if (fit(t, 1, g)) {
             threads = t;
             gpt = g;
             return;

@@ -84,6 +84,18 @@ __device__ __forceinline__ float group_max(float v, int G) {
 }
 
 // Wave maximum, returned as a wave-uniform value.
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS (and
+// scalar) accesses, not for its outstanding global loads and stores.  A
+// __syncthreads also drains those, which would expose the write latency of a
+// block's phase-1 stores, and any loads already issued for the next block,
+// at every reduction.  The memory clobbers keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float wave_max(float v) {
     v = group_max(v, 32);
     const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
@@ -296,22 +308,31 @@ __device__ __forceinline__ float elem_g(const In<CH>& x, int i) {
     return (i & 1) ? bf_hi(x.g[i >> 1]) : bf_lo(x.g[i >> 1]);
 }
 
+// AdamW update of one chunk's master values from its held inputs; folds the
+// fresh moments into the running absmax (nothing when act is false: an idle
+// lane whose registers duplicate a valid chunk).
+template <int CH>
+__device__ __forceinline__ void adam_update(const In<CH>& x, float (&mst)[CH], float sm, float sv,
+                                            const StepScalars& sc, float& am, float& av, bool act = true) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        float m1, v1;
+        moments(elem_g(x, i), code_at(x.m[i >> 2], i & 3), code_at(x.v[i >> 2], i & 3), sm, sv, sc, m1, v1);
+        am = fmaxf(am, act ? fabsf(m1) : 0.f);
+        av = fmaxf(av, act ? v1 : 0.f);
+        const float d = __builtin_fmaf(__builtin_amdgcn_sqrtf(v1), sc.inv_sqrt_bc2, sc.eps);
+        const float u = m1 * __builtin_amdgcn_rcpf(d);
+        mst[i] = __builtin_fmaf(-sc.step_size, u, mst[i] * sc.decay);
+    }
+}
+
 // Phase 1 on one chunk: moments, AdamW update, writes of master, bf16 param
 // and the gradient copy; folds the chunk into the running absmax.
 template <int CH>
 __device__ __forceinline__ void phase1(const In<CH>& x, float (&mst)[CH], const Ptrs& p, const ChunkPos& c,
                                        bool vec, float sm, float sv, const StepScalars& sc, float& am,
                                        float& av) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-        float m1, v1;
-        moments(elem_g(x, i), code_at(x.m[i >> 2], i & 3), code_at(x.v[i >> 2], i & 3), sm, sv, sc, m1, v1);
-        am = fmaxf(am, fabsf(m1));
-        av = fmaxf(av, v1);
-        const float d = __builtin_fmaf(__builtin_amdgcn_sqrtf(v1), sc.inv_sqrt_bc2, sc.eps);
-        const float u = m1 * __builtin_amdgcn_rcpf(d);
-        mst[i] = __builtin_fmaf(-sc.step_size, u, mst[i] * sc.decay);
-    }
+    adam_update(x, mst, sm, sv, sc, am, av);
     uint32_t pb[CH / 2];
 #pragma unroll
     for (int i = 0; i < CH / 2; ++i) pb[i] = pack_bf16x2(mst[2 * i], mst[2 * i + 1]);
@@ -348,12 +369,11 @@ __device__ __forceinline__ uint32_t quant_byte(float x, float inv) {
     return (uint32_t)((int32_t)q) & 0xffu;
 }
 
-// Phase 2 on one chunk: recompute the moments from the held inputs and write
-// their codes under the block's new scales.
+// Codes of one chunk under the block's new scales, recomputed from the held
+// inputs.
 template <int CH>
-__device__ __forceinline__ void phase2(const In<CH>& x, const Ptrs& p, const ChunkPos& c, bool vec, float sm,
-                                       float sv, float im, float iv, const StepScalars& sc) {
-    uint32_t qm[CH / 4], qv[CH / 4];
+__device__ __forceinline__ void quantise(const In<CH>& x, float sm, float sv, float im, float iv,
+                                         const StepScalars& sc, uint32_t (&qm)[CH / 4], uint32_t (&qv)[CH / 4]) {
 #pragma unroll
     for (int i = 0; i < CH / 4; ++i) qm[i] = qv[i] = 0;
 #pragma unroll
@@ -363,6 +383,15 @@ __device__ __forceinline__ void phase2(const In<CH>& x, const Ptrs& p, const Chu
         qm[i >> 2] |= quant_byte(m1, im) << (8 * (i & 3));
         qv[i >> 2] |= quant_byte(v1, iv) << (8 * (i & 3));
     }
+}
+
+// Phase 2 on one chunk: recompute the moments from the held inputs and write
+// their codes under the block's new scales.
+template <int CH>
+__device__ __forceinline__ void phase2(const In<CH>& x, const Ptrs& p, const ChunkPos& c, bool vec, float sm,
+                                       float sv, float im, float iv, const StepScalars& sc) {
+    uint32_t qm[CH / 4], qv[CH / 4];
+    quantise(x, sm, sv, im, iv, sc, qm, qv);
     if (vec) {
         if constexpr (CH == 16) {
             stv<kStream<CH>>((VE_GLOBAL u32x4*)(p.m_q + c.s), u32x4{qm[0], qm[1], qm[2], qm[3]});
@@ -380,6 +409,87 @@ __device__ __forceinline__ void phase2(const In<CH>& x, const Ptrs& p, const Chu
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Block-relative access for fully vectorised workgroup blocks.  Every
+// stream is a raw buffer resource (wave-uniform base at the block's first
+// element, range = the block's span) addressed by one 32-bit per-lane
+// element offset per 4-element chunk; the same offset serves the tensor-side
+// gradient and the shard-side arrays.  A lane without a chunk uses an offset
+// beyond every range: the hardware's range check then returns zeros for its
+// loads and drops its stores, so a block needs no branch at all (zero inputs
+// give zero moments, which never raise the absmax).
+struct FastRsrc {
+    __amdgpu_buffer_rsrc_t grad;        // bf16, tensor element e0
+    __amdgpu_buffer_rsrc_t grad_shard;  // bf16, shard element shard_base + e0 (same for the rest)
+    __amdgpu_buffer_rsrc_t master;      // fp32
+    __amdgpu_buffer_rsrc_t m_q;         // int8
+    __amdgpu_buffer_rsrc_t v_q;         // int8
+    __amdgpu_buffer_rsrc_t param;       // bf16
+};
+// Buffer resource word 3 for raw (unformatted, stride 0) buffers on gfx9-
+// family targets; cache-policy bit 1 = non-temporal.
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kBufNT = VE_NONTEMPORAL ? 2 : 0;
+// FAST blocks span fewer than 2^27 elements, so every byte offset inside a
+// block, and every scalar slot offset (at most twice the span), is below
+// 2^30.  A lane without a chunk takes the per-lane byte offset kNoChunkByte:
+// past the end of every stream, with or without the scalar part added, and
+// without wrapping 32 bits.
+constexpr int64_t kFastMaxSpan = int64_t(1) << 27;
+constexpr uint32_t kNoChunkByte = 1u << 31;
+
+template <class T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const VE_GLOBAL T* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)base, (short)0, (int)(uint32_t)bytes,
+                                             kRawBufferWord3);
+}
+
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Byte offsets of one chunk in the 1-, 2- and 4-byte streams: a per-lane
+// part (v*) and a wave-uniform part (s*, the instruction's scalar offset).
+struct ChunkAddr {
+    uint32_t v1, v2, v4;
+    uint32_t s1, s2, s4;
+};
+
+__device__ __forceinline__ void load_in_fast(In<4>& x, const FastRsrc& f, const ChunkAddr& a) {
+    const i32x2 g = __builtin_amdgcn_raw_buffer_load_b64(f.grad, (int)a.v2, (int)a.s2, kBufNT);
+    x.g[0] = (uint32_t)g.x;
+    x.g[1] = (uint32_t)g.y;
+    x.m[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(f.m_q, (int)a.v1, (int)a.s1, kBufNT);
+    x.v[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(f.v_q, (int)a.v1, (int)a.s1, kBufNT);
+}
+
+__device__ __forceinline__ void load_master_fast(float (&mst)[4], const FastRsrc& f, const ChunkAddr& a) {
+    const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(f.master, (int)a.v4, (int)a.s4, kBufNT);
+    mst[0] = __int_as_float(v.x);
+    mst[1] = __int_as_float(v.y);
+    mst[2] = __int_as_float(v.z);
+    mst[3] = __int_as_float(v.w);
+}
+
+__device__ __forceinline__ void phase1_fast(const In<4>& x, float (&mst)[4], const FastRsrc& f,
+                                            const ChunkAddr& a, float sm, float sv, const StepScalars& sc,
+                                            float& am, float& av) {
+    adam_update(x, mst, sm, sv, sc, am, av);
+    const uint32_t p0 = pack_bf16x2(mst[0], mst[1]), p1 = pack_bf16x2(mst[2], mst[3]);
+    const i32x4 mv = {__float_as_int(mst[0]), __float_as_int(mst[1]), __float_as_int(mst[2]), __float_as_int(mst[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(mv, f.master, (int)a.v4, (int)a.s4, kBufNT);
+    __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int32_t)p0, (int32_t)p1}, f.param, (int)a.v2, (int)a.s2, kBufNT);
+    __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int32_t)x.g[0], (int32_t)x.g[1]}, f.grad_shard, (int)a.v2,
+                                          (int)a.s2, kBufNT);
+}
+
+__device__ __forceinline__ void phase2_fast(const In<4>& x, const FastRsrc& f, const ChunkAddr& a, float sm,
+                                            float sv, float im, float iv, const StepScalars& sc) {
+    uint32_t qm[1], qv[1];
+    quantise(x, sm, sv, im, iv, sc, qm, qv);
+    __builtin_amdgcn_raw_buffer_store_b32((int32_t)qm[0], f.m_q, (int)a.v1, (int)a.s1, kBufNT);
+    __builtin_amdgcn_raw_buffer_store_b32((int32_t)qv[0], f.v_q, (int)a.v1, (int)a.s1, kBufNT);
 }
 
 template <int CH>
@@ -493,83 +603,257 @@ __global__ void __launch_bounds__(256) k_step_small(StepArgs a) {
 // it.  All input loads are therefore issued first (they stay in registers),
 // and each group's master is loaded MA groups ahead of its update, i.e.
 // before the stores of the groups in between.
-template <int T, int GPT>
-__global__ void __launch_bounds__(T) k_step_wg(StepArgs a) {
-    constexpr int CH = kWgChunk;
-    constexpr int MA0 = VE_MASTER_AHEAD > 0 ? VE_MASTER_AHEAD : (GPT >= 12 ? 8 : 4);
-    constexpr int MA = MA0 < GPT ? MA0 : GPT;
-    __shared__ float s_red[2][T / 64];
-    const int tid = threadIdx.x;
-    int64_t local;
-    const Seg sg = find_inline(a, blockIdx.x, local);
-    const ve_shard_state st = a.states[blockIdx.y];
-    const Geo geo = block_geo<CH>(sg, local);
-    const Ptrs p = make_ptrs<true>(st, sg.tensor);
-    const float sm = sload(st.m_scale + geo.blk), sv = sload(st.v_scale + geo.blk);
+//
+// The counter waits are placed by the compiler, and any control flow that
+// makes the number of accesses in flight path-dependent turns them into
+// full drains (every group's update would then wait for the previous
+// group's stores to reach memory).  A block whose chunks are all full and
+// aligned -- every block of a contiguous, 16-byte-aligned layout -- is
+// therefore handled by a straight-line FAST form: block-relative vector
+// accesses only, the loads of idle lanes clamped to the block's last chunk
+// (in bounds, result unused), the arithmetic done by every lane, and only
+// the stores and the absmax contribution predicated.  Two FAST forms: LINEAR,
+// where a lane's chunk in slot k sits at lane0 + k * step (one contiguous run
+// per block, or tiles whose rows hold a whole number of workgroup sweeps), so
+// a lane keeps three byte offsets in all and the slot part goes into the
+// instruction's scalar offset; and TILED, with one offset per chunk.
+// Anything else takes the general form.
+enum WgMode : int { kWgGeneral = 0, kWgLinear = 1, kWgTiled = 2 };
 
-    In<CH> x[GPT];
-    float mst[MA + 1][CH];  // ring of master values in flight
-    float am = 0.f, av = 0.f;
+struct WgItem {
+    Seg sg;
+    Geo geo;
+    Ptrs p;
+    FastRsrc fb;  // block-relative buffers (FAST modes)
+    float sm, sv;
+    float* m_scale;
+    float* v_scale;
+    int rot;
+    int mode;        // WgMode
+    uint32_t lane0;  // LINEAR: this lane's element offset in slot 0
+    uint32_t step;   // LINEAR: element offset between slots (wave-uniform)
+};
+
+// Item (state y, block xw of the launch's segment slice).
+template <int GPT>
+__device__ __forceinline__ WgItem wg_item_at(const StepArgs& a, int64_t y, int64_t xw) {
+    constexpr int CH = kWgChunk;
+    WgItem it;
+    int64_t local;
+    it.sg = find_inline(a, xw, local);
+    ve_shard_state st;
+    {
+        static_assert(sizeof(ve_shard_state) == 8 * sizeof(uint64_t), "eight pointers");
+        const uint64_t* src = reinterpret_cast<const uint64_t*>(a.states + y);
+        uint64_t* dst = reinterpret_cast<uint64_t*>(&st);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dst[i] = sload(src + i);
+    }
+    it.geo = block_geo<CH>(it.sg, local);
+    it.p = make_ptrs<true>(st, it.sg.tensor);
+    it.sm = sload(st.m_scale + it.geo.blk);
+    it.sv = sload(st.v_scale + it.geo.blk);
+    it.m_scale = st.m_scale;
+    it.v_scale = st.v_scale;
     // Register slot c holds group tid + ((c + rot) mod GPT) * T: neighbouring
     // workgroups start their sweeps at different offsets of their blocks, so
     // the sweep fronts of the resident blocks (whose starts are a multiple of
     // the block size apart) do not all address the same memory channels.
-    const int rot = VE_WG_ROTATE ? (int)(blockIdx.x % GPT) : 0;
-    auto slot_chunk = [&](int c) { return tid + ((c + rot) % GPT) * T; };
+    it.rot = VE_WG_ROTATE ? (int)(xw % GPT) : 0;
+    // FAST: every chunk full and naturally aligned, and the block's span
+    // small enough for 32-bit buffer offsets.
+    const int64_t span = (int64_t)(it.geo.nruns - 1) * it.geo.stride + it.geo.run;
+    const bool fast = it.p.aligned && ((it.geo.e0 | it.sg.shard_base | it.geo.run) & (CH - 1)) == 0 &&
+                      (it.geo.nruns == 1 || (it.geo.stride & (CH - 1)) == 0) && span < kFastMaxSpan;
+    const uint32_t tid = threadIdx.x, cpr = (uint32_t)it.geo.cpr;
+    if (!fast) {
+        it.mode = kWgGeneral;
+    } else if (it.geo.nruns == 1) {
+        it.mode = kWgLinear;
+        it.lane0 = tid * CH;
+        it.step = (uint32_t)blockDim.x * CH;
+    } else if (blockDim.x % cpr == 0) {
+        it.mode = kWgLinear;
+        it.lane0 = (tid / cpr) * (uint32_t)it.geo.stride + (tid % cpr) * CH;
+        it.step = (blockDim.x / cpr) * (uint32_t)it.geo.stride;
+    } else {
+        it.mode = kWgTiled;
+    }
+    if (fast) {
+        const int64_t s0 = it.sg.shard_base + it.geo.e0;
+        it.fb.grad = buf_rsrc(it.p.grad + it.geo.e0, 2 * span);
+        it.fb.grad_shard = buf_rsrc(it.p.grad_shard + s0, 2 * span);
+        it.fb.master = buf_rsrc(it.p.master + s0, 4 * span);
+        it.fb.m_q = buf_rsrc(it.p.m_q + s0, span);
+        it.fb.v_q = buf_rsrc(it.p.v_q + s0, span);
+        it.fb.param = buf_rsrc(it.p.param + s0, 2 * span);
+    }
+    return it;
+}
+
+template <int T, int GPT>
+__device__ __forceinline__ int wg_slot_chunk(const WgItem& it, int c) {
+    return (int)threadIdx.x + ((c + it.rot) % GPT) * T;
+}
+
+// TILED: element offset of chunk ci, kept per chunk (kNoChunkByte / 4 past
+// the block's end).
+__device__ __forceinline__ uint32_t tiled_off(const WgItem& it, int ci) {
+    constexpr int CH = kWgChunk;
+    const uint32_t cpr = (uint32_t)it.geo.cpr;
+    const uint32_t ri = (uint32_t)ci / cpr;
+    const uint32_t o = ri * (uint32_t)it.geo.stride + ((uint32_t)ci - ri * cpr) * CH;
+    return ci < it.geo.nchunks ? o : kNoChunkByte / 4;
+}
+
+// Byte offsets of register slot c's chunk.
+template <int T, int GPT, int MODE>
+__device__ __forceinline__ ChunkAddr wg_addr(const WgItem& it, const uint32_t (&off)[GPT], int c) {
+    ChunkAddr a;
+    if constexpr (MODE == kWgLinear) {
+        const int k = (c + it.rot) % GPT;  // wave-uniform slot
+        // Recomputed at every use (the opaque copy keeps the compiler from
+        // holding each slot's offsets in registers across the block).
+        uint32_t l0 = it.lane0;
+        opaque(l0);
+        const bool ok = (int)threadIdx.x < it.geo.nchunks - k * T;
+        const uint32_t so = (uint32_t)k * it.step;
+        a.v1 = ok ? l0 : kNoChunkByte;
+        a.v2 = ok ? l0 * 2u : kNoChunkByte;
+        a.v4 = ok ? l0 * 4u : kNoChunkByte;
+        a.s1 = so;
+        a.s2 = so * 2u;
+        a.s4 = so * 4u;
+    } else {
+        uint32_t o = off[c];
+        opaque(o);
+        a.v1 = o;
+        a.v2 = o * 2u;
+        a.v4 = o * 4u;
+        a.s1 = a.s2 = a.s4 = 0;
+    }
+    return a;
+}
+
+// Issue the input loads of every group and the master loads of the first MA
+// (FAST modes also record each group's offset).
+template <int T, int GPT, int MA, int MODE>
+__device__ __forceinline__ void wg_issue(In<kWgChunk> (&x)[GPT], float (&mst)[MA + 1][kWgChunk],
+                                         uint32_t (&off)[GPT], const WgItem& it) {
+    constexpr int CH = kWgChunk;
 #pragma unroll
     for (int c = 0; c < GPT; ++c) {
-        const int ci = slot_chunk(c);
-        if (ci < geo.nchunks) {
-            const ChunkPos cp = chunk_pos<CH>(geo, sg.shard_base, ci);
-            const bool vec = vec_ok<CH>(p, cp);
-            load_in(x[c], p, cp, vec);
-            if (c < MA) load_master(mst[c % (MA + 1)], p, cp, vec);
+        const int ci = wg_slot_chunk<T, GPT>(it, c);
+        if constexpr (MODE != kWgGeneral) {
+            if constexpr (MODE == kWgTiled) off[c] = tiled_off(it, ci);
+            const ChunkAddr ad = wg_addr<T, GPT, MODE>(it, off, c);
+            load_in_fast(x[c], it.fb, ad);
+            if (c < MA) load_master_fast(mst[c % (MA + 1)], it.fb, ad);
+            __builtin_amdgcn_sched_barrier(0);  // group-major issue order
+        } else if (ci < it.geo.nchunks) {
+            const ChunkPos cp = chunk_pos<CH>(it.geo, it.sg.shard_base, ci);
+            const bool vec = vec_ok<CH>(it.p, cp);
+            load_in(x[c], it.p, cp, vec);
+            if (c < MA) load_master(mst[c % (MA + 1)], it.p, cp, vec);
         }
     }
+    // every load issued before any arithmetic starts
+    if constexpr (MODE != kWgGeneral) __builtin_amdgcn_sched_barrier(0);
+}
+
+// One block: phase 1 (inputs already issued), the absmax reduction, phase 2.
+template <int T, int GPT, int MA, int MODE>
+__device__ __forceinline__ void wg_block(In<kWgChunk> (&x)[GPT], float (&mst)[MA + 1][kWgChunk],
+                                         const uint32_t (&off)[GPT], const WgItem& it, float (&red)[2][T / 64],
+                                         const StepScalars& sc) {
+    constexpr int CH = kWgChunk;
+    const int tid = threadIdx.x;
+    const int nch = it.geo.nchunks;
+    float am = 0.f, av = 0.f;
 #pragma unroll
     for (int c = 0; c < GPT; ++c) {
-        if (c + MA < GPT) {
-            const int cn = slot_chunk(c + MA);
-            if (cn < geo.nchunks) {
-                const ChunkPos cpn = chunk_pos<CH>(geo, sg.shard_base, cn);
-                load_master(mst[(c + MA) % (MA + 1)], p, cpn, vec_ok<CH>(p, cpn));
+        const int ci = wg_slot_chunk<T, GPT>(it, c);
+        if constexpr (MODE != kWgGeneral) {
+            if (c + MA < GPT) load_master_fast(mst[(c + MA) % (MA + 1)], it.fb, wg_addr<T, GPT, MODE>(it, off, c + MA));
+            phase1_fast(x[c], mst[c % (MA + 1)], it.fb, wg_addr<T, GPT, MODE>(it, off, c), it.sm, it.sv, sc, am, av);
+            // keep the groups in program order (hoisting later groups' work
+            // would run out of registers)
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            if (c + MA < GPT) {
+                const int cn = wg_slot_chunk<T, GPT>(it, c + MA);
+                if (cn < nch) {
+                    const ChunkPos cpn = chunk_pos<CH>(it.geo, it.sg.shard_base, cn);
+                    load_master(mst[(c + MA) % (MA + 1)], it.p, cpn, vec_ok<CH>(it.p, cpn));
+                }
             }
-        }
-        const int ci = slot_chunk(c);
-        if (ci < geo.nchunks) {
-            const ChunkPos cp = chunk_pos<CH>(geo, sg.shard_base, ci);
-            phase1(x[c], mst[c % (MA + 1)], p, cp, vec_ok<CH>(p, cp), sm, sv, a.sc, am, av);
+            if (ci < nch) {
+                const ChunkPos cp = chunk_pos<CH>(it.geo, it.sg.shard_base, ci);
+                phase1(x[c], mst[c % (MA + 1)], it.p, cp, vec_ok<CH>(it.p, cp), it.sm, it.sv, sc, am, av);
+            }
         }
     }
     am = wave_max(am);
     av = wave_max(av);
     if ((tid & 63) == 0) {
-        s_red[0][tid >> 6] = am;
-        s_red[1][tid >> 6] = av;
+        red[0][tid >> 6] = am;
+        red[1][tid >> 6] = av;
     }
-    __syncthreads();
+    lds_barrier();
     am = 0.f;
     av = 0.f;
 #pragma unroll
     for (int i = 0; i < T / 64; ++i) {
-        am = fmaxf(am, s_red[0][i]);
-        av = fmaxf(av, s_red[1][i]);
+        am = fmaxf(am, red[0][i]);
+        av = fmaxf(av, red[1][i]);
     }
     const float im = am > 0.f ? 127.0f / am : 0.f;
     const float iv = av > 0.f ? 127.0f / av : 0.f;
     if (tid == 0) {
-        ((VE_GLOBAL float*)st.m_scale)[geo.blk] = am / 127.0f;
-        ((VE_GLOBAL float*)st.v_scale)[geo.blk] = av / 127.0f;
+        ((VE_GLOBAL float*)it.m_scale)[it.geo.blk] = am / 127.0f;
+        ((VE_GLOBAL float*)it.v_scale)[it.geo.blk] = av / 127.0f;
     }
 #pragma unroll
     for (int c = 0; c < GPT; ++c) {
-        const int ci = slot_chunk(c);
-        if (ci < geo.nchunks) {
-            make_opaque(x[c]);
-            const ChunkPos cp = chunk_pos<CH>(geo, sg.shard_base, ci);
-            phase2(x[c], p, cp, vec_ok<CH>(p, cp), sm, sv, im, iv, a.sc);
+        const int ci = wg_slot_chunk<T, GPT>(it, c);
+        make_opaque(x[c]);
+        if constexpr (MODE != kWgGeneral) {
+            phase2_fast(x[c], it.fb, wg_addr<T, GPT, MODE>(it, off, c), it.sm, it.sv, im, iv, sc);
+            __builtin_amdgcn_sched_barrier(0);
+        } else if (ci < nch) {
+            const ChunkPos cp = chunk_pos<CH>(it.geo, it.sg.shard_base, ci);
+            phase2(x[c], it.p, cp, vec_ok<CH>(it.p, cp), it.sm, it.sv, im, iv, sc);
         }
     }
+}
+
+// Groups whose master values are in flight ahead of their update: more for
+// the FAST forms with many groups per thread; the general form keeps 4 (its
+// register use would otherwise set the kernel's occupancy).
+template <int GPT, int MODE>
+struct WgAhead {
+    static constexpr int v0 =
+        MODE == kWgGeneral ? 4 : (VE_MASTER_AHEAD > 0 ? VE_MASTER_AHEAD : (GPT >= 12 ? 8 : 4));
+    static constexpr int value = v0 < GPT ? v0 : GPT;
+};
+
+template <int T, int GPT, int MODE>
+__device__ __forceinline__ void wg_one(const WgItem& it, float (&red)[2][T / 64], const StepScalars& sc) {
+    constexpr int MA = WgAhead<GPT, MODE>::value;
+    In<kWgChunk> x[GPT];
+    float mst[MA + 1][kWgChunk];  // ring of master values in flight
+    uint32_t off[GPT];
+    wg_issue<T, GPT, MA, MODE>(x, mst, off, it);
+    wg_block<T, GPT, MA, MODE>(x, mst, off, it, red, sc);
+}
+
+template <int T, int GPT>
+__global__ void __launch_bounds__(T) k_step_wg(StepArgs a) {
+    __shared__ float s_red[2][T / 64];
+    const WgItem it = wg_item_at<GPT>(a, blockIdx.y, blockIdx.x);
+    if (it.mode == kWgLinear) wg_one<T, GPT, kWgLinear>(it, s_red, a.sc);
+    else if (it.mode == kWgTiled) wg_one<T, GPT, kWgTiled>(it, s_red, a.sc);
+    else wg_one<T, GPT, kWgGeneral>(it, s_red, a.sc);
 }
 
 // Blocks too large for registers: two sweeps, the second re-reading inputs.

@@ -113,6 +113,31 @@ def test_edge_layouts(case):
     tally.check()
 
 
+# Workgroup blocks take one of three access forms: linear (one contiguous run,
+# or tiles whose rows hold a whole number of workgroup sweeps), per-chunk
+# offsets (other tiles), general (chunks not all full and aligned).  Each
+# tensor below lands in one form; every launch shape here holds its largest
+# block, so the forced shape is the one launched.
+FORM_TENSORS = [
+    TensorDef("tile32", 200, 512, 64, 128),  # 64x128 tiles: 32 chunks per row, divides every T
+    TensorDef("tile24", 130, 384, 64, 96),   # 64x96 tiles: 24 chunks per row, divides no T
+    TensorDef("rows", 37, 1024, 4, 1024),    # contiguous 4096-element blocks, 1-row last panel
+    TensorDef("odd", 50, 102, 25, 102),      # 2550-element row blocks: a partial last chunk
+]
+
+
+@pytest.mark.parametrize("shape", [(256, 8), (512, 4), (1024, 2), (1024, 8), (512, 16)])
+def test_workgroup_access_forms(shape, monkeypatch):
+    monkeypatch.setenv("VE_WG_THREADS", str(shape[0]))
+    monkeypatch.setenv("VE_WG_GPT", str(shape[1]))
+    lay = plan_p0(FORM_TENSORS, 2)
+    assert max(t.block_rows * t.block_cols for t in FORM_TENSORS) <= 4 * shape[0] * shape[1]
+    cfg = Config("forms", list(FORM_TENSORS), fsdp=2, grad_scale=1e-3, steps=2)
+    tally = Tally()
+    _run_parity(cfg, lay, [0, 1], 2, tally)
+    tally.check()
+
+
 def test_one_element_blocks_codes_exact():
     # 1-element blocks: every nonzero code is +-127 and the scale is |m|/127
     cfg, lay = _explicit("unit", [TensorDef("a", 999, 1, 1, 1), TensorDef("b", 21, 17, 1, 1)], [0, 1008], 2, 768)
