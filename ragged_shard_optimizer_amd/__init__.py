@@ -118,6 +118,20 @@ class Plan:
         self.fsdp_size = int(fsdp_size)
         self.shard_elems = int(shard_elems)
         self.device = int(device)
+        self._pieces = {}
+
+    def pieces(self, rank: int):
+        """[(tensor, elem_end)] of every tensor ``rank`` (or the whole bucket
+        for -1) holds a piece of; queried once per rank and kept (the plan is
+        immutable)."""
+        if rank not in self._pieces:
+            got = []
+            for k in range(self.n_tensors):
+                sl = self.slice(rank, k)
+                if sl is not None:
+                    got.append((k, sl[2]))
+            self._pieces[rank] = got
+        return self._pieces[rank]
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:
@@ -154,10 +168,9 @@ class Plan:
         _require_buffer(bucket, need, 2, "bucket")
         if len(grad_table.grads) != self.n_tensors:
             raise ValueError("grad table length != number of tensors in the plan")
-        for k in range(self.n_tensors):
-            sl = self.slice(rank, k)
+        for k, end in self.pieces(rank):
             g = grad_table.grads[k]
-            if sl is not None and (g is None or g.numel() < sl[2]):
+            if g is None or g.numel() < end:
                 raise ValueError(f"tensor {k} is copied on rank {rank} but its gradient is missing or short")
         _check(lib().ve_dbuffer_copy_in(self._h, int(rank), C.c_void_p(grad_table.table.data_ptr()),
                                         C.c_void_p(bucket.data_ptr()), _stream_handle(stream)))
@@ -301,10 +314,11 @@ class StateTable:
             gt = st["grad_table"]
             if len(gt.grads) != plan.n_tensors:
                 raise ValueError("grad table length != number of tensors in the plan")
-            for k in range(plan.n_tensors):
-                if plan.slice(rank, k) is not None and gt.grads[k] is None:
+            for k, _end in plan.pieces(rank):
+                if gt.grads[k] is None:
                     raise ValueError(f"tensor {k} has a piece on rank {rank} but no gradient")
-                if gt.grads[k] is not None and gt.grads[k].numel() < self._numel(plan, k):
+            for k, numel in plan.pieces(-1):  # the whole bucket holds every tensor whole
+                if gt.grads[k] is not None and gt.grads[k].numel() < numel:
                     raise ValueError(f"gradient {k} is smaller than the tensor")
             _require_buffer(st["grad_shard"], S, 2, "grad_shard")
             _require_buffer(st["master"], S, 4, "master")
@@ -317,11 +331,6 @@ class StateTable:
             self.keep.append(st)
         self.table = torch.tensor(rows, dtype=torch.int64, device=device).reshape(-1)
         self.n = len(rows)
-
-    @staticmethod
-    def _numel(plan, k):
-        off, lo, hi = plan.slice(-1, k)
-        return hi
 
     def __len__(self):
         return self.n
@@ -354,10 +363,9 @@ class GroupTable:
             if gt is not None:
                 if len(gt.grads) != plan.n_tensors:
                     raise ValueError("grad table length != number of tensors in the plan")
-                for k in range(plan.n_tensors):
-                    sl = plan.slice(rank, k)
+                for k, end in plan.pieces(rank):
                     g = gt.grads[k]
-                    if sl is not None and (g is None or g.numel() < sl[2]):
+                    if g is None or g.numel() < end:
                         raise ValueError(f"tensor {k} has elements in the range but its gradient is "
                                          "missing or short")
             rows.append([b.data_ptr(), 0 if gt is None else gt.table.data_ptr()])

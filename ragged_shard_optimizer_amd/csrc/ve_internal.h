@@ -34,8 +34,11 @@ constexpr int64_t kWgMaxGroups = 1024 * 16;
 // without a dependent chain of memory loads; a class with more segments is
 // launched in slices of at most this many.
 constexpr int kInlineSegs = 16;
-// Elements per tile of the run copier (copy-in and padding fill).
-constexpr int kRunTile = 4096;
+// Elements per tile of the run copier (copy-in, padding fill, group ops).
+#ifndef VE_RUN_TILE
+#define VE_RUN_TILE 4096
+#endif
+constexpr int kRunTile = VE_RUN_TILE;
 // A dispatch's grid is at most 2^32 - 1 work-items per dimension.
 constexpr int64_t kMaxGridItems = 0xFFFFFFFFll;
 constexpr int64_t kMaxRunTiles = kMaxGridItems / 256;  // run kernels: 256 threads per tile
