@@ -226,7 +226,10 @@ ve_status ve_plan_layout(ve_tensor_spec* specs, int32_t n_tensors, int32_t fsdp_
  *   G, out: device, bf16 rows x cols row-major (out may not alias G or the
  *   workspace).  steps in [0, 64] (0: out = bf16(G / (|G|_F + eps))).
  *   workspace: device, 256-byte aligned, at least ve_muon_workspace_bytes
- *   bytes, owned by the caller; its contents are scratch.
+ *   bytes, owned by the caller; its contents are scratch (two copies of X
+ *   and of X^T, A, B, and for matrices of more than 256 tiles of 256 x 256
+ *   a further 64 MiB for the fp32 K slices of products whose last round of
+ *   tiles is split along the contraction).
  * Errors: NULL pointers, a non-positive shape, steps outside [0, 64], eps
  * negative or not finite, a short or misaligned workspace:
  * VE_ERR_INVALID_ARG; a matrix beyond one launch: VE_ERR_UNSUPPORTED;

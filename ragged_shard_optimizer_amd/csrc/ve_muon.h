@@ -9,6 +9,8 @@
 
 namespace ve {
 
+constexpr int kCUs = 256;  // MI355X compute units
+
 // Product C = alpha * P Q^T + beta * D on the MFMA units (ve_muon.hip).  P is
 // M x K, Q is N x K, D / C are M x N and CT is N x M, all bf16 row-major
 // with the given leading dimensions; D, C or CT may be null (C or CT must
@@ -26,7 +28,16 @@ struct GemmArgs {
     int32_t tiles_n;                 // set by the launcher
     bool vec_p, vec_q, vec_d, vec_c, vec_ct;  // rows allow 16-byte accesses
     bool xcd_remap;                  // set by the launcher: XCD-aware tile order
+    // Tail split (set by the launcher): a launch covers logical tiles from
+    // tile_base; with ksplit > 1 each tile's K steps are cut into ksplit
+    // slices whose fp32 accumulators go to `partial` (the caller's scratch,
+    // kSplitPartialBytes; null: never split).
+    int32_t tiles_total, tile_base, ksplit;
+    float* partial;
 };
+// Scratch for the split tail of a product: at most one launch's worth of
+// 256 x 256 fp32 tiles, one per CU.
+constexpr int64_t kSplitPartialBytes = int64_t(256) * 256 * 256 * 4;
 hipError_t launch_gemm_nt(GemmArgs g, hipStream_t s);
 int64_t gemm_tiles(int64_t M, int64_t N);
 // Frobenius norm: fp64 partial sums (norm_blocks() of them), then the fp32 scale.

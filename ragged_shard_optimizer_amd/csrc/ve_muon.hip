@@ -37,6 +37,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "ve_device.h"
 #include "ve_muon.h"
 
@@ -73,7 +75,6 @@ struct Cfg {
     X(2, 256, 256, 64, 128, 64)
 
 constexpr int kNormBlocks = 1024;    // partial sums of the Frobenius norm
-constexpr int kCUs = 256;           // MI355X compute units
 
 __device__ __forceinline__ uint16_t to_bf16(float x) { return (uint16_t)pack_bf16x2(x, 0.f); }
 __device__ __forceinline__ float from_bf16(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -108,29 +109,46 @@ __device__ __forceinline__ u32x4 load8(const uint16_t* base, int64_t ld, int64_t
 // tile rows column by column, so the operand panels a slice touches are few
 // and stay in its L2.  A symmetric product launches only the tiles on or
 // above the diagonal, row by row, so every slice carries the same work.
-__device__ __forceinline__ void tile_of(const GemmArgs& g, int& ti, int& tj) {
-    const int nb = gridDim.x;
-    int bid = blockIdx.x;
-    if (g.xcd_remap && nb % 8 == 0) bid = (bid % 8) * (nb / 8) + bid / 8;
+// Tile (ti, tj) of logical tile index t: the upper triangle row by row for
+// symmetric products, else groups of 8 tile rows walked column by column.
+__device__ __forceinline__ void tile_at(const GemmArgs& g, int t, int& ti, int& tj) {
     if (g.symmetric) {
-        // row t of the upper triangle holds tiles_n - t tiles
-        int t = 0, rem = bid;
-        while (rem >= g.tiles_n - t) {
-            rem -= g.tiles_n - t;
-            ++t;
+        // row r of the upper triangle holds tiles_n - r tiles
+        int r = 0, rem = t;
+        while (rem >= g.tiles_n - r) {
+            rem -= g.tiles_n - r;
+            ++r;
         }
-        ti = t;
-        tj = t + rem;
+        ti = r;
+        tj = r + rem;
         return;
     }
     constexpr int kGroup = 8;
-    const int tiles_m = nb / g.tiles_n;
+    const int tiles_m = g.tiles_total / g.tiles_n;
     const int per_group = kGroup * g.tiles_n;
-    const int first = (bid / per_group) * kGroup;
+    const int first = (t / per_group) * kGroup;
     const int gm = min(tiles_m - first, kGroup);
-    const int r = bid % per_group;
+    const int r = t % per_group;
     ti = first + r % gm;
     tj = r / gm;
+}
+
+// This workgroup's tile and K slice.  Launches cover logical tiles
+// [tile_base, tile_base + gridDim.x / ksplit); with ksplit > 1, consecutive
+// workgroups take the K slices of one tile.  Whole-tile launches whose size
+// is a multiple of 8 spread consecutive tiles over the 8 XCDs' L2s in
+// blocks (block b -> (b mod 8) * nb/8 + b / 8).
+__device__ __forceinline__ int tile_of(const GemmArgs& g, int& ti, int& tj) {
+    const int nb = gridDim.x;
+    int bid = blockIdx.x, split = 0;
+    if (g.ksplit > 1) {
+        split = bid % g.ksplit;
+        bid /= g.ksplit;
+    } else if (g.xcd_remap && nb % 8 == 0) {
+        bid = (bid % 8) * (nb / 8) + bid / 8;
+    }
+    tile_at(g, g.tile_base + bid, ti, tj);
+    return split;
 }
 
 // 8 bf16 <-> a 16-byte vector
@@ -338,6 +356,13 @@ template <int WM_, int WN_, int BK_, int STAGES_>
 struct DmaCfg {
     static constexpr int BM = 256, BN = 256, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_;
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, WAVES = WAVES_M * WAVES_N;
+#ifndef VE_EARLY_BARRIER
+#define VE_EARLY_BARRIER 1
+#endif
+    // The next step's barrier and first fragment reads are placed inside
+    // the last sub-step's MFMAs, so the read latency after each barrier is
+    // covered by MFMAs instead of stalling every wave at the step boundary.
+    static constexpr bool EARLY_BARRIER = VE_EARLY_BARRIER != 0;
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int TM = WM / 32, TN = WN / 32;
     static constexpr int CHUNKS = BK / 8;                      // 16-byte chunks per operand row
@@ -362,15 +387,26 @@ struct DmaCfg {
     X(9, 128, 64, 64, 2)
 
 template <class CF, bool HAS_D, bool HAS_C, bool HAS_CT>
+__device__ __forceinline__ void dma_epilogue(const GemmArgs& g, f32x16 (&acc)[CF::TM][CF::TN], int ti, int tj,
+                                             unsigned char* smem);
+
+// Raw accumulators of one (tile, K slice) work item, in fragment order
+// [wave][a][b][r][lane] (64 consecutive floats per store), at item
+// (tile - tile_base) * ksplit + split of the fp32 partial buffer.
+template <class CF>
+__device__ __forceinline__ float* partial_at(const GemmArgs& g, int item) {
+    return g.partial + (int64_t)item * (CF::BM * CF::BN);
+}
+
+template <class CF, bool HAS_D, bool HAS_C, bool HAS_CT>
 __global__ void __launch_bounds__(CF::THREADS) k_gemm_nt_dma(GemmArgs g) {
     constexpr int BM = CF::BM, BN = CF::BN, BK = CF::BK, WM = CF::WM, WN = CF::WN, TM = CF::TM, TN = CF::TN;
-    constexpr int NT = CF::THREADS, LDC = CF::LDC, S = CF::STAGES, SE = CF::STAGE_ELEMS;
+    constexpr int S = CF::STAGES, SE = CF::STAGE_ELEMS;
     int ti, tj;
-    tile_of(g, ti, tj);
+    const int split = tile_of(g, ti, tj);
     const int64_t i0 = (int64_t)ti * BM, j0 = (int64_t)tj * BN;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[CF::SMEM];
     uint16_t* ops = (uint16_t*)smem;                  // stage s: P rows [BM * BK], then Q rows [BN * BK]
-    float* sC = (float*)smem;                         // [PASS_ROWS][LDC]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave / CF::WAVES_N, wc = wave % CF::WAVES_N;
 
@@ -381,6 +417,15 @@ __global__ void __launch_bounds__(CF::THREADS) k_gemm_nt_dma(GemmArgs g) {
         for (int b = 0; b < TN; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+    // K steps of this work item: all of them, or slice `split` of ksplit
+    const int64_t nk_all = g.K / BK;
+    int64_t kbeg = 0, nk = nk_all;
+    if (g.ksplit > 1) {
+        const int64_t per = (nk_all + g.ksplit - 1) / g.ksplit;
+        kbeg = min((int64_t)split * per, nk_all);
+        nk = min(per, nk_all - kbeg);
+    }
 
     // DMA: instruction q of wave w fills rows [(WAVES q + w) R, +R) of an
     // operand (R = rows per KiB); lane l writes slot l % CHUNKS of row
@@ -400,56 +445,94 @@ __global__ void __launch_bounds__(CF::THREADS) k_gemm_nt_dma(GemmArgs g) {
     };
     auto dma_step = [&](int64_t kt) {
         uint16_t* st = ops + (int)(kt % S) * SE;
-        dma_op(g.P, g.ldp, g.M, i0, st, kt * BK);
-        dma_op(g.Q, g.ldq, g.N, j0, st + BM * BK, kt * BK);
+        dma_op(g.P, g.ldp, g.M, i0, st, (kbeg + kt) * BK);
+        dma_op(g.Q, g.ldq, g.N, j0, st + BM * BK, (kbeg + kt) * BK);
     };
 
-    const int64_t nk = g.K / BK;
     // prologue: stages 0 .. S-2 in flight
 #pragma unroll
     for (int p = 0; p < S - 1; ++p)
         if (p < nk) dma_step(p);
     const int frow = lane & 31, fhalf = lane >> 5;
     const int fs = CF::swz(lane & 15);                // rows t*32 + frow share frow's swizzle
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        // step kt's stage is complete when at most the S-2 younger stages are outstanding
+    // fragments double-buffered over the 16-deep sub-steps: the reads for
+    // sub-step kk+1 are issued before the MFMAs of kk, so the LDS latency
+    // hides behind TM*TN MFMAs
+    bf16x8 fa[2][TM], fb[2][TN];
+    auto frag = [&](int buf, int kk, int64_t kt) {
+        const uint16_t* st = ops + (int)(kt % S) * SE;
+        const uint16_t* cp = st + (wr * WM + frow) * BK;
+        const uint16_t* cq = st + BM * BK + (wc * WN + frow) * BK;
+        const int slot = ((2 * kk + fhalf) ^ fs) * 8;
+#pragma unroll
+        for (int t = 0; t < TM; ++t) fa[buf][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)&cp[t * 32 * BK + slot]);
+#pragma unroll
+        for (int t = 0; t < TN; ++t) fb[buf][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)&cq[t * 32 * BK + slot]);
+    };
+    // step kt's stage is complete when at most the S-2 younger stages are
+    // outstanding; then every wave has its own loads of it complete, and a
+    // bare barrier (no memory fence, which would wait for the younger stages
+    // too) with compiler-level clobbers, so no LDS access moves across it
+    auto stage_ready = [&](int64_t kt) {
         if (kt + S - 2 < nk) {
             constexpr int younger = (S - 2) * 2 * CF::DMA_PER_OP;
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(younger));
         } else {
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         }
-        // every wave has its own loads of this stage complete; a bare barrier
-        // (no memory fence, which would wait for the younger stages too) and
-        // compiler-level clobbers so no LDS access moves across it
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (kt + S - 1 < nk) dma_step(kt + S - 1);     // into the stage consumed at step kt - 1
-        const uint16_t* st = ops + (int)(kt % S) * SE;
-        const uint16_t* cp = st + (wr * WM + frow) * BK;
-        const uint16_t* cq = st + BM * BK + (wc * WN + frow) * BK;
-        // fragments double-buffered over the 16-deep sub-steps: the reads for
-        // sub-step kk+1 are issued before the MFMAs of kk, so the LDS latency
-        // hides behind TM*TN MFMAs
-        bf16x8 fa[2][TM], fb[2][TN];
-        auto frag = [&](int buf, int kk) {
-            const int slot = ((2 * kk + fhalf) ^ fs) * 8;
-#pragma unroll
-            for (int t = 0; t < TM; ++t) fa[buf][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)&cp[t * 32 * BK + slot]);
-#pragma unroll
-            for (int t = 0; t < TN; ++t) fb[buf][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)&cq[t * 32 * BK + slot]);
-        };
-        frag(0, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, TM + TN, 0);
+    };
+    auto mfma = [&](int buf, int a, int b) {
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][a], fb[buf][b], acc[a][b], 0, 0, 0);
+    };
+    if constexpr (CF::EARLY_BARRIER) {
+        stage_ready(0);
+        frag(0, 0, 0);
+    }
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        if constexpr (!CF::EARLY_BARRIER) {
+            stage_ready(kt);
+            if (kt + S - 1 < nk) dma_step(kt + S - 1);  // into the stage consumed at step kt - 1
+            frag(0, 0, kt);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, TM + TN, 0);
+        } else {
+            // the barrier that frees this stage (every wave's reads of step
+            // kt - 1 complete) was passed inside step kt - 1
+            if (kt + S - 1 < nk) dma_step(kt + S - 1);
+        }
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
-            if (kk + 1 < BK / 16) frag((kk + 1) & 1, kk + 1);
+            if (kk + 1 < BK / 16) frag((kk + 1) & 1, kk + 1, kt);
+            if constexpr (CF::EARLY_BARRIER) {
+                if (kk + 1 == BK / 16) {
+                    // last sub-step: every read of this step's stage is
+                    // complete (waited before these MFMAs).  A few MFMAs,
+                    // then the next step's barrier and its first fragment
+                    // reads, each followed by one MFMA.  On the last step
+                    // the reads fetch an unused stage.
+                    constexpr int post = TM + TN, pre = TM * TN - post;
+                    static_assert(pre >= 1, "early-barrier shape");
+#pragma unroll
+                    for (int i = 0; i < pre; ++i) mfma(kk & 1, i / TN, i % TN);
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, pre, 0);
+                    stage_ready(kt + 1);
+                    frag(0, 0, kt + 1);
+#pragma unroll
+                    for (int i = pre; i < TM * TN; ++i) mfma(kk & 1, i / TN, i % TN);
+#pragma unroll
+                    for (int i = 0; i < post; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    }
+                    continue;
+                }
+            }
 #pragma unroll
             for (int a = 0; a < TM; ++a)
 #pragma unroll
-                for (int b = 0; b < TN; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][a], fb[kk & 1][b], acc[a][b], 0, 0, 0);
+                for (int b = 0; b < TN; ++b) mfma(kk & 1, a, b);
             // schedule: one MFMA, then one read of the next sub-step, ...
             if (kk + 1 < BK / 16) {
 #pragma unroll
@@ -468,9 +551,58 @@ __global__ void __launch_bounds__(CF::THREADS) k_gemm_nt_dma(GemmArgs g) {
         }
     }
     __syncthreads();
+    if (g.ksplit > 1) {
+        // K slice of a split tile: the raw accumulators, summed later
+        float* out = partial_at<CF>(g, (int)blockIdx.x) + (int64_t)wave * (TM * TN * 16 * 64) + lane;
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int b = 0; b < TN; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) out[((a * TN + b) * 16 + r) * 64] = acc[a][b][r];
+        return;
+    }
+    dma_epilogue<CF, HAS_D, HAS_C, HAS_CT>(g, acc, ti, tj, smem);
+}
 
-    // epilogue in passes of 64 tile rows, the same three phases as the
-    // register-staged kernel
+// The sum of a split tile's K slices (in slice order), then the epilogue.
+template <class CF, bool HAS_D, bool HAS_C, bool HAS_CT>
+__global__ void __launch_bounds__(CF::THREADS) k_gemm_split_reduce(GemmArgs g) {
+    constexpr int TM = CF::TM, TN = CF::TN;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[CF::SMEM];
+    int ti, tj;
+    tile_at(g, g.tile_base + (int)blockIdx.x, ti, tj);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+    for (int sp = 0; sp < g.ksplit; ++sp) {
+        const float* in = partial_at<CF>(g, (int)blockIdx.x * g.ksplit + sp) + (int64_t)wave * (TM * TN * 16 * 64) + lane;
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int b = 0; b < TN; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[a][b][r] += in[((a * TN + b) * 16 + r) * 64];
+    }
+    dma_epilogue<CF, HAS_D, HAS_C, HAS_CT>(g, acc, ti, tj, smem);
+}
+
+// Epilogue of the direct-to-LDS kernels: in passes of 64 tile rows, the
+// same three phases as the register-staged kernel.
+template <class CF, bool HAS_D, bool HAS_C, bool HAS_CT>
+__device__ __forceinline__ void dma_epilogue(const GemmArgs& g, f32x16 (&acc)[CF::TM][CF::TN], int ti, int tj,
+                                             unsigned char* smem) {
+    constexpr int BM = CF::BM, BN = CF::BN, WM = CF::WM, WN = CF::WN, TN = CF::TN;
+    constexpr int NT = CF::THREADS, LDC = CF::LDC;
+    const int64_t i0 = (int64_t)ti * BM, j0 = (int64_t)tj * BN;
+    float* sC = (float*)smem;                         // [PASS_ROWS][LDC]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave / CF::WAVES_N, wc = wave % CF::WAVES_N;
     const bool mirror = g.symmetric && ti < tj;
     const bool transpose = HAS_CT || mirror;
     uint16_t* T = HAS_CT ? g.CT : g.C;
@@ -629,8 +761,11 @@ int64_t launch_tiles(const GemmArgs& g, int bm) {
 }
 
 template <class CF, bool HAS_D, bool HAS_C, bool HAS_CT>
-hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s) {
+hipError_t launch_gemm_t(GemmArgs g, hipStream_t s) {
     const int64_t tiles = launch_tiles(g, CF::BM);
+    g.tiles_total = (int32_t)tiles;
+    g.tile_base = 0;
+    g.ksplit = 1;
     if (g.vec_p && g.vec_q && g.K % 8 == 0)
         hipLaunchKernelGGL((k_gemm_nt<CF, HAS_D, HAS_C, HAS_CT, true>), dim3((unsigned)tiles), dim3(CF::THREADS), 0, s, g);
     else
@@ -639,10 +774,45 @@ hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Tail split: when the tiles fill some whole rounds of the CUs plus a short
+// last round, the last round's tiles are cut along K into slices that fill
+// one round (each slice writes fp32 accumulators), and a reduce launch sums
+// the slices in order and runs the epilogue.  Worth it only for a short
+// tail over long contractions.
+// VE_GEMM_SPLIT=0 turns it off (read at every launch).
+inline int tail_split(int64_t tiles, int64_t nk, bool has_partial, int64_t& full) {
+    full = tiles;
+    const char* e = getenv("VE_GEMM_SPLIT");
+    if (e && atoi(e) == 0) return 1;
+    full = tiles / kCUs * kCUs;
+    const int64_t tail = tiles - full;
+    if (!has_partial || full == 0 || tail == 0 || tail * 4 > kCUs || nk < 32) return 1;
+    return (int)std::min<int64_t>(std::min<int64_t>(kCUs / tail, nk / 8), 32);
+}
+
 template <class CF, bool HAS_D, bool HAS_C, bool HAS_CT>
-hipError_t launch_dma_t(const GemmArgs& g, hipStream_t s) {
+hipError_t launch_dma_t(GemmArgs g, hipStream_t s) {
     const int64_t tiles = launch_tiles(g, CF::BM);
-    hipLaunchKernelGGL((k_gemm_nt_dma<CF, HAS_D, HAS_C, HAS_CT>), dim3((unsigned)tiles), dim3(CF::THREADS), 0, s, g);
+    g.tiles_total = (int32_t)tiles;
+    g.tile_base = 0;
+    g.ksplit = 1;
+    int64_t full = tiles;
+    const int ks = tail_split(tiles, g.K / CF::BK, g.partial != nullptr, full);
+    if (ks <= 1) {
+        hipLaunchKernelGGL((k_gemm_nt_dma<CF, HAS_D, HAS_C, HAS_CT>), dim3((unsigned)tiles), dim3(CF::THREADS), 0, s,
+                           g);
+        return hipGetLastError();
+    }
+    const int64_t tail = tiles - full;
+    static_assert(int64_t(CF::BM) * CF::BN * 4 * kCUs <= kSplitPartialBytes, "split scratch");
+    hipLaunchKernelGGL((k_gemm_nt_dma<CF, HAS_D, HAS_C, HAS_CT>), dim3((unsigned)full), dim3(CF::THREADS), 0, s, g);
+    GemmArgs t = g;
+    t.tile_base = (int32_t)full;
+    t.ksplit = ks;
+    hipLaunchKernelGGL((k_gemm_nt_dma<CF, HAS_D, HAS_C, HAS_CT>), dim3((unsigned)(tail * ks)), dim3(CF::THREADS), 0,
+                       s, t);
+    hipLaunchKernelGGL((k_gemm_split_reduce<CF, HAS_D, HAS_C, HAS_CT>), dim3((unsigned)tail), dim3(CF::THREADS), 0,
+                       s, t);
     return hipGetLastError();
 }
 

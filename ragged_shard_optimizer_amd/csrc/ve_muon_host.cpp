@@ -28,7 +28,7 @@ constexpr float kNsA = 3.4445f, kNsB = -4.7750f, kNsC = 2.0315f;
 int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 
 struct MuonLayout {
-    int64_t partial, scale, x[2], xt[2], a, b, total;
+    int64_t partial, scale, x[2], xt[2], a, b, split, total;
 };
 
 // Workspace carve-up; false if the sizes overflow.
@@ -42,6 +42,9 @@ bool muon_layout(int64_t rows, int64_t cols, MuonLayout& L) {
     for (int i = 0; i < 2; ++i) { L.x[i] = off; off += mn; L.xt[i] = off; off += mn; }
     L.a = off; off += mm;
     L.b = off; off += mm;
+    // scratch for split tails, needed once a product has more tiles than CUs
+    L.split = -1;
+    if (((m + 255) / 256) * ((n + 255) / 256) > kCUs) { L.split = off; off += kSplitPartialBytes; }
     L.total = off;
     return true;
 }
@@ -116,6 +119,7 @@ ve_status ve_muon_newton_schulz(const uint16_t* G, uint16_t* out, int64_t rows, 
     uint16_t* XT[2] = {(uint16_t*)(w + L.xt[0]), (uint16_t*)(w + L.xt[1])};
     uint16_t* A = (uint16_t*)(w + L.a);
     uint16_t* B = (uint16_t*)(w + L.b);
+    float* split = L.split >= 0 ? (float*)(w + L.split) : nullptr;
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     ve_status st;
@@ -132,17 +136,17 @@ ve_status ve_muon_newton_schulz(const uint16_t* G, uint16_t* out, int64_t rows, 
         GemmArgs g{};
         // A = X X^T
         g.P = X[cur]; g.ldp = n; g.Q = X[cur]; g.ldq = n; g.C = A; g.ldc = m;
-        g.M = m; g.N = m; g.K = n; g.alpha = 1.f; g.beta = 0.f; g.symmetric = 1;
+        g.M = m; g.N = m; g.K = n; g.alpha = 1.f; g.beta = 0.f; g.symmetric = 1; g.partial = split;
         if ((st = gemm(g, s, "X X^T")) != VE_OK) return st;
         // B = c A A + b A
         g = GemmArgs{};
         g.P = A; g.ldp = m; g.Q = A; g.ldq = m; g.D = A; g.ldd = m; g.C = B; g.ldc = m;
-        g.M = m; g.N = m; g.K = m; g.alpha = kNsC; g.beta = kNsB; g.symmetric = 1;
+        g.M = m; g.N = m; g.K = m; g.alpha = kNsC; g.beta = kNsB; g.symmetric = 1; g.partial = split;
         if ((st = gemm(g, s, "A A")) != VE_OK) return st;
         // X' = B X + a X, with X = (X^T)^T as the second operand
         g = GemmArgs{};
         g.P = B; g.ldp = m; g.Q = XT[cur]; g.ldq = m; g.D = X[cur]; g.ldd = n;
-        g.M = m; g.N = n; g.K = m; g.alpha = 1.f; g.beta = kNsA; g.symmetric = 0;
+        g.M = m; g.N = n; g.K = m; g.alpha = 1.f; g.beta = kNsA; g.symmetric = 0; g.partial = split;
         if (last) {
             if (wide) { g.C = out; g.ldc = n; }
             else { g.CT = out; g.ldct = m; }

@@ -194,6 +194,42 @@ def test_five_steps(shape):
     assert np.abs(s_got - s_ex).max() <= 0.05
 
 
+# Split tails: once a product has more 256 x 256 tiles than the GPU has CUs
+# and the last round is short, that round's tiles are cut along K, their fp32
+# slices summed in a second kernel.  At 5760 x 5760 all three products of a
+# step split (symmetric: 276 tiles, 20 in the tail; B X: 529 tiles, 17 in the
+# tail; 11 slices of 90 K steps, the last one empty).
+SPLIT_SHAPE = (5760, 5760)
+
+
+def test_split_tail_one_step_within_propagated_bound():
+    Gb = _bf16_host(SPLIT_SHAPE, 15)
+    G = muon.bf16_bits_to_f64(Gb)
+    _say(f"[gpu] newton-schulz steps=1 {SPLIT_SHAPE} (split tails)")
+    got = _run_ns(Gb, 1)
+    trace = []
+    want = muon.newton_schulz(G, steps=1, trace=trace)
+    X0 = muon.newton_schulz(G, steps=0)
+    (A, B, X1), = trace[0]
+    dX0 = U * np.abs(X0) + ulp_bf16(X0)
+    bound = ns_one_step_bound(X0, A, B, X1, dX0)
+    bad = np.abs(got - want) > bound
+    assert not bad.any(), (int(bad.sum()), float(np.abs(got - want).max()))
+
+
+def test_split_tail_matches_unsplit(monkeypatch):
+    """The split path only reorders fp32 additions: two steps with and
+    without it agree to within a few bf16 roundings."""
+    Gb = _bf16_host(SPLIT_SHAPE, 16)
+    _say(f"[gpu] newton-schulz steps=2 {SPLIT_SHAPE}, split and unsplit")
+    a = _run_ns(Gb, 2)
+    monkeypatch.setenv("VE_GEMM_SPLIT", "0")
+    b = _run_ns(Gb, 2)
+    assert np.isfinite(a).all() and np.isfinite(b).all()
+    assert np.linalg.norm(a - b) <= 1e-3 * np.linalg.norm(b)
+    assert np.abs(a - b).max() <= 2.0 ** -6 * np.abs(b).max()
+
+
 def test_repeat_calls_are_deterministic():
     import torch
     ve = _ve()
