@@ -150,10 +150,10 @@ def time_group_ops(torch, ve, plan, rank, states, lay, valid, steps, warmup, tra
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
-def time_muon(torch, ve, dev, rows=8192, cols=28672, steps=3, warmup=1):
-    """Muon's Newton-Schulz iteration (5 steps) on one gathered matrix of the
-    LLaMA-3-70B MLP shape, HIP events on the launch stream; flops counted the
-    minimal way (symmetric products at half cost)."""
+def time_muon(torch, ve, dev, rows=8192, cols=28672, steps=3, warmup=1, name="LLaMA-3-70B MLP"):
+    """Muon's Newton-Schulz iteration (5 steps) on one gathered matrix (by
+    default of the LLaMA-3-70B MLP shape), HIP events on the launch stream;
+    flops counted the minimal way (symmetric products at half cost)."""
     from oracle import muon
     stream = torch.cuda.current_stream()
     g = torch.Generator(device=dev)
@@ -200,7 +200,7 @@ def time_muon(torch, ve, dev, rows=8192, cols=28672, steps=3, warmup=1):
     log(f"[bench] torch addmm iteration for comparison: {tms:.3f} ms")
     del X
     torch.cuda.empty_cache()
-    return {"workload": f"Muon Newton-Schulz, 5 steps, one {rows}x{cols} bf16 matrix (LLaMA-3-70B MLP)",
+    return {"workload": f"Muon Newton-Schulz, 5 steps, one {rows}x{cols} bf16 matrix ({name})",
             "bound": "mfma", "ms": round(ms, 4), "flops": flops, "achieved": round(tf, 1),
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
             "torch_addmm_ms": round(tms, 4)}
@@ -363,6 +363,9 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_muon:
         out["muon"] = time_muon(torch, ve, dev)
+        # a matrix far below one round of 256 x 256 tiles: a routed expert
+        out["muon_expert"] = time_muon(torch, ve, dev, rows=2048, cols=7168, steps=20, warmup=3,
+                                       name="DeepSeek-V3 routed expert")
     if not args.no_planner:
         out["planner"] = time_planner(ve)
     if args.copy_gib > 0:

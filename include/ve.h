@@ -227,8 +227,8 @@ ve_status ve_plan_layout(ve_tensor_spec* specs, int32_t n_tensors, int32_t fsdp_
  *   workspace).  steps in [0, 64] (0: out = bf16(G / (|G|_F + eps))).
  *   workspace: device, 256-byte aligned, at least ve_muon_workspace_bytes
  *   bytes, owned by the caller; its contents are scratch (two copies of X
- *   and of X^T, A, B, and for matrices of more than 256 tiles of 256 x 256
- *   a further 64 MiB for the fp32 K slices of products whose last round of
+ *   and of X^T, A, B, and when the longer side is at least 1024 a further
+ *   64 MiB for the fp32 K slices of products whose last (or only) round of
  *   tiles is split along the contraction).
  * Errors: NULL pointers, a non-positive shape, steps outside [0, 64], eps
  * negative or not finite, a short or misaligned workspace:

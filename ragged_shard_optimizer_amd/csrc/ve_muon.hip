@@ -565,7 +565,22 @@ __global__ void __launch_bounds__(CF::THREADS) k_gemm_nt_dma(GemmArgs g) {
     dma_epilogue<CF, HAS_D, HAS_C, HAS_CT>(g, acc, ti, tj, smem);
 }
 
-// The sum of a split tile's K slices (in slice order), then the epilogue.
+// Sums of split tiles' K slices, in slice order, into each tile's first
+// slice: workgroup b adds up 1024 consecutive floats of tile b / per_tile.
+constexpr int kSumChunk = 1024;
+__global__ void __launch_bounds__(256) k_split_sum(float* partial, int tile_floats, int ksplit) {
+    const int per_tile = tile_floats / kSumChunk;
+    const int tile = blockIdx.x / per_tile, chunk = blockIdx.x % per_tile;
+    float* base = partial + (int64_t)tile * ksplit * tile_floats + chunk * kSumChunk + threadIdx.x * 4;
+    f32x4 acc = *(const f32x4*)base;
+    for (int sp = 1; sp < ksplit; ++sp) {
+        const f32x4 v = *(const f32x4*)(base + (int64_t)sp * tile_floats);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    *(f32x4*)base = acc;
+}
+
+// A split tile's summed accumulators (its first slice), then the epilogue.
 template <class CF, bool HAS_D, bool HAS_C, bool HAS_CT>
 __global__ void __launch_bounds__(CF::THREADS) k_gemm_split_reduce(GemmArgs g) {
     constexpr int TM = CF::TM, TN = CF::TN;
@@ -580,15 +595,13 @@ __global__ void __launch_bounds__(CF::THREADS) k_gemm_split_reduce(GemmArgs g) {
         for (int b = 0; b < TN; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-    for (int sp = 0; sp < g.ksplit; ++sp) {
-        const float* in = partial_at<CF>(g, (int)blockIdx.x * g.ksplit + sp) + (int64_t)wave * (TM * TN * 16 * 64) + lane;
+    const float* in = partial_at<CF>(g, (int)blockIdx.x * g.ksplit) + (int64_t)wave * (TM * TN * 16 * 64) + lane;
 #pragma unroll
-        for (int a = 0; a < TM; ++a)
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
-            for (int b = 0; b < TN; ++b)
+        for (int b = 0; b < TN; ++b)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[a][b][r] += in[((a * TN + b) * 16 + r) * 64];
-    }
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = in[((a * TN + b) * 16 + r) * 64];
     dma_epilogue<CF, HAS_D, HAS_C, HAS_CT>(g, acc, ti, tj, smem);
 }
 
@@ -775,19 +788,22 @@ hipError_t launch_gemm_t(GemmArgs g, hipStream_t s) {
 }
 
 // Tail split: when the tiles fill some whole rounds of the CUs plus a short
-// last round, the last round's tiles are cut along K into slices that fill
-// one round (each slice writes fp32 accumulators), and a reduce launch sums
-// the slices in order and runs the epilogue.  Worth it only for a short
-// tail over long contractions.
-// VE_GEMM_SPLIT=0 turns it off (read at every launch).
+// last round (at most a quarter of the CUs), or fewer tiles than CUs in all,
+// the last round's tiles are cut along K into slices that fill one round
+// (each slice writes fp32 accumulators), and a reduce launch sums the slices
+// in order and runs the epilogue.  Only over long contractions (at least 8
+// steps per slice).  Returns the slice count (1: no split) and the number of
+// tiles launched whole.  VE_GEMM_SPLIT=0 turns it off (read at every launch).
 inline int tail_split(int64_t tiles, int64_t nk, bool has_partial, int64_t& full) {
     full = tiles;
     const char* e = getenv("VE_GEMM_SPLIT");
-    if (e && atoi(e) == 0) return 1;
-    full = tiles / kCUs * kCUs;
-    const int64_t tail = tiles - full;
-    if (!has_partial || full == 0 || tail == 0 || tail * 4 > kCUs || nk < 32) return 1;
-    return (int)std::min<int64_t>(std::min<int64_t>(kCUs / tail, nk / 8), 32);
+    if (!has_partial || (e && atoi(e) == 0) || nk < 16) return 1;
+    const int64_t whole = tiles / kCUs * kCUs, tail = tiles - whole;
+    if (tail == 0 || (whole > 0 && tail * 4 > kCUs)) return 1;
+    const int64_t ks = std::min<int64_t>(std::min<int64_t>(kCUs / tail, nk / 8), 32);
+    if (ks < 2) return 1;
+    full = whole;
+    return (int)ks;
 }
 
 template <class CF, bool HAS_D, bool HAS_C, bool HAS_CT>
@@ -805,12 +821,18 @@ hipError_t launch_dma_t(GemmArgs g, hipStream_t s) {
     }
     const int64_t tail = tiles - full;
     static_assert(int64_t(CF::BM) * CF::BN * 4 * kCUs <= kSplitPartialBytes, "split scratch");
-    hipLaunchKernelGGL((k_gemm_nt_dma<CF, HAS_D, HAS_C, HAS_CT>), dim3((unsigned)full), dim3(CF::THREADS), 0, s, g);
+    if (full > 0)  // whole rounds first (none when the product is split whole)
+        hipLaunchKernelGGL((k_gemm_nt_dma<CF, HAS_D, HAS_C, HAS_CT>), dim3((unsigned)full), dim3(CF::THREADS), 0, s,
+                           g);
     GemmArgs t = g;
     t.tile_base = (int32_t)full;
     t.ksplit = ks;
     hipLaunchKernelGGL((k_gemm_nt_dma<CF, HAS_D, HAS_C, HAS_CT>), dim3((unsigned)(tail * ks)), dim3(CF::THREADS), 0,
                        s, t);
+    constexpr int kTileFloats = CF::BM * CF::BN;
+    static_assert(kTileFloats % kSumChunk == 0 && kSumChunk == 256 * 4, "slice sum shape");
+    hipLaunchKernelGGL(k_split_sum, dim3((unsigned)(tail * (kTileFloats / kSumChunk))), dim3(256), 0, s, g.partial,
+                       kTileFloats, ks);
     hipLaunchKernelGGL((k_gemm_split_reduce<CF, HAS_D, HAS_C, HAS_CT>), dim3((unsigned)tail), dim3(CF::THREADS), 0,
                        s, t);
     return hipGetLastError();
@@ -859,11 +881,28 @@ int gemm_cfg_override() {
 // multiple of 64, 16-byte operand rows) and the product has at least two
 // rounds of 256 x 256 tiles; else the register-staged 256 x 256 or 128 x 128
 // kernel by the same rule.
+// 256 x 256 tiles on the direct-to-LDS kernel from two rounds of them on;
+// below that, the configuration with the smaller modelled time: rounds of
+// work items times their K steps, a 128 x 128 step costing 0.45 of a
+// 256 x 256 one (a quarter of the work at 56% of the rate, measured), split
+// slices adding their fp32 traffic (about 0.05 of a step each).
 int gemm_cfg_auto(const GemmArgs& g) {
     const int64_t tm = (g.M + 255) / 256, tn = (g.N + 255) / 256;
     const int64_t active = g.symmetric ? tm * (tm + 1) / 2 : tm * tn;
-    if (active < 2 * kCUs) return 0;
-    return (g.vec_p && g.vec_q && g.K % 64 == 0) ? 9 : 2;
+    const bool dma = g.vec_p && g.vec_q && g.K % 64 == 0;
+    if (!dma) return active >= 2 * kCUs ? 2 : 0;
+    if (active >= 2 * kCUs) return 9;
+    const int64_t nk = g.K / 64;
+    auto rounds = [](int64_t items) { return (double)((items + kCUs - 1) / kCUs); };
+    int64_t full = active;
+    const int ks = tail_split(active, nk, g.partial != nullptr, full);
+    const int64_t sliced = (active - full) * ks;
+    double t9 = rounds(full) * (double)nk;
+    if (sliced > 0) t9 += rounds(sliced) * (double)((nk + ks - 1) / ks) + 0.05 * (double)sliced;
+    const int64_t sm = (g.M + 127) / 128, sn = (g.N + 127) / 128;
+    const int64_t tiles0 = g.symmetric ? sm * (sm + 1) / 2 : sm * sn;
+    const double t0 = rounds(tiles0) * (double)nk * 0.45;
+    return t9 <= t0 ? 9 : 0;
 }
 
 }  // namespace

@@ -42,9 +42,10 @@ bool muon_layout(int64_t rows, int64_t cols, MuonLayout& L) {
     for (int i = 0; i < 2; ++i) { L.x[i] = off; off += mn; L.xt[i] = off; off += mn; }
     L.a = off; off += mm;
     L.b = off; off += mm;
-    // scratch for split tails, needed once a product has more tiles than CUs
+    // scratch for split products: a split needs a contraction of at least
+    // 16 steps of 64 (K = n for X X^T)
     L.split = -1;
-    if (((m + 255) / 256) * ((n + 255) / 256) > kCUs) { L.split = off; off += kSplitPartialBytes; }
+    if (n >= 1024) { L.split = off; off += kSplitPartialBytes; }
     L.total = off;
     return true;
 }

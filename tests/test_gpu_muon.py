@@ -194,34 +194,45 @@ def test_five_steps(shape):
     assert np.abs(s_got - s_ex).max() <= 0.05
 
 
-# Split tails: once a product has more 256 x 256 tiles than the GPU has CUs
-# and the last round is short, that round's tiles are cut along K, their fp32
-# slices summed in a second kernel.  At 5760 x 5760 all three products of a
-# step split (symmetric: 276 tiles, 20 in the tail; B X: 529 tiles, 17 in the
-# tail; 11 slices of 90 K steps, the last one empty).
-SPLIT_SHAPE = (5760, 5760)
+# Split products: a product whose last round of 256 x 256 tiles is short
+# (at most a quarter of the CUs), or that has fewer tiles than CUs, has that
+# round's tiles cut along K, their fp32 slices summed in a second kernel.
+#   5760 x 5760: all three products split their tail (symmetric 276 tiles, 20
+#     in the tail; B X 529, 17 in the tail; 11 slices of 90 K steps, the last
+#     one empty);
+#   1024 x 8192: X X^T (10 tiles, 16 slices) and B X (128 tiles, 2 slices)
+#     split whole, A A stays on 128 x 128 tiles;
+#   2048 x 7168 (a routed expert) and its transpose: X X^T (36 tiles, 7
+#     slices) and A A (4 slices) split whole, B X does not.
+SPLIT_SHAPES = [(5760, 5760), (1024, 8192), (2048, 7168), (7168, 2048)]
 
 
-def test_split_tail_one_step_within_propagated_bound():
-    Gb = _bf16_host(SPLIT_SHAPE, 15)
+@pytest.mark.parametrize("shape", SPLIT_SHAPES)
+def test_split_one_step_within_propagated_bound(shape):
+    Gb = _bf16_host(shape, 15)
     G = muon.bf16_bits_to_f64(Gb)
-    _say(f"[gpu] newton-schulz steps=1 {SPLIT_SHAPE} (split tails)")
+    _say(f"[gpu] newton-schulz steps=1 {shape} (split products)")
     got = _run_ns(Gb, 1)
     trace = []
     want = muon.newton_schulz(G, steps=1, trace=trace)
     X0 = muon.newton_schulz(G, steps=0)
+    if shape[0] > shape[1]:
+        X0 = X0.T
     (A, B, X1), = trace[0]
     dX0 = U * np.abs(X0) + ulp_bf16(X0)
     bound = ns_one_step_bound(X0, A, B, X1, dX0)
+    if shape[0] > shape[1]:
+        bound = bound.T
     bad = np.abs(got - want) > bound
     assert not bad.any(), (int(bad.sum()), float(np.abs(got - want).max()))
 
 
-def test_split_tail_matches_unsplit(monkeypatch):
+@pytest.mark.parametrize("shape", SPLIT_SHAPES[:3])
+def test_split_matches_unsplit(shape, monkeypatch):
     """The split path only reorders fp32 additions: two steps with and
     without it agree to within a few bf16 roundings."""
-    Gb = _bf16_host(SPLIT_SHAPE, 16)
-    _say(f"[gpu] newton-schulz steps=2 {SPLIT_SHAPE}, split and unsplit")
+    Gb = _bf16_host(shape, 16)
+    _say(f"[gpu] newton-schulz steps=2 {shape}, split and unsplit")
     a = _run_ns(Gb, 2)
     monkeypatch.setenv("VE_GEMM_SPLIT", "0")
     b = _run_ns(Gb, 2)
