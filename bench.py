@@ -238,6 +238,75 @@ def time_planner(ve, sizes=(64, 256, 1024)):
     return out
 
 
+def whole_bucket_grads(torch, cfg, lay, dev):
+    """Every tensor's bf16 gradient of bucket 0 (flat int16 views)."""
+    from synth.data import device_grad
+    return [device_grad(cfg, lay, 0, k, dev) for k in range(len(lay.tensors))]
+
+
+def time_copy_in_whole(torch, ve, plan, lay, grads, dev, reps=10, warmup=2):
+    """Whole-bucket group copy-in (``ve_dbuffer_copy_in`` with rank -1): every
+    tensor's bf16 gradient into the m*S bucket that the reduce-scatter reads,
+    padding written as 0.  Algorithmic bytes: 4 per tensor element (read +
+    write), 2 per padding element.  HIP events on the launch stream."""
+    n = lay.fsdp * lay.shard
+    elems = sum(t.numel for t in lay.tensors)
+    alg = 4 * elems + 2 * (n - elems)
+    gt = ve.grad_pointer_table(grads, dev)
+    bucket = torch.empty(n, dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        plan.copy_in(-1, gt, bucket, stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        plan.copy_in(-1, gt, bucket, stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    gbs = alg / (ms / 1e3) / 1e9
+    log(f"[bench] whole-bucket copy-in: {ms:.4f} ms, {gbs:.0f} GB/s")
+    del bucket
+    return {"bound": "hbm", "bucket_elems": n, "tensor_elems": elems, "alg_bytes": alg, "ms": round(ms, 5),
+            "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def rank_sweep(torch, ve, plan, lay, grads, dev, reps=10):
+    """The fused step on one bucket for every rank of the FSDP group in turn
+    (one bucket per call, so a call is ~20 us and launch gaps count): each
+    rank's time per call, as min / median / max over the ranks."""
+    import statistics
+    gt = ve.grad_pointer_table(grads, dev)
+    S = lay.shard
+    from synth import HPARAMS
+    hp = dict(HPARAMS)
+    stream = torch.cuda.current_stream()
+    master = torch.zeros(S, dtype=torch.float32, device=dev)
+    rows = []
+    for r in range(lay.fsdp):
+        valid, nblocks, _ = plan.query(r)
+        st = ve.new_state(plan, r, gt, master)
+        table = ve.state_table(plan, r, [st])
+        plan.step(r, table, hp, 1, stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(reps):
+            plan.step(r, table, hp, 2 + i, stream)
+        b.record(stream)
+        b.synchronize()
+        ms = a.elapsed_time(b) / reps
+        alg = BYTES_PER_ELEM * valid + BYTES_PER_BLOCK * nblocks + BYTES_PER_PAD * (S - valid)
+        rows.append((ms, alg / (ms / 1e3) / 1e9))
+        del st, table
+    us = sorted(1e3 * ms for ms, _ in rows)
+    gb = sorted(g for _, g in rows)
+    log(f"[bench] rank sweep: {us[0]:.1f} / {statistics.median(us):.1f} / {us[-1]:.1f} us per call")
+    return {"ranks": lay.fsdp, "buckets_per_call": 1, "calls_per_rank": reps,
+            "us_per_call": {"min": round(us[0], 2), "median": round(statistics.median(us), 2), "max": round(us[-1], 2)},
+            "gbs": {"min": round(gb[0], 1), "median": round(statistics.median(gb), 1), "max": round(gb[-1], 1)}}
+
+
 def copy_ceiling(torch, dev, gib, reps=10):
     """A plain device-to-device copy (torch's copy kernel) of ``gib`` GiB:
     read + write bytes over its time -- the practical streaming ceiling."""
@@ -269,6 +338,8 @@ def main():
     ap.add_argument("--no-group-ops", action="store_true", help="skip timing the DBuffer group operations")
     ap.add_argument("--no-muon", action="store_true", help="skip timing Muon's Newton-Schulz iteration")
     ap.add_argument("--no-planner", action="store_true", help="skip the bucket planner's padding / time report")
+    ap.add_argument("--no-copy-in", action="store_true", help="skip timing the whole-bucket copy-in")
+    ap.add_argument("--no-rank-sweep", action="store_true", help="skip the step over every rank of one bucket")
     ap.add_argument("--copy-gib", type=float, default=2.0,
                     help="size of the plain device copy that measures the copy ceiling (0: skip)")
     args = ap.parse_args()
@@ -361,6 +432,14 @@ def main():
                                           measured_group_traffic(args.workload))
     del states, table, buckets
     torch.cuda.empty_cache()
+    if not (args.no_copy_in and args.no_rank_sweep):
+        grads_all = whole_bucket_grads(torch, cfg, lay, dev)
+        if not args.no_copy_in:
+            out["copy_in_whole"] = time_copy_in_whole(torch, ve, plan, lay, grads_all, dev)
+        if not args.no_rank_sweep:
+            out["rank_sweep"] = rank_sweep(torch, ve, plan, lay, grads_all, dev)
+        del grads_all
+        torch.cuda.empty_cache()
     if not args.no_muon:
         out["muon"] = time_muon(torch, ve, dev)
         # a matrix far below one round of 256 x 256 tiles: a routed expert
