@@ -544,6 +544,11 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
         rt.huge.prefix.back() * 256 > kMaxGridItems || rt.pad.tile_prefix.back() > kMaxRunTiles)
         return fail(VE_ERR_UNSUPPORTED, "rank %d has more blocks than one launch covers", rank);
 
+    // A rank with small blocks and padding zero-fills the padding in the
+    // small-block launch (one launch fewer), when the grid allows it.
+    const int64_t small_wgs = (rt.small.prefix.back() + 3) / 4;
+    const bool fuse_pad = small_wgs > 0 && rt.pad.tile_prefix.back() > 0 &&
+                          (small_wgs + rt.pad.tile_prefix.back()) * 256 <= kMaxGridItems;
     StepArgs a{};
     a.states = states;
     a.segs = plan->dptr<Seg>(rt.off_segs);
@@ -572,7 +577,9 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
     }
     if (rt.small.prefix.back() > 0) {
         set_work(a, *plan, rt.small);
+        if (fuse_pad) a.pad = run_args(*plan, rt.pad);  // the padding fill rides along
         if ((st = launch_status(launch_step_small(a, n_states, s), "small-block step")) != VE_OK) return st;
+        a.pad = RunArgs{};
     }
     if (rt.huge.prefix.back() > 0) {
         for (size_t i0 = 0; i0 < rt.huge.seg_idx.size(); i0 += kInlineSegs) {
@@ -581,7 +588,7 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
             if ((st = launch_status(launch_step_huge(a, n_states, s), "large-block step")) != VE_OK) return st;
         }
     }
-    if (rt.pad.tile_prefix.back() > 0) {
+    if (rt.pad.tile_prefix.back() > 0 && !fuse_pad) {
         if ((st = launch_status(launch_runs_pad(run_args(*plan, rt.pad), states, n_states, s), "padding fill")) != VE_OK)
             return st;
     }

@@ -91,16 +91,6 @@ struct StepScalars {
     float decay;                     // 1 - lr * weight_decay
 };
 
-struct StepArgs {
-    const ve_shard_state* states;  // device [n_states]
-    const Seg* segs;               // device, this rank's segments
-    WorkList work;
-    StepScalars sc;
-    int32_t n_inline;              // workgroup paths: segments given inline below
-    int64_t inl_prefix[kInlineSegs + 1];  // work-item prefix, inl_prefix[0] = 0
-    Seg inl_segs[kInlineSegs];
-};
-
 struct RunArgs {
     const Run* runs;              // device
     const int64_t* tile_prefix;   // device, n_runs + 1
@@ -109,7 +99,22 @@ struct RunArgs {
     int64_t n_tiles;
 };
 
+struct StepArgs {
+    const ve_shard_state* states;  // device [n_states]
+    const Seg* segs;               // device, this rank's segments
+    WorkList work;
+    StepScalars sc;
+    RunArgs pad;                   // small-block path: padding tiles fused into the launch (n_tiles 0: none)
+    int64_t pad_wg0;               // small-block path: first workgroup of the padding tiles
+    int32_t n_inline;              // workgroup paths: segments given inline below
+    int64_t inl_prefix[kInlineSegs + 1];  // work-item prefix, inl_prefix[0] = 0
+    Seg inl_segs[kInlineSegs];
+};
+
+
 // Launchers (ve_kernels.hip).  Return the hipError_t of the launch.
+// Small-block step; a.pad's tiles (zero fill of grad_shard and param_shard)
+// run as extra workgroups of the same launch.
 hipError_t launch_step_small(const StepArgs& a, int n_states, hipStream_t s);
 hipError_t launch_step_wg(const StepArgs& a, int n_states, int threads, int groups_per_thread,
                           hipStream_t s);

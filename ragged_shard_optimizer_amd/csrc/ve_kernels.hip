@@ -538,7 +538,59 @@ __device__ __forceinline__ Seg find_global(const StepArgs& a, int64_t w, int64_t
 
 // ---------------------------------------------------------------------------
 // kernels
+// Tiled runs: copy a tensor range into the output, or write zeros.
+// mode 0: one output `out`; mode 1: grad_shard and param_shard of states[y].
+__device__ __forceinline__ void run_tile(const RunArgs& r, int64_t tile, const uint16_t* const* grad_ptrs,
+                                         uint16_t* out, const ve_shard_state* states, int mode, int y) {
+    constexpr int V = 8;                        // bf16 per 16-byte vector
+    constexpr int PER = kRunTile / (256 * V);   // vectors per thread
+    const int ri = r.tile_run[tile];
+    const Run rn = r.runs[ri];
+    const int64_t t0 = (tile - r.tile_prefix[ri]) * kRunTile;
+    const int64_t len = min((int64_t)kRunTile, rn.len - t0);
+    uint16_t* o0 = out;
+    uint16_t* o1 = nullptr;
+    if (mode == 1) {
+        o0 = states[y].grad_shard;
+        o1 = states[y].param_shard;
+    }
+    const uint16_t* src = rn.tensor >= 0 ? grad_ptrs[rn.tensor] + rn.src + t0 : nullptr;
+    const bool aligned = (((uintptr_t)(o0 + rn.dst + t0) | (uintptr_t)(o1 ? o1 + rn.dst + t0 : nullptr) |
+                           (uintptr_t)src) & 15) == 0;
+    const VE_GLOBAL uint16_t* s = (const VE_GLOBAL uint16_t*)src;
+    VE_GLOBAL uint16_t* d0 = (VE_GLOBAL uint16_t*)(o0 + rn.dst + t0);
+    VE_GLOBAL uint16_t* d1 = o1 ? (VE_GLOBAL uint16_t*)(o1 + rn.dst + t0) : nullptr;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        // vector q*256 + tid: each wave-wide access is 1 KB contiguous
+        const int64_t i0 = ((int64_t)q * 256 + threadIdx.x) * V;
+        if (i0 >= len) break;
+        if (aligned && i0 + V <= len) {
+            u32x4 a = u32x4{0, 0, 0, 0};
+            if (s) a = ldv<VE_NONTEMPORAL>((const VE_GLOBAL u32x4*)(s + i0));
+            stv<VE_NONTEMPORAL>((VE_GLOBAL u32x4*)(d0 + i0), a);
+            if (d1) stv<VE_NONTEMPORAL>((VE_GLOBAL u32x4*)(d1 + i0), a);
+        } else {
+            const int64_t n = min((int64_t)V, len - i0);
+            for (int64_t k = 0; k < n; ++k) {
+                const uint16_t v = s ? s[i0 + k] : (uint16_t)0;
+                d0[i0 + k] = v;
+                if (d1) d1[i0 + k] = v;
+            }
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256) k_runs(RunArgs r, const uint16_t* const* grad_ptrs, uint16_t* out,
+                                              const ve_shard_state* states, int mode) {
+    run_tile(r, blockIdx.x, grad_ptrs, out, states, mode, blockIdx.y);
+}
+
 __global__ void __launch_bounds__(256) k_step_small(StepArgs a) {
+    if ((int64_t)blockIdx.x >= a.pad_wg0) {  // a padding tile of the same launch
+        run_tile(a.pad, (int64_t)blockIdx.x - a.pad_wg0, nullptr, nullptr, a.states, 1, blockIdx.y);
+        return;
+    }
     constexpr int CH = kSmallChunk;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -908,59 +960,16 @@ __global__ void __launch_bounds__(256) k_step_huge(StepArgs a) {
     }
 }
 
-// Tiled runs: copy a tensor range into the output, or write zeros.
-// mode 0: one output `out`; mode 1: grad_shard and param_shard of states[y].
-__global__ void __launch_bounds__(256) k_runs(RunArgs r, const uint16_t* const* grad_ptrs, uint16_t* out,
-                                              const ve_shard_state* states, int mode) {
-    constexpr int V = 8;                        // bf16 per 16-byte vector
-    constexpr int PER = kRunTile / (256 * V);   // vectors per thread
-    const int64_t tile = blockIdx.x;
-    const int ri = r.tile_run[tile];
-    const Run rn = r.runs[ri];
-    const int64_t t0 = (tile - r.tile_prefix[ri]) * kRunTile;
-    const int64_t len = min((int64_t)kRunTile, rn.len - t0);
-    uint16_t* o0 = out;
-    uint16_t* o1 = nullptr;
-    if (mode == 1) {
-        o0 = states[blockIdx.y].grad_shard;
-        o1 = states[blockIdx.y].param_shard;
-    }
-    const uint16_t* src = rn.tensor >= 0 ? grad_ptrs[rn.tensor] + rn.src + t0 : nullptr;
-    const bool aligned = (((uintptr_t)(o0 + rn.dst + t0) | (uintptr_t)(o1 ? o1 + rn.dst + t0 : nullptr) |
-                           (uintptr_t)src) & 15) == 0;
-    const VE_GLOBAL uint16_t* s = (const VE_GLOBAL uint16_t*)src;
-    VE_GLOBAL uint16_t* d0 = (VE_GLOBAL uint16_t*)(o0 + rn.dst + t0);
-    VE_GLOBAL uint16_t* d1 = o1 ? (VE_GLOBAL uint16_t*)(o1 + rn.dst + t0) : nullptr;
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        // vector q*256 + tid: each wave-wide access is 1 KB contiguous
-        const int64_t i0 = ((int64_t)q * 256 + threadIdx.x) * V;
-        if (i0 >= len) break;
-        if (aligned && i0 + V <= len) {
-            u32x4 a = u32x4{0, 0, 0, 0};
-            if (s) a = ldv<VE_NONTEMPORAL>((const VE_GLOBAL u32x4*)(s + i0));
-            stv<VE_NONTEMPORAL>((VE_GLOBAL u32x4*)(d0 + i0), a);
-            if (d1) stv<VE_NONTEMPORAL>((VE_GLOBAL u32x4*)(d1 + i0), a);
-        } else {
-            const int64_t n = min((int64_t)V, len - i0);
-            for (int64_t k = 0; k < n; ++k) {
-                const uint16_t v = s ? s[i0 + k] : (uint16_t)0;
-                d0[i0 + k] = v;
-                if (d1) d1[i0 + k] = v;
-            }
-        }
-    }
-}
-
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // launchers
 static inline unsigned grid_x(int64_t n) { return (unsigned)n; }
 
-hipError_t launch_step_small(const StepArgs& a, int n_states, hipStream_t s) {
-    const int64_t wgs = (a.work.total + 3) / 4;
-    hipLaunchKernelGGL(k_step_small, dim3(grid_x(wgs), n_states), dim3(256), 0, s, a);
+hipError_t launch_step_small(const StepArgs& a0, int n_states, hipStream_t s) {
+    StepArgs a = a0;
+    a.pad_wg0 = (a.work.total + 3) / 4;
+    hipLaunchKernelGGL(k_step_small, dim3(grid_x(a.pad_wg0 + a.pad.n_tiles), n_states), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
