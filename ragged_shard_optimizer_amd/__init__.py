@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import ctypes as C
 import os
+import weakref
 
 import numpy as np
 
@@ -119,6 +120,7 @@ class Plan:
         self.shard_elems = int(shard_elems)
         self.device = int(device)
         self._pieces = {}
+        self._grads_ok = {}  # rank -> gradient tables already checked for it
 
     def pieces(self, rank: int):
         """[(tensor, elem_end)] of every tensor ``rank`` (or the whole bucket
@@ -132,6 +134,22 @@ class Plan:
                     got.append((k, sl[2]))
             self._pieces[rank] = got
         return self._pieces[rank]
+
+    def _check_grads(self, rank: int, grad_table):
+        """Every tensor whose piece ``rank`` copies has a gradient reaching the
+        piece's end.  A gradient table is fixed once built, so each one is
+        checked once per rank (a bucket of 10,000 tensors would otherwise
+        spend longer here than in the copy)."""
+        ok = self._grads_ok.setdefault(int(rank), weakref.WeakSet())
+        if grad_table in ok:
+            return
+        if len(grad_table.grads) != self.n_tensors:
+            raise ValueError("grad table length != number of tensors in the plan")
+        for k, end in self.pieces(rank):
+            g = grad_table.grads[k]
+            if g is None or g.numel() < end:
+                raise ValueError(f"tensor {k} is copied on rank {rank} but its gradient is missing or short")
+        ok.add(grad_table)
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:
@@ -166,12 +184,7 @@ class Plan:
         elements."""
         need = self.shard_elems * (self.fsdp_size if rank < 0 else 1)
         _require_buffer(bucket, need, 2, "bucket")
-        if len(grad_table.grads) != self.n_tensors:
-            raise ValueError("grad table length != number of tensors in the plan")
-        for k, end in self.pieces(rank):
-            g = grad_table.grads[k]
-            if g is None or g.numel() < end:
-                raise ValueError(f"tensor {k} is copied on rank {rank} but its gradient is missing or short")
+        self._check_grads(rank, grad_table)
         _check(lib().ve_dbuffer_copy_in(self._h, int(rank), C.c_void_p(grad_table.table.data_ptr()),
                                         C.c_void_p(bucket.data_ptr()), _stream_handle(stream)))
 

@@ -15,7 +15,8 @@
 //
 // Bound: HBM.  Algorithmic bytes per tensor element: zero 2 (write), scale 4
 // (read + write), accumulate 6 (bucket read + write, gradient read); 2 per
-// padding element (write).  A tile is 4096 elements of one run; a thread
+// padding element (write).  A tile is up to 4096 elements of one run, cut at
+// 128-byte positions of the bucket (run_tile_span); a thread
 // moves two 16-byte vectors, lane-contiguous, so every wave access covers
 // 1 KB of whole cache lines and carries the streaming hint.  A tile whose
 // bucket or gradient address is not 16-byte aligned (ragged pieces of 1-D
@@ -51,8 +52,9 @@ __global__ void __launch_bounds__(256) k_group(RunArgs r, const ve_group_operand
     const int64_t tile = blockIdx.x;
     const int ri = r.tile_run[tile];
     const Run rn = r.runs[ri];
-    const int64_t t0 = (tile - r.tile_prefix[ri]) * kRunTile;
-    const int len = (int)min((int64_t)kRunTile, rn.len - t0);
+    int64_t t0, n;
+    run_tile_span(rn.dst, rn.len, tile - r.tile_prefix[ri], t0, n);
+    const int len = (int)n;
     const ve_group_operand od = ops[blockIdx.y];
     VE_GLOBAL uint16_t* d = (VE_GLOBAL uint16_t*)(od.bucket + rn.dst + t0);
     // zero, and padding under every op: plain fill, nothing read

@@ -72,7 +72,7 @@ void add_run(HostRuns& h, int64_t dst, int64_t src, int64_t len, int32_t tensor)
     Run r{dst, src, len, tensor, 0};
     const int32_t ri = (int32_t)h.runs.size();
     h.runs.push_back(r);
-    const int64_t tiles = (len + kRunTile - 1) / kRunTile;
+    const int64_t tiles = run_tiles(dst, len);
     h.tile_prefix.push_back(h.tile_prefix.back() + tiles);
     for (int64_t t = 0; t < tiles; ++t) h.tile_run.push_back(ri);
     if (tensor < 0) h.zero_elems += len;

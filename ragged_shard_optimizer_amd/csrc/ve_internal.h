@@ -39,6 +39,22 @@ constexpr int kInlineSegs = 16;
 #define VE_RUN_TILE 4096
 #endif
 constexpr int kRunTile = VE_RUN_TILE;
+// Tiles are cut at multiples of kRunAlign elements of the destination (128
+// bytes of bf16), so that no cache line is written by two workgroups (which
+// run on different XCDs, whose L2s would each write back a partial line):
+// the first tile of a run is short by the run's offset mod kRunAlign.
+constexpr int kRunAlign = 64;
+__host__ __device__ inline int64_t run_head(int64_t dst) { return dst & (kRunAlign - 1); }
+__host__ __device__ inline int64_t run_tiles(int64_t dst, int64_t len) {
+    return len <= 0 ? 0 : (len + run_head(dst) + kRunTile - 1) / kRunTile;
+}
+// Tile j of a run covers run elements [t0, t0 + n), 0 < n <= kRunTile.
+__host__ __device__ inline void run_tile_span(int64_t dst, int64_t len, int64_t j, int64_t& t0, int64_t& n) {
+    const int64_t h = run_head(dst);
+    const int64_t end = (j + 1) * kRunTile - h;
+    t0 = j == 0 ? 0 : j * kRunTile - h;
+    n = (end < len ? end : len) - t0;
+}
 // A dispatch's grid is at most 2^32 - 1 work-items per dimension.
 constexpr int64_t kMaxGridItems = 0xFFFFFFFFll;
 constexpr int64_t kMaxRunTiles = kMaxGridItems / 256;  // run kernels: 256 threads per tile

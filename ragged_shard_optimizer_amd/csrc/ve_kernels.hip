@@ -546,8 +546,8 @@ __device__ __forceinline__ void run_tile(const RunArgs& r, int64_t tile, const u
     constexpr int PER = kRunTile / (256 * V);   // vectors per thread
     const int ri = r.tile_run[tile];
     const Run rn = r.runs[ri];
-    const int64_t t0 = (tile - r.tile_prefix[ri]) * kRunTile;
-    const int64_t len = min((int64_t)kRunTile, rn.len - t0);
+    int64_t t0, len;
+    run_tile_span(rn.dst, rn.len, tile - r.tile_prefix[ri], t0, len);
     uint16_t* o0 = out;
     uint16_t* o1 = nullptr;
     if (mode == 1) {

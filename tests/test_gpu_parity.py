@@ -103,6 +103,26 @@ def test_copy_in_bit_exact(name):
     plan.close()
 
 
+def test_copy_in_rejects_short_gradient_per_table():
+    """The binding checks each gradient table once per rank; a second table
+    with a short gradient is still rejected after a good one was used."""
+    import torch
+    ve = _ve()
+    cfg, lay = layout_of("toy_mix")
+    plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
+    from synth.data import host_grads
+    grads = [to_dev_u16(g) for g in host_grads(cfg, lay, 0, 1)]
+    out = torch.zeros(lay.shard, dtype=torch.int16, device=DEV)
+    plan.copy_in(1, ve.grad_pointer_table(grads), out)
+    k = plan.pieces(1)[0][0]
+    short = list(grads)
+    short[k] = grads[k][:1]
+    with pytest.raises(ValueError, match="missing or short"):
+        plan.copy_in(1, ve.grad_pointer_table(short), out)
+    torch.cuda.synchronize()
+    plan.close()
+
+
 # ---------------------------------------------------------------------------
 # edge-case layouts, placed by hand (edge_layouts.py)
 @pytest.mark.parametrize("case", list(EDGE))
