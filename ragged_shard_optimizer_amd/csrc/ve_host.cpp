@@ -61,7 +61,6 @@ struct RankTables {
     std::vector<Seg> segs;
     size_t off_segs = 0;
     HostWork small, wg, huge;
-    int32_t wg_max_groups = 0;
     HostRuns copy;  // pieces + padding of the rank slice
     HostRuns pad;   // padding only (the step's zero fill)
     int64_t valid = 0, nblocks = 0;
@@ -212,7 +211,6 @@ void build_rank(ve_plan& P, int32_t r, RankTables& rt) {
         const int64_t items = s.cls == kSmall ? ceil_div(s.nblocks, 64 / s.group) : s.nblocks;
         w.seg_idx.push_back(si);
         w.prefix.push_back(w.prefix.back() + items);
-        if (s.cls == kWg) rt.wg_max_groups = std::max(rt.wg_max_groups, s.max_groups);
         const int64_t dst = a - c0;
         add_run(rt.copy, cursor, 0, dst - cursor, -1);
         add_run(rt.pad, cursor, 0, dst - cursor, -1);
@@ -291,8 +289,8 @@ int64_t set_inline(StepArgs& a, const RankTables& rt, const HostWork& w, size_t 
 }
 
 // Workgroup path shape: threads and 4-element groups per thread for blocks
-// of up to `groups` groups.  Measured on MI355X over the model workloads
-// (one launch per rank, all blocks of a class share the shape):
+// of up to `groups` groups (each run of segments with one shape is a launch).
+// Measured on MI355X over the model workloads:
 //   2,049 .. 4,096 groups (128x128 tiles): 1024 threads x 4 (two resident
 //     workgroups per CU) beat 512 x 8 by ~2%;
 //   4,097 .. 12,288 groups (row blocks of 16K..48K elements): 512 threads
@@ -538,9 +536,7 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
         return fail(VE_ERR_INVALID_ARG, "lr / eps / weight_decay must be finite and eps > 0");
     if (!plan->dev) return fail(VE_ERR_INVALID_ARG, "host-only plan (device -1) cannot launch kernels");
     const RankTables& rt = plan->ranks[(size_t)rank];
-    int threads = 256, gpt = 1;
-    if (rt.wg.prefix.back() > 0) wg_shape(rt.wg_max_groups, threads, gpt);
-    if ((rt.small.prefix.back() + 3) / 4 * 256 > kMaxGridItems || rt.wg.prefix.back() * threads > kMaxGridItems ||
+    if ((rt.small.prefix.back() + 3) / 4 * 256 > kMaxGridItems || rt.wg.prefix.back() * kWgMaxThreads > kMaxGridItems ||
         rt.huge.prefix.back() * 256 > kMaxGridItems || rt.pad.tile_prefix.back() > kMaxRunTiles)
         return fail(VE_ERR_UNSUPPORTED, "rank %d has more blocks than one launch covers", rank);
 
@@ -568,9 +564,23 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
     hipStream_t s = (hipStream_t)stream;
     ve_status st;
     if (rt.wg.prefix.back() > 0) {
-        for (size_t i0 = 0; i0 < rt.wg.seg_idx.size(); i0 += kInlineSegs) {
-            const size_t i1 = std::min(rt.wg.seg_idx.size(), i0 + (size_t)kInlineSegs);
-            if (set_inline(a, rt, rt.wg, i0, i1) == 0) continue;
+        // One launch per run of consecutive segments whose blocks take the same
+        // shape (a rank's segments are sorted by block size, so a rank holding
+        // the end of one tensor and most of a tensor with smaller blocks gets
+        // two launches instead of running every block in the larger shape).
+        const size_t n = rt.wg.seg_idx.size();
+        auto shape_of = [&](size_t i, int& t, int& g) { wg_shape(rt.segs[(size_t)rt.wg.seg_idx[i]].max_groups, t, g); };
+        for (size_t i0 = 0; i0 < n;) {
+            int threads = 256, gpt = 1;
+            shape_of(i0, threads, gpt);
+            size_t i1 = i0 + 1;
+            for (int t1, g1; i1 < n && i1 - i0 < (size_t)kInlineSegs; ++i1) {
+                shape_of(i1, t1, g1);
+                if (t1 != threads || g1 != gpt) break;
+            }
+            const int64_t nb = set_inline(a, rt, rt.wg, i0, i1);
+            i0 = i1;
+            if (nb == 0) continue;
             if ((st = launch_status(launch_step_wg(a, n_states, threads, gpt, s), "workgroup step")) != VE_OK)
                 return st;
         }
