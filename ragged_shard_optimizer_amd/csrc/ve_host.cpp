@@ -193,7 +193,10 @@ void build_rank(ve_plan& P, int32_t r, RankTables& rt) {
         const int64_t chunks = chunks_of(kSmallChunk), groups = chunks_of(kWgChunk);
         s.max_chunks = (int32_t)std::min<int64_t>(chunks, INT32_MAX);
         s.max_groups = (int32_t)std::min<int64_t>(groups, INT32_MAX);
-        if (chunks <= kSmallMaxChunks) {
+        if (br * t.cols == 1) {  // one-element blocks (then block_cols == cols == 1)
+            s.cls = kUnit;
+            s.group = 1;
+        } else if (chunks <= kSmallMaxChunks) {
             s.cls = kSmall;
             s.group = next_pow2((int32_t)chunks);
         } else if (groups <= kWgMaxGroups) {
@@ -207,8 +210,10 @@ void build_rank(ve_plan& P, int32_t r, RankTables& rt) {
         rt.segs.push_back(s);
         block0 += s.nblocks;
         rt.valid += s.elem_hi - s.elem_lo;
-        HostWork& w = s.cls == kSmall ? rt.small : (s.cls == kWg ? rt.wg : rt.huge);
-        const int64_t items = s.cls == kSmall ? ceil_div(s.nblocks, 64 / s.group) : s.nblocks;
+        HostWork& w = (s.cls == kSmall || s.cls == kUnit) ? rt.small : (s.cls == kWg ? rt.wg : rt.huge);
+        const int64_t items = s.cls == kSmall  ? ceil_div(s.nblocks, 64 / s.group)
+                              : s.cls == kUnit ? ceil_div(s.nblocks, kUnitPerWave)
+                                               : s.nblocks;
         w.seg_idx.push_back(si);
         w.prefix.push_back(w.prefix.back() + items);
         const int64_t dst = a - c0;

@@ -59,7 +59,10 @@ __host__ __device__ inline void run_tile_span(int64_t dst, int64_t len, int64_t 
 constexpr int64_t kMaxGridItems = 0xFFFFFFFFll;
 constexpr int64_t kMaxRunTiles = kMaxGridItems / 256;  // run kernels: 256 threads per tile
 
-enum SegClass : int32_t { kSmall = 0, kWg = 1, kHuge = 2 };
+// kUnit: one-element blocks (a block's maximum is the element itself), on
+// the small-block work list with kUnitPerWave blocks per wave item.
+enum SegClass : int32_t { kSmall = 0, kWg = 1, kHuge = 2, kUnit = 3 };
+constexpr int kUnitPerWave = 64 * kSmallChunk;
 
 // One tensor piece on one rank ("segment"), in device-visible form.
 struct Seg {

@@ -329,10 +329,8 @@ __device__ __forceinline__ void adam_update(const In<CH>& x, float (&mst)[CH], f
 // Phase 1 on one chunk: moments, AdamW update, writes of master, bf16 param
 // and the gradient copy; folds the chunk into the running absmax.
 template <int CH>
-__device__ __forceinline__ void phase1(const In<CH>& x, float (&mst)[CH], const Ptrs& p, const ChunkPos& c,
-                                       bool vec, float sm, float sv, const StepScalars& sc, float& am,
-                                       float& av) {
-    adam_update(x, mst, sm, sv, sc, am, av);
+__device__ __forceinline__ void store_phase1(const In<CH>& x, const float (&mst)[CH], const Ptrs& p,
+                                             const ChunkPos& c, bool vec) {
     uint32_t pb[CH / 2];
 #pragma unroll
     for (int i = 0; i < CH / 2; ++i) pb[i] = pack_bf16x2(mst[2 * i], mst[2 * i + 1]);
@@ -363,6 +361,14 @@ __device__ __forceinline__ void phase1(const In<CH>& x, float (&mst)[CH], const 
     }
 }
 
+template <int CH>
+__device__ __forceinline__ void phase1(const In<CH>& x, float (&mst)[CH], const Ptrs& p, const ChunkPos& c,
+                                       bool vec, float sm, float sv, const StepScalars& sc, float& am,
+                                       float& av) {
+    adam_update(x, mst, sm, sv, sc, am, av);
+    store_phase1(x, mst, p, c, vec);
+}
+
 __device__ __forceinline__ uint32_t quant_byte(float x, float inv) {
     float q = __builtin_rintf(x * inv);
     q = __builtin_fminf(__builtin_fmaxf(q, -127.f), 127.f);
@@ -388,10 +394,8 @@ __device__ __forceinline__ void quantise(const In<CH>& x, float sm, float sv, fl
 // Phase 2 on one chunk: recompute the moments from the held inputs and write
 // their codes under the block's new scales.
 template <int CH>
-__device__ __forceinline__ void phase2(const In<CH>& x, const Ptrs& p, const ChunkPos& c, bool vec, float sm,
-                                       float sv, float im, float iv, const StepScalars& sc) {
-    uint32_t qm[CH / 4], qv[CH / 4];
-    quantise(x, sm, sv, im, iv, sc, qm, qv);
+__device__ __forceinline__ void store_codes(const uint32_t (&qm)[CH / 4], const uint32_t (&qv)[CH / 4],
+                                            const Ptrs& p, const ChunkPos& c, bool vec) {
     if (vec) {
         if constexpr (CH == 16) {
             stv<kStream<CH>>((VE_GLOBAL u32x4*)(p.m_q + c.s), u32x4{qm[0], qm[1], qm[2], qm[3]});
@@ -409,6 +413,14 @@ __device__ __forceinline__ void phase2(const In<CH>& x, const Ptrs& p, const Chu
             }
         }
     }
+}
+
+template <int CH>
+__device__ __forceinline__ void phase2(const In<CH>& x, const Ptrs& p, const ChunkPos& c, bool vec, float sm,
+                                       float sv, float im, float iv, const StepScalars& sc) {
+    uint32_t qm[CH / 4], qv[CH / 4];
+    quantise(x, sm, sv, im, iv, sc, qm, qv);
+    store_codes<CH>(qm, qv, p, c, vec);
 }
 
 // ---------------------------------------------------------------------------
@@ -586,6 +598,82 @@ __global__ void __launch_bounds__(256) k_runs(RunArgs r, const uint16_t* const* 
     run_tile(r, blockIdx.x, grad_ptrs, out, states, mode, blockIdx.y);
 }
 
+// One-element blocks (kUnit): a lane takes one 16-element chunk, i.e. 16
+// consecutive blocks, each with its own pair of scales.  A block's maximum is
+// its element's own |m1| (v1), so no lane exchange is needed.  Every value
+// goes through the general path's operations in the same order, so the
+// results are bit-identical to a group of one lane per block.
+__device__ __forceinline__ void step_unit(const StepArgs& a, const Seg& sg, const ve_shard_state& st,
+                                          int64_t local, int lane) {
+    constexpr int CH = kSmallChunk;
+    const int64_t k0 = local * kUnitPerWave + (int64_t)lane * CH;  // the lane's first block
+    const int64_t left = sg.nblocks - k0;
+    if (left <= 0) return;
+    const Ptrs p = make_ptrs(st, sg.tensor);
+    ChunkPos c;
+    c.e = sg.panel0 + k0;  // one element per row, one row per block
+    c.s = sg.shard_base + c.e;
+    c.n = (int32_t)min((int64_t)CH, left);
+    const bool vec = vec_ok<CH>(p, c);
+    VE_GLOBAL float* msc = (VE_GLOBAL float*)st.m_scale + (sg.block0 + k0);
+    VE_GLOBAL float* vsc = (VE_GLOBAL float*)st.v_scale + (sg.block0 + k0);
+    const bool svec = c.n == CH && ((((uintptr_t)msc) | ((uintptr_t)vsc)) & 15) == 0;
+    In<CH> x;
+    float mst[CH], sm[CH], sv[CH];
+    load_in(x, p, c, vec);
+    load_master(mst, p, c, vec);
+    if (svec) {
+#pragma unroll
+        for (int i = 0; i < CH / 4; ++i) {
+            const f32x4 m = ((const VE_GLOBAL f32x4*)msc)[i], v = ((const VE_GLOBAL f32x4*)vsc)[i];
+            sm[4 * i] = m.x; sm[4 * i + 1] = m.y; sm[4 * i + 2] = m.z; sm[4 * i + 3] = m.w;
+            sv[4 * i] = v.x; sv[4 * i + 1] = v.y; sv[4 * i + 2] = v.z; sv[4 * i + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            sm[i] = i < c.n ? msc[i] : 0.f;
+            sv[i] = i < c.n ? vsc[i] : 0.f;
+        }
+    }
+    uint32_t qm[CH / 4], qv[CH / 4];
+    float nm[CH], nv[CH];
+#pragma unroll
+    for (int i = 0; i < CH / 4; ++i) qm[i] = qv[i] = 0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        float m1, v1;
+        moments(elem_g(x, i), code_at(x.m[i >> 2], i & 3), code_at(x.v[i >> 2], i & 3), sm[i], sv[i], a.sc, m1, v1);
+        const float am = fmaxf(0.f, fabsf(m1)), av = fmaxf(0.f, v1);
+        const float d = __builtin_fmaf(__builtin_amdgcn_sqrtf(v1), a.sc.inv_sqrt_bc2, a.sc.eps);
+        const float u = m1 * __builtin_amdgcn_rcpf(d);
+        mst[i] = __builtin_fmaf(-a.sc.step_size, u, mst[i] * a.sc.decay);
+        const float im = am > 0.f ? 127.0f / am : 0.f;
+        const float iv = av > 0.f ? 127.0f / av : 0.f;
+        qm[i >> 2] |= quant_byte(m1, im) << (8 * (i & 3));
+        qv[i >> 2] |= quant_byte(v1, iv) << (8 * (i & 3));
+        nm[i] = am / 127.0f;
+        nv[i] = av / 127.0f;
+    }
+    store_phase1(x, mst, p, c, vec);
+    store_codes<CH>(qm, qv, p, c, vec);
+    if (svec) {
+#pragma unroll
+        for (int i = 0; i < CH / 4; ++i) {
+            ((VE_GLOBAL f32x4*)msc)[i] = f32x4{nm[4 * i], nm[4 * i + 1], nm[4 * i + 2], nm[4 * i + 3]};
+            ((VE_GLOBAL f32x4*)vsc)[i] = f32x4{nv[4 * i], nv[4 * i + 1], nv[4 * i + 2], nv[4 * i + 3]};
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            if (i < c.n) {
+                msc[i] = nm[i];
+                vsc[i] = nv[i];
+            }
+        }
+    }
+}
+
 __global__ void __launch_bounds__(256) k_step_small(StepArgs a) {
     if ((int64_t)blockIdx.x >= a.pad_wg0) {  // a padding tile of the same launch
         run_tile(a.pad, (int64_t)blockIdx.x - a.pad_wg0, nullptr, nullptr, a.states, 1, blockIdx.y);
@@ -599,6 +687,10 @@ __global__ void __launch_bounds__(256) k_step_small(StepArgs a) {
     int64_t local;
     const Seg sg = find_global(a, gw, local);
     const ve_shard_state st = a.states[blockIdx.y];
+    if (sg.cls == kUnit) {
+        step_unit(a, sg, st, local, lane);
+        return;
+    }
     const int G = sg.group;
     const int64_t k = local * (64 / G) + lane / G;
     const int li = lane & (G - 1);
