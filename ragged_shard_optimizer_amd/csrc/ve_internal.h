@@ -8,13 +8,15 @@
 
 namespace ve {
 
-// Elements per lane-chunk.  Small blocks: 16 (one 16-byte vector of codes,
-// two of bf16, four of fp32 per lane).  Workgroup blocks: 4 (a dword of
-// codes, 8 bytes of bf16, 16 bytes of fp32 per lane, so that the 64 lanes of
-// a wave touch one contiguous span per access).
-constexpr int kSmallChunk = 16;
+// Elements per lane-chunk: 4 on both paths (a dword of codes, 8 bytes of
+// bf16, 16 bytes of fp32 per lane, so that the 64 lanes of a wave touch one
+// contiguous span per access).  Small blocks are latency-bound (a ragged
+// rank holds ~700 K elements), and 4-element chunks give them four times the
+// waves of 16-element ones.  The small-block code also takes 16-element
+// chunks (kernel helpers are written for both).
+constexpr int kSmallChunk = 4;
 constexpr int kWgChunk = 4;
-// A block with at most this many 16-element chunks is handled by a group of
+// A block with at most this many chunks (256 elements) is handled by a group of
 // <= 64 lanes of one wave (one chunk per lane); larger blocks take a whole
 // workgroup.
 constexpr int kSmallMaxChunks = 64;
@@ -78,7 +80,7 @@ struct Seg {
     int32_t tiles;       // tiles per panel = cols / block_cols
     int32_t cls;         // SegClass
     int32_t group;       // small path: lanes per block (power of two <= 64)
-    int32_t max_chunks;  // 16-element chunks of a full block (small path)
+    int32_t max_chunks;  // small-path chunks of a full block
     int32_t max_groups;  // 4-element groups of a full block (workgroup path)
 };
 

@@ -20,9 +20,11 @@
 //            scale, write the codes.
 //
 // Block-size classes (decided per rank segment at plan load):
-//   small  <= 64 chunks of 16 elements: a group of G (power of two) lanes of
-//          one wave owns a block, one 16-element chunk per lane, 64/G blocks
-//          per wave (1-, 16-, 128-element blocks of ragged buckets);
+//   small  <= 64 chunks of kSmallChunk (4) elements: a group of G (power of
+//          two) lanes of one wave owns a block, one chunk per lane, 64/G
+//          blocks per wave (16- and 128-element blocks of ragged buckets);
+//   unit   one-element blocks, kSmallChunk blocks per lane (norms, ragged
+//          buckets' 1-row vectors);
 //   wg     one workgroup owns a block; lanes own 4-element groups so that
 //          every wave-wide access is one contiguous span (1 KB of fp32
 //          master, 512 B of bf16, 256 B of codes), GPT groups per thread
@@ -598,7 +600,7 @@ __global__ void __launch_bounds__(256) k_runs(RunArgs r, const uint16_t* const* 
     run_tile(r, blockIdx.x, grad_ptrs, out, states, mode, blockIdx.y);
 }
 
-// One-element blocks (kUnit): a lane takes one 16-element chunk, i.e. 16
+// One-element blocks (kUnit): a lane takes one chunk, i.e. kSmallChunk
 // consecutive blocks, each with its own pair of scales.  A block's maximum is
 // its element's own |m1| (v1), so no lane exchange is needed.  Every value
 // goes through the general path's operations in the same order, so the

@@ -22,7 +22,8 @@ def _group_sizes_case():
     for i, (rows, cols, br, bc) in enumerate([
             (33, 1, 1, 1), (40, 1, 16, 1), (9, 24, 1, 24), (7, 64, 1, 64), (5, 96, 2, 96),
             (6, 128, 2, 128), (8, 64, 8, 64), (4, 256, 4, 256), (3, 1024, 1, 1024),
-            (2, 2048, 2, 2048), (40, 48, 8, 12), (64, 80, 16, 16), (17, 7, 3, 7)]):
+            (2, 2048, 2, 2048), (40, 48, 8, 12), (64, 80, 16, 16), (17, 7, 3, 7), (36, 1, 4, 1),
+            (24, 1, 8, 1), (10, 3, 1, 3)]):
         ts.append(TensorDef(f"g{i}", rows, cols, br, bc))
         offs.append(cur)
         cur += rows * cols + (16 if i % 2 else 0)
