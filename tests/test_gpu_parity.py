@@ -158,6 +158,20 @@ def test_workgroup_access_forms(shape, monkeypatch):
     tally.check()
 
 
+# A rank holding the end of one tensor and rows of another with smaller
+# blocks takes one launch per block shape (llama_mini rank 4: 3,584- and
+# 1,024-element rows; llama_rowblk rank 20: 28,672-element rows of `down`,
+# then 512-element rows of q, k, v, o).
+@pytest.mark.parametrize("name,rank", [("llama_mini", 4), ("llama_rowblk", 20)])
+def test_rank_with_two_block_shapes(name, rank):
+    cfg, lay = layout_of(name)
+    sizes = {lay.tensors[k].block_rows * lay.tensors[k].cols for k, *_ in lay.chunk_intervals(rank)}
+    assert len([b for b in sizes if b > 256]) > 1  # two workgroup-path block sizes
+    tally = Tally()
+    _run_parity(cfg, lay, [rank], 2, tally)
+    tally.check()
+
+
 def test_one_element_blocks_codes_exact():
     # 1-element blocks: every nonzero code is +-127 and the scale is |m|/127
     cfg, lay = _explicit("unit", [TensorDef("a", 999, 1, 1, 1), TensorDef("b", 21, 17, 1, 1)], [0, 1008], 2, 768)
