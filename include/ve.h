@@ -133,7 +133,11 @@ ve_status ve_dbuffer_copy_in(const ve_plan* plan, int32_t rank, const uint16_t* 
                              uint16_t* bucket, void* stream);
 
 /* The fused shard step on `rank` for n_states buckets that share this plan
- * (one launch per path; states is a DEVICE array [n_states]).  For every
+ * (states is a DEVICE array [n_states]; a few launches on `stream`: one per
+ * workgroup block shape among the rank's pieces, one for small blocks that
+ * also zero-fills the padding, one per slice of blocks too large for
+ * registers, and a separate padding fill when there are no small blocks).
+ * For every
  * piece element: copy the gradient into grad_shard, dequantise the moments
  * with the block's stored scales, update the Adam moments, update master
  * with decoupled weight decay and bias correction for step `step` (>= 1),
