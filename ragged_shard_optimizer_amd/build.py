@@ -28,10 +28,7 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(os.path.dirname(OUT), exist_ok=True)
-    tmp = OUT + f".tmp{os.getpid()}"
-    cmd = ["hipcc", *HIPCC_FLAGS, *SOURCES, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,6 +38,24 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(noise))
     if verbose and noise:
         print("\n".join(noise), file=sys.stderr)
+
+
+def build(verbose: bool = False, defines=()) -> str:
+    """Compile every source to an object (in parallel), then link libve.so.
+    ``defines``: extra ``NAME=VALUE`` macros (measurement builds)."""
+    from concurrent.futures import ThreadPoolExecutor
+    odir = os.path.join(os.path.dirname(OUT), f"obj{os.getpid()}")
+    os.makedirs(odir, exist_ok=True)
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"] + [f"-D{d}" for d in defines]
+    objs = [os.path.join(odir, os.path.basename(src) + ".o") for src in SOURCES]
+    jobs = min(len(SOURCES), max(1, os.cpu_count() or 1))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(lambda so: _run(["hipcc", *flags, "-c", so[0], "-o", so[1]], verbose), zip(SOURCES, objs)))
+    tmp = OUT + f".tmp{os.getpid()}"
+    _run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    for o in objs:
+        os.remove(o)
+    os.rmdir(odir)
     os.replace(tmp, OUT)
     return OUT
 

@@ -293,6 +293,26 @@ int64_t set_inline(StepArgs& a, const RankTables& rt, const HostWork& w, size_t 
     return a.work.total;
 }
 
+// Launch-shape knobs for measurement, read from the environment once per
+// process (the defaults are the measured choices): VE_WG_THREADS and
+// VE_WG_GPT pin the workgroup shape of the step.
+struct Tuning {
+    int wg_threads = 0, wg_gpt = 0;
+};
+
+const Tuning& tuning() {
+    static const Tuning t = [] {
+        Tuning r;
+        auto num = [](const char* name, int& v) {
+            if (const char* e = std::getenv(name)) v = std::atoi(e);
+        };
+        num("VE_WG_THREADS", r.wg_threads);
+        num("VE_WG_GPT", r.wg_gpt);
+        return r;
+    }();
+    return t;
+}
+
 // Workgroup path shape: threads and 4-element groups per thread for blocks
 // of up to `groups` groups (each run of segments with one shape is a launch).
 // Measured on MI355X over the model workloads:
@@ -306,11 +326,10 @@ int64_t set_inline(StepArgs& a, const RankTables& rt, const HostWork& w, size_t 
 //     least 6 groups (fewer leave the per-block prologue exposed), else 256.
 // VE_WG_THREADS / VE_WG_GPT override it (launch-shape tuning).
 void wg_shape(int32_t groups, int& threads, int& gpt) {
-    const char* et = std::getenv("VE_WG_THREADS");
-    const char* eg = std::getenv("VE_WG_GPT");
-    if (et && eg) {
-        threads = std::atoi(et);
-        gpt = std::atoi(eg);
+    const Tuning& tn = tuning();
+    if (tn.wg_threads > 0 && tn.wg_gpt > 0) {
+        threads = tn.wg_threads;
+        gpt = tn.wg_gpt;
         if (wg_config_supported(threads, gpt) && (int64_t)threads * gpt >= groups) return;
     }
     auto fit = [&](int t, int min_g, int& g) {

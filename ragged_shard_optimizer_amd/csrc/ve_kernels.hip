@@ -313,19 +313,31 @@ __device__ __forceinline__ float elem_g(const In<CH>& x, int i) {
 // AdamW update of one chunk's master values from its held inputs; folds the
 // fresh moments into the running absmax (nothing when act is false: an idle
 // lane whose registers duplicate a valid chunk).
+// The fresh moments are also left in km / kv (for a caller that keeps them
+// in registers through the reduction instead of recomputing them).
 template <int CH>
-__device__ __forceinline__ void adam_update(const In<CH>& x, float (&mst)[CH], float sm, float sv,
-                                            const StepScalars& sc, float& am, float& av, bool act = true) {
+__device__ __forceinline__ void adam_update_k(const In<CH>& x, float (&mst)[CH], float sm, float sv,
+                                              const StepScalars& sc, float& am, float& av, float (&km)[CH],
+                                              float (&kv)[CH], bool act = true) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
         float m1, v1;
         moments(elem_g(x, i), code_at(x.m[i >> 2], i & 3), code_at(x.v[i >> 2], i & 3), sm, sv, sc, m1, v1);
+        km[i] = m1;
+        kv[i] = v1;
         am = fmaxf(am, act ? fabsf(m1) : 0.f);
         av = fmaxf(av, act ? v1 : 0.f);
         const float d = __builtin_fmaf(__builtin_amdgcn_sqrtf(v1), sc.inv_sqrt_bc2, sc.eps);
         const float u = m1 * __builtin_amdgcn_rcpf(d);
         mst[i] = __builtin_fmaf(-sc.step_size, u, mst[i] * sc.decay);
     }
+}
+
+template <int CH>
+__device__ __forceinline__ void adam_update(const In<CH>& x, float (&mst)[CH], float sm, float sv,
+                                            const StepScalars& sc, float& am, float& av, bool act = true) {
+    float km[CH], kv[CH];
+    adam_update_k(x, mst, sm, sv, sc, am, av, km, kv, act);
 }
 
 // Phase 1 on one chunk: moments, AdamW update, writes of master, bf16 param
@@ -486,16 +498,36 @@ __device__ __forceinline__ void load_master_fast(float (&mst)[4], const FastRsrc
     mst[3] = __int_as_float(v.w);
 }
 
-__device__ __forceinline__ void phase1_fast(const In<4>& x, float (&mst)[4], const FastRsrc& f,
-                                            const ChunkAddr& a, float sm, float sv, const StepScalars& sc,
-                                            float& am, float& av) {
-    adam_update(x, mst, sm, sv, sc, am, av);
+__device__ __forceinline__ void phase1_fast_k(const In<4>& x, float (&mst)[4], const FastRsrc& f,
+                                              const ChunkAddr& a, float sm, float sv, const StepScalars& sc,
+                                              float& am, float& av, float (&km)[4], float (&kv)[4]) {
+    adam_update_k(x, mst, sm, sv, sc, am, av, km, kv);
     const uint32_t p0 = pack_bf16x2(mst[0], mst[1]), p1 = pack_bf16x2(mst[2], mst[3]);
     const i32x4 mv = {__float_as_int(mst[0]), __float_as_int(mst[1]), __float_as_int(mst[2]), __float_as_int(mst[3])};
     __builtin_amdgcn_raw_buffer_store_b128(mv, f.master, (int)a.v4, (int)a.s4, kBufNT);
     __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int32_t)p0, (int32_t)p1}, f.param, (int)a.v2, (int)a.s2, kBufNT);
     __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int32_t)x.g[0], (int32_t)x.g[1]}, f.grad_shard, (int)a.v2,
                                           (int)a.s2, kBufNT);
+}
+
+__device__ __forceinline__ void phase1_fast(const In<4>& x, float (&mst)[4], const FastRsrc& f,
+                                            const ChunkAddr& a, float sm, float sv, const StepScalars& sc,
+                                            float& am, float& av) {
+    float km[4], kv[4];
+    phase1_fast_k(x, mst, f, a, sm, sv, sc, am, av, km, kv);
+}
+
+// Phase 2 from moments kept in registers since phase 1.
+__device__ __forceinline__ void phase2_fast_kept(const float (&km)[4], const float (&kv)[4], const FastRsrc& f,
+                                                 const ChunkAddr& a, float im, float iv) {
+    uint32_t qm = 0, qv = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        qm |= quant_byte(km[i], im) << (8 * i);
+        qv |= quant_byte(kv[i], iv) << (8 * i);
+    }
+    __builtin_amdgcn_raw_buffer_store_b32((int32_t)qm, f.m_q, (int)a.v1, (int)a.s1, kBufNT);
+    __builtin_amdgcn_raw_buffer_store_b32((int32_t)qv, f.v_q, (int)a.v1, (int)a.s1, kBufNT);
 }
 
 __device__ __forceinline__ void phase2_fast(const In<4>& x, const FastRsrc& f, const ChunkAddr& a, float sm,
@@ -907,21 +939,41 @@ __device__ __forceinline__ void wg_issue(In<kWgChunk> (&x)[GPT], float (&mst)[MA
     if constexpr (MODE != kWgGeneral) __builtin_amdgcn_sched_barrier(0);
 }
 
+// Whether a FAST block keeps its fresh moments in registers from phase 1 to
+// phase 2 (eight VGPRs per group) instead of recomputing them from the four
+// held input registers (more VALU work than the quantisation itself).
+// Measured on MI355X: 1.0% faster for 128x128 tiles in 1024 x 4 workgroups,
+// 2-3% slower for the 28,672- and 46,080-element row blocks in 512-thread
+// workgroups, so it is used for the 1024-thread shapes with few groups only.
+#ifndef VE_KEEP_MOMENTS
+#define VE_KEEP_MOMENTS 2  // 0: never, 1: always, 2: 1024-thread shapes of up to 8 groups
+#endif
+template <int T, int GPT>
+struct WgKeep {
+    static constexpr bool value = VE_KEEP_MOMENTS == 1 || (VE_KEEP_MOMENTS == 2 && T == 1024 && GPT <= 8);
+};
+
 // One block: phase 1 (inputs already issued), the absmax reduction, phase 2.
 template <int T, int GPT, int MA, int MODE>
 __device__ __forceinline__ void wg_block(In<kWgChunk> (&x)[GPT], float (&mst)[MA + 1][kWgChunk],
                                          const uint32_t (&off)[GPT], const WgItem& it, float (&red)[2][T / 64],
                                          const StepScalars& sc) {
     constexpr int CH = kWgChunk;
+    constexpr bool KEEP = MODE != kWgGeneral && WgKeep<T, GPT>::value;
     const int tid = threadIdx.x;
     const int nch = it.geo.nchunks;
     float am = 0.f, av = 0.f;
+    float km[KEEP ? GPT : 1][CH], kv[KEEP ? GPT : 1][CH];
 #pragma unroll
     for (int c = 0; c < GPT; ++c) {
         const int ci = wg_slot_chunk<T, GPT>(it, c);
         if constexpr (MODE != kWgGeneral) {
             if (c + MA < GPT) load_master_fast(mst[(c + MA) % (MA + 1)], it.fb, wg_addr<T, GPT, MODE>(it, off, c + MA));
-            phase1_fast(x[c], mst[c % (MA + 1)], it.fb, wg_addr<T, GPT, MODE>(it, off, c), it.sm, it.sv, sc, am, av);
+            if constexpr (KEEP)
+                phase1_fast_k(x[c], mst[c % (MA + 1)], it.fb, wg_addr<T, GPT, MODE>(it, off, c), it.sm, it.sv, sc, am,
+                              av, km[c], kv[c]);
+            else
+                phase1_fast(x[c], mst[c % (MA + 1)], it.fb, wg_addr<T, GPT, MODE>(it, off, c), it.sm, it.sv, sc, am, av);
             // keep the groups in program order (hoisting later groups' work
             // would run out of registers)
             __builtin_amdgcn_sched_barrier(0);
@@ -962,6 +1014,11 @@ __device__ __forceinline__ void wg_block(In<kWgChunk> (&x)[GPT], float (&mst)[MA
 #pragma unroll
     for (int c = 0; c < GPT; ++c) {
         const int ci = wg_slot_chunk<T, GPT>(it, c);
+        if constexpr (KEEP) {
+            phase2_fast_kept(km[c], kv[c], it.fb, wg_addr<T, GPT, MODE>(it, off, c), im, iv);
+            __builtin_amdgcn_sched_barrier(0);
+            continue;
+        }
         make_opaque(x[c]);
         if constexpr (MODE != kWgGeneral) {
             phase2_fast(x[c], it.fb, wg_addr<T, GPT, MODE>(it, off, c), it.sm, it.sv, im, iv, sc);
