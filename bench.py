@@ -74,43 +74,70 @@ def measured_group_traffic(workload):
     return None if d is None else d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, lay, rank, budget_s=12.0):
-    """The oracle (single-threaded plain C) on a bounded sample of the same
-    workload: a few distinct host buckets of the rank's shard, stepped in turn
-    until about ``budget_s`` of CPU time is spent."""
-    import numpy as np
+def host_cores():
+    """(threads the CPU legs use, CPUs visible to this process): the visible
+    CPUs, capped by OMP_NUM_THREADS when that is set (the machine's CPU share)."""
+    try:
+        visible = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        visible = os.cpu_count() or 1
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(visible, int(share)) if share.isdigit() and int(share) > 0 else visible
+    return threads, visible
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, lay, rank, budget_s=8.0):
+    """The oracle (plain C, fp64 updates) on a bounded sample of the same
+    workload: bucket 0 of the rank's shard, with the workload's seeded
+    inputs (the rank's gradient pieces, its master shard), stepped over and
+    over for about ``budget_s`` seconds per leg.  Two legs: one host thread,
+    and the rank's blocks split over every host thread this process may use
+    (bit-identical results).  Input generation is not timed."""
     import oracle
-    from synth.data import f32_to_bf16_bits
+    from synth import HPARAMS
+    from synth.data import host_master, host_piece_grads
     spec, S = lay.spec_array(), lay.shard
-    pieces = list(lay.chunk_intervals(rank))
-    rng = np.random.default_rng(1)
-    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
-    sets = []
-    n_sets = 4
-    for _ in range(n_sets):
-        grads, bases = [None] * len(lay.tensors), [0] * len(lay.tensors)
-        for k, lo, hi, _dst in pieces:
-            grads[k] = f32_to_bf16_bits((rng.standard_normal(hi - lo) * cfg.grad_scale).astype(np.float32))
-            bases[k] = lo
-        st = oracle.new_state(spec, S, rank, (rng.standard_normal(S) * cfg.param_std).astype(np.float32))
-        sets.append((grads, bases, st))
-    oracle.shard_step(spec, lay.fsdp, S, rank, sets[0][0], sets[0][2], hp, 1, bases=sets[0][1])  # warm
-    done, t0, step = 0, time.perf_counter(), 2
-    while True:
-        grads, bases, st = sets[done % n_sets]
-        oracle.shard_step(spec, lay.fsdp, S, rank, grads, st, hp, step, bases=bases)
-        done += 1
-        if done % n_sets == 0:
-            step += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s and done >= n_sets:
-            break
+    hp = dict(HPARAMS)
+    grads, bases = host_piece_grads(cfg, lay, 0, rank, step=1)
+    st = oracle.new_state(spec, S, rank, host_master(cfg, lay, 0, rank))
     nb, nv = oracle.rank_blocks(spec, S, rank)
     alg = BYTES_PER_ELEM * nv + BYTES_PER_BLOCK * nb + BYTES_PER_PAD * (S - nv)
-    return {"value": round(alg * done / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "params_per_s": round(nv * done / el, 1),
-            "sample": f"{done} bucket-steps of rank {rank} ({nv} elements each, {n_sets} distinct host "
-                      f"buckets stepped in turn), {el:.1f} s wall, single thread"}
+    threads, visible = host_cores()
+    step = 1
+    oracle.shard_step(spec, lay.fsdp, S, rank, grads, st, hp, step, bases=bases)  # warm (step 1 from zero)
+    legs = {}
+    for name, nthr in (("single_thread", 1), ("all_threads", threads)):
+        done, t0 = 0, time.perf_counter()
+        while True:
+            step += 1
+            oracle.shard_step_threads(spec, lay.fsdp, S, rank, grads, st, hp, step, bases=bases, threads=nthr)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+        legs[name] = {"threads": nthr, "steps": done, "seconds": round(el, 3),
+                      "value": round(alg * done / el / 1e9, 4), "params_per_s": round(nv * done / el, 1)}
+        log(f"[bench] oracle {name} ({nthr} threads): {legs[name]['value']} GB/s")
+    best = legs["all_threads"]
+    return {"value": best["value"], "unit": "GB/s", "cores": best["threads"], "kind": "oracle",
+            "params_per_s": best["params_per_s"],
+            "single_thread": legs["single_thread"], "all_threads": legs["all_threads"],
+            "host": {"cpus_visible": visible, "cpu_model": cpu_model()},
+            "sample": f"bucket 0 of rank {rank} ({nv} elements, {nb} blocks; the workload's seeded gradient "
+                      f"pieces and master shard), stepped repeatedly for ~{budget_s:.0f} s on 1 thread and "
+                      f"~{budget_s:.0f} s on {best['threads']} threads (blocks split over the threads); "
+                      f"value is the {best['threads']}-thread rate"}
 
 
 def time_group_ops(torch, ve, plan, rank, states, lay, valid, steps, warmup, traffic=None):
@@ -148,13 +175,23 @@ def time_group_ops(torch, ve, plan, rank, states, lay, valid, steps, warmup, tra
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+# Muon's published quintic coefficients (a, b, c) of X <- a X + (b A + c A^2) X
+NS_COEFFS = (3.4445, -4.7750, 2.0315)
+
+
+def ns_flops(rows, cols, steps=5):
+    """Work of the Newton-Schulz iteration counted the minimal way, two flops
+    per multiply-add: with m = min(rows, cols) and n = max, each step is
+    X X^T (symmetric, m*m*n multiply-adds), A A (symmetric, m^3) and B X
+    (2*m*m*n)."""
+    m, n = min(rows, cols), max(rows, cols)
+    return steps * (3 * m * m * n + m * m * m)
 
 
 def time_muon(torch, ve, dev, rows=8192, cols=28672, steps=3, warmup=1, name="LLaMA-3-70B MLP"):
     """Muon's Newton-Schulz iteration (5 steps) on one gathered matrix (by
     default of the LLaMA-3-70B MLP shape), HIP events on the launch stream;
     flops counted the minimal way (symmetric products at half cost)."""
-    from oracle import muon
     stream = torch.cuda.current_stream()
     g = torch.Generator(device=dev)
     g.manual_seed(5)
@@ -171,7 +208,7 @@ def time_muon(torch, ve, dev, rows=8192, cols=28672, steps=3, warmup=1, name="LL
         b.record(stream)
     torch.cuda.synchronize()
     ms = sum(a.elapsed_time(b) for a, b in ev) / steps
-    flops = muon.flops(rows, cols)
+    flops = ns_flops(rows, cols)
     tf = flops / (ms / 1e3) / 1e12
     log(f"[bench] muon newton-schulz {rows}x{cols}: {ms:.3f} ms, {tf:.1f} TFLOP/s")
     del G, out, ws
@@ -180,7 +217,7 @@ def time_muon(torch, ve, dev, rows=8192, cols=28672, steps=3, warmup=1, name="LL
     # fused into addmm), timed the same way
     m, n = min(rows, cols), max(rows, cols)
     X = torch.randn(m, n, device=dev, dtype=torch.bfloat16, generator=g) / (m * n) ** 0.5
-    a_, b_, c_ = muon.NS_COEFFS
+    a_, b_, c_ = NS_COEFFS
 
     def torch_ns(X):
         for _ in range(5):
@@ -239,9 +276,10 @@ def time_planner(ve, sizes=(64, 256, 1024)):
 
 
 def whole_bucket_grads(torch, cfg, lay, dev):
-    """Every tensor's bf16 gradient of bucket 0 (flat int16 views)."""
-    from synth.data import device_grad
-    return [device_grad(cfg, lay, 0, k, dev) for k in range(len(lay.tensors))]
+    """Every tensor's bf16 gradient of bucket 0 (flat int16 views, drawn a
+    few hundred million elements per launch)."""
+    from synth.workload import whole_bucket_grads as draw
+    return draw(cfg, lay, dev)
 
 
 def time_copy_in_whole(torch, ve, plan, lay, grads, dev, reps=10, warmup=2):
@@ -307,24 +345,169 @@ def rank_sweep(torch, ve, plan, lay, grads, dev, reps=10):
             "gbs": {"min": round(gb[0], 1), "median": round(statistics.median(gb), 1), "max": round(gb[-1], 1)}}
 
 
-def copy_ceiling(torch, dev, gib, reps=10):
-    """A plain device-to-device copy (torch's copy kernel) of ``gib`` GiB:
-    read + write bytes over its time -- the practical streaming ceiling."""
-    n = int(gib * (1 << 30)) // 4
-    src = torch.ones(n, dtype=torch.float32, device=dev)
+def _hip_memcpy_dtod():
+    """hipMemcpyDtoDAsync from the HIP runtime (via ctypes), or None."""
+    import ctypes as C
+    for name in ("libamdhip64.so", "libamdhip64.so.7", "libamdhip64.so.6"):
+        try:
+            L = C.CDLL(name)
+        except OSError:
+            continue
+        f = L.hipMemcpyDtoDAsync
+        f.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+        f.restype = C.c_int
+        return f
+    return None
+
+
+def copy_ceiling(torch, ve, dev, gib, reps=10):
+    """The streaming reference on ``gib`` GiB: the library's 16-byte
+    non-temporal copy kernel (ve_stream_copy) and the runtime's
+    hipMemcpyDtoD on the same buffers; read + write bytes over the time,
+    HIP events on the launch stream."""
+    import ctypes as C
+    nbytes = int(gib * (1 << 30)) // 16 * 16
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        dst.copy_(src)
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    ms = timed(lambda: ve.stream_copy(dst, src, stream))
+    assert torch.equal(dst, src)
+    out = {"bytes": 2 * nbytes, "kernel": "ve_stream_copy (16-byte non-temporal loads and stores)",
+           "ms": round(ms, 5), "gbs": round(2 * nbytes / (ms / 1e3) / 1e9, 2)}
+    dtod = _hip_memcpy_dtod()
+    if dtod is not None:
+        h = C.c_void_p(stream.cuda_stream)
+        mt = timed(lambda: dtod(C.c_void_p(dst.data_ptr()), C.c_void_p(src.data_ptr()), nbytes, h))
+        out["hipMemcpyDtoD"] = {"ms": round(mt, 5), "gbs": round(2 * nbytes / (mt / 1e3) / 1e9, 2)}
+    log(f"[bench] copy ceiling {gib} GiB: stream copy {out['gbs']} GB/s"
+        + (f", hipMemcpyDtoD {out['hipMemcpyDtoD']['gbs']} GB/s" if "hipMemcpyDtoD" in out else ""))
     del src, dst
     torch.cuda.empty_cache()
-    return {"bytes": 2 * 4 * n, "ms": round(ms, 5), "gbs": round(2 * 4 * n / (ms / 1e3) / 1e9, 2)}
+    return out
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (the text and JSON files under profiles/)
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _workload_alg(workload, buckets=None):
+    """(algorithmic bytes of one all-bucket step launch, buckets, valid, blocks, shard)."""
+    from synth import CONFIGS, plan_p0
+    import ragged_shard_optimizer_amd as ve
+    cfg = CONFIGS[workload]
+    lay = plan_p0(cfg.tensors, cfg.fsdp)
+    rank = lay.largest_rank()
+    nv, nb, _ = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=-1).query(rank)
+    nbk = buckets or cfg.n_buckets
+    alg = nbk * (BYTES_PER_ELEM * nv + BYTES_PER_BLOCK * nb + BYTES_PER_PAD * (lay.shard - nv))
+    return alg, nbk, nv, nb, lay.shard
+
+
+def _step_dispatches(rows, name_key, grid_key):
+    """The step-kernel rows of the launch that covers every bucket: kernels
+    named k_step_*, at the largest grid among them."""
+    st = [r for r in rows if "k_step" in r[name_key]]
+    if not st:
+        raise SystemExit("no k_step_* kernel in the profile")
+    big = max(int(r[grid_key]) for r in st)
+    return [r for r in st if int(r[grid_key]) == big]
+
+
+def summarize_counters(args):
+    """HBM bytes per launch of the step kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each counter scaled by
+    what it reads for the streaming copy of known size in the same run."""
+    import statistics
+    f_rows = [r for r in _csv_rows(os.path.join(args.fetch_dir, "run_counter_collection.csv"))
+              if r["Counter_Name"] == "FETCH_SIZE"]
+    w_rows = [r for r in _csv_rows(os.path.join(args.write_dir, "run_counter_collection.csv"))
+              if r["Counter_Name"] == "WRITE_SIZE"]
+    copy_kib = int(args.copy_gib * (1 << 30)) // 16 * 16 / 1024.0
+
+    def calib(rows):
+        v = [float(r["Counter_Value"]) for r in rows if "k_stream_copy" in r["Kernel_Name"]]
+        if not v:
+            raise SystemExit("no streaming-copy dispatch in the counter run (run bench.py with --copy-gib > 0)")
+        return copy_kib / statistics.mean(v), statistics.mean(v)
+
+    fx, fc = calib(f_rows)
+    wx, wc = calib(w_rows)
+    fs = _step_dispatches(f_rows, "Kernel_Name", "Grid_Size")
+    ws = _step_dispatches(w_rows, "Kernel_Name", "Grid_Size")
+    kernel = fs[0]["Kernel_Name"]
+    fk = statistics.mean(float(r["Counter_Value"]) for r in fs)
+    wk = statistics.mean(float(r["Counter_Value"]) for r in ws)
+    rb, wb = fk * fx * 1024, wk * wx * 1024
+    alg, nbk, nv, nb, S = _workload_alg(args.workload, args.buckets)
+    h = kernel_source_hash(STEP_SOURCES)
+    txt = [f"# HBM traffic of the fused shard step, {args.workload} workload (rocprofv3 --pmc)",
+           f"kernel sources hash: {h}", "",
+           "commands (run from the repository root on the GPU box), one pass per counter:",
+           "  " + args.command_fetch, "  " + args.command_write, "",
+           f"calibration: the streaming copy (k_stream_copy) reads and writes {copy_kib:.0f} KiB per dispatch;",
+           f"  it reads FETCH_SIZE {fc:.1f} KiB and WRITE_SIZE {wc:.1f} KiB -> FETCH_SIZE x {fx:.4f}, WRITE_SIZE x {wx:.4f}",
+           "", f"kernel: {kernel} ({len(fs)} / {len(ws)} dispatches of the all-bucket launch)",
+           f"  per dispatch FETCH_SIZE {fk:.1f} KiB, WRITE_SIZE {wk:.1f} KiB",
+           f"  HBM bytes per launch: read {rb / 1e9:.4f} GB + write {wb / 1e9:.4f} GB = {(rb + wb) / 1e9:.4f} GB",
+           f"  algorithmic bytes per launch ({nbk} buckets x ({BYTES_PER_ELEM} B x {nv} elements + "
+           f"{BYTES_PER_BLOCK} B x {nb} blocks + {BYTES_PER_PAD} B x {S - nv} padding)) = {alg / 1e9:.4f} GB",
+           f"  measured / algorithmic = {(rb + wb) / alg:.4f}"]
+    base = os.path.join(ROOT, "profiles", f"shard_step_{args.workload}")
+    with open(base + "_hbm_counters.txt", "w") as fh:
+        fh.write("\n".join(txt) + "\n")
+    with open(base + "_traffic.json", "w") as fh:
+        json.dump({"kernel": kernel, "kernel_source_hash": h, "hbm_bytes_per_launch": rb + wb, "read_bytes": rb,
+                   "write_bytes": wb, "alg_bytes_per_launch": float(alg), "fetch_factor": fx, "write_factor": wx,
+                   "summary": f"profiles/shard_step_{args.workload}_hbm_counters.txt"}, fh, indent=1)
+    print("\n".join(txt))
+
+
+def summarize_trace(args):
+    """Kernel table and the step kernel's average duration (all-bucket
+    launches) from a rocprofv3 --kernel-trace --stats run."""
+    import statistics
+    stats = _csv_rows(os.path.join(args.trace_dir, "run_kernel_stats.csv"))
+    trace = _csv_rows(os.path.join(args.trace_dir, "run_kernel_trace.csv"))
+    st = _step_dispatches(trace, "Kernel_Name", "Grid_Size")
+    kernel = st[0]["Kernel_Name"]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in st]
+    avg = statistics.mean(durs)
+    alg, nbk, nv, nb, S = _workload_alg(args.workload, args.buckets)
+    t = [f"# Kernel trace of bench.py, {args.workload} workload (rocprofv3 --kernel-trace --stats)", "",
+         f"kernel sources hash: {kernel_source_hash(STEP_SOURCES)}", "",
+         "command (run from the repository root on the GPU box):", "  " + args.command, "",
+         f"{'kernel':72s} {'calls':>6s} {'avg us':>10s} {'min us':>10s} {'max us':>10s}"]
+    for r in stats[:args.top]:
+        t.append(f"{r['Name'][:72]:72s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
+                 f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f}")
+    t += ["", f"step: {kernel}",
+          f"  all-bucket launches: average {avg:.1f} us over {len(durs)} dispatches (min {min(durs):.1f}, "
+          f"max {max(durs):.1f}); algorithmic bytes per launch {alg / 1e9:.4f} GB -> {alg / avg / 1e3:.1f} GB/s "
+          f"= {alg / avg / 1e3 / HBM_PEAK_GBS * 100:.1f}% of 8 TB/s"]
+    if args.bench_log and os.path.exists(args.bench_log):
+        with open(args.bench_log) as fh:
+            keep = [ln.strip() for ln in fh if ln.startswith("[bench]")]
+        t += ["", "bench.py's own HIP-event timing in the same run:"] + ["  " + ln for ln in keep]
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(t) + "\n")
+    print("\n".join(t))
 
 
 def main():
@@ -340,9 +523,25 @@ def main():
     ap.add_argument("--no-planner", action="store_true", help="skip the bucket planner's padding / time report")
     ap.add_argument("--no-copy-in", action="store_true", help="skip timing the whole-bucket copy-in")
     ap.add_argument("--no-rank-sweep", action="store_true", help="skip the step over every rank of one bucket")
-    ap.add_argument("--copy-gib", type=float, default=2.0,
-                    help="size of the plain device copy that measures the copy ceiling (0: skip)")
+    ap.add_argument("--copy-gib", type=float, default=1.0,
+                    help="size of the streaming-reference copy that measures the copy ceiling (0: skip)")
+    sm = ap.add_argument_group("profile summaries (no GPU needed)")
+    sm.add_argument("--summarize", choices=["counters", "trace"], default=None,
+                    help="write a profiles/ summary from rocprofv3 output instead of benchmarking")
+    sm.add_argument("--fetch-dir", help="counters: output folder of the FETCH_SIZE run")
+    sm.add_argument("--write-dir", help="counters: output folder of the WRITE_SIZE run")
+    sm.add_argument("--command-fetch", default="", help="counters: the FETCH_SIZE command, for the record")
+    sm.add_argument("--command-write", default="", help="counters: the WRITE_SIZE command, for the record")
+    sm.add_argument("--trace-dir", help="trace: output folder of the --kernel-trace --stats run")
+    sm.add_argument("--command", default="", help="trace: the profiled command, for the record")
+    sm.add_argument("--bench-log", default=None, help="trace: bench.py's stderr of the profiled run")
+    sm.add_argument("--out", default=None, help="trace: summary file to write")
+    sm.add_argument("--top", type=int, default=16, help="trace: kernels listed")
     args = ap.parse_args()
+    if args.summarize:
+        sys.path.insert(0, ROOT)
+        (summarize_counters if args.summarize == "counters" else summarize_trace)(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the data-parallel step; --gpus {args.gpus} is not "
               f"supported (the collectives around the step are outside this library)", file=sys.stderr)
@@ -448,7 +647,7 @@ def main():
     if not args.no_planner:
         out["planner"] = time_planner(ve)
     if args.copy_gib > 0:
-        out["copy_ceiling"] = copy_ceiling(torch, dev, args.copy_gib)
+        out["copy_ceiling"] = copy_ceiling(torch, ve, dev, args.copy_gib)
         out["copy_ceiling_frac"] = round(gbs / out["copy_ceiling"]["gbs"], 4)
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on host cores")

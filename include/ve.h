@@ -191,6 +191,15 @@ typedef struct {
 ve_status ve_dbuffer_group_op(const ve_plan* plan, int32_t rank, int32_t op, float alpha,
                               const ve_group_operand* operands, int32_t n_operands, void* stream);
 
+/* Streaming reference (not part of the method): copy `bytes` bytes from
+ * `src` to `dst` (device pointers, both 16-byte aligned, bytes a multiple
+ * of 16, not overlapping) with 16-byte non-temporal accesses on `stream`.
+ * It is the measured bandwidth that the HBM-bound kernels above are
+ * compared with: read + write bytes over its time.  Errors: a NULL or
+ * misaligned buffer, a size that is negative or not a multiple of 16, or
+ * overlapping buffers give VE_ERR_INVALID_ARG; bytes == 0 is a no-op. */
+ve_status ve_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
+
 /* Structure-aware bucket planner (talk notes, "2. Structure-aware planning
  * algorithm"; Dutch summary, "2B"; Korean summary, "2.2").  Host only: no
  * device is touched.  Reads rows, cols and block_rows of the host array

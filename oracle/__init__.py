@@ -220,7 +220,7 @@ def shard_step(spec, m: int, S: int, rank: int, grads, state: dict, hp: dict, t:
     # exactly those values, widened to double
     f = lambda key: float(np.float32(hp[key]))
     h = _HParams(f("lr"), f("beta1"), f("beta2"), f("eps"), f("weight_decay"))
-    sel = None if blocks is None else np.ascontiguousarray(blocks, dtype=np.int64)
+    sel = None if blocks is None else np.unique(np.asarray(blocks, dtype=np.int64))
     rc = lib().ora_shard_step(arr, n, m, S, rank, ptrs, _ptr(base),
                               _ptr(state["grad_shard"]), _ptr(state["master"]), _ptr(state["m_q"]),
                               _ptr(state["v_q"]), _ptr(state["m_scale"]), _ptr(state["v_scale"]),
@@ -228,6 +228,35 @@ def shard_step(spec, m: int, S: int, rank: int, grads, state: dict, hp: dict, t:
                               _ptr(sel), 0 if sel is None else len(sel))
     if rc != 0:
         raise OracleError(lib().ora_last_error().decode())
+    return state
+
+
+def shard_step_threads(spec, m: int, S: int, rank: int, grads, state: dict, hp: dict, t: int, bases=None,
+                       threads: int = 1) -> dict:
+    """The same step as :func:`shard_step`, with the rank's blocks split into
+    ``threads`` contiguous ranges stepped by that many host threads at once
+    (each C call releases the interpreter lock; blocks touch disjoint
+    elements and scales).  Padding is zeroed afterwards as the full step
+    does.  Every block is still computed by the same serial code, so the
+    result does not depend on ``threads``."""
+    nb, _ = rank_blocks(spec, S, rank)
+    if threads <= 1 or nb < 2:
+        return shard_step(spec, m, S, rank, grads, state, hp, t, bases=bases)
+    lib()
+    cuts = np.linspace(0, nb, min(threads, nb) + 1).astype(np.int64)
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=len(cuts) - 1) as ex:
+        futs = [ex.submit(shard_step, spec, m, S, rank, grads, state, hp, t, bases, np.arange(a, b))
+                for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+        for f in futs:
+            f.result()
+    covered = np.zeros(S, dtype=bool)
+    for k in range(len(np.asarray(spec).reshape(-1, 5))):
+        sl = slice_(spec, m, S, rank, k)
+        if sl is not None:
+            covered[sl[0]:sl[0] + sl[2] - sl[1]] = True
+    state["grad_shard"][~covered] = 0
+    state["param_shard"][~covered] = 0
     return state
 
 

@@ -65,7 +65,7 @@ typedef struct {
     int64_t rows, cols, block_rows, block_cols, offset;
 } ora_tensor;
 
-static char g_msg[512];
+static _Thread_local char g_msg[512];
 const char* ora_last_error(void) { return g_msg; }
 
 static int fail(const char* fmt, ...) {
@@ -106,18 +106,29 @@ static int piece(const ora_tensor* t, int64_t S, int64_t r, int64_t* lo, int64_t
     return 1;
 }
 
-static const ora_tensor* g_sort_base;
+/* (offset, index) pairs sort by offset; no shared state, so independent
+ * buckets can be stepped from several threads at once. */
+typedef struct {
+    int64_t offset;
+    int index;
+} ora_key;
 static int by_offset(const void* a, const void* b) {
-    int64_t x = g_sort_base[*(const int*)a].offset, y = g_sort_base[*(const int*)b].offset;
-    return (x > y) - (x < y);
+    int64_t x = ((const ora_key*)a)->offset, y = ((const ora_key*)b)->offset;
+    if (x != y) return (x > y) - (x < y);
+    return ((const ora_key*)a)->index - ((const ora_key*)b)->index;
 }
 
 /* indices of the tensors sorted by bucket offset (caller frees) */
 static int* offset_order(const ora_tensor* t, int n) {
     int* idx = (int*)malloc(sizeof(int) * (size_t)(n > 0 ? n : 1));
-    for (int i = 0; i < n; ++i) idx[i] = i;
-    g_sort_base = t;
-    qsort(idx, (size_t)n, sizeof(int), by_offset);
+    ora_key* keys = (ora_key*)malloc(sizeof(ora_key) * (size_t)(n > 0 ? n : 1));
+    for (int i = 0; i < n; ++i) {
+        keys[i].offset = t[i].offset;
+        keys[i].index = i;
+    }
+    qsort(keys, (size_t)n, sizeof(ora_key), by_offset);
+    for (int i = 0; i < n; ++i) idx[i] = keys[i].index;
+    free(keys);
     return idx;
 }
 
@@ -346,11 +357,15 @@ typedef struct {
     double lr, beta1, beta2, eps, wd;
 } ora_hparams;
 
+/* Is block b in the ascending list sel[0..nsel) (every block when sel is NULL)? */
 static int selected(int64_t b, const int64_t* sel, int64_t nsel) {
     if (!sel) return 1;
-    for (int64_t i = 0; i < nsel; ++i)
-        if (sel[i] == b) return 1;
-    return 0;
+    int64_t lo = 0, hi = nsel;
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo) / 2;
+        if (sel[mid] < b) lo = mid + 1; else hi = mid;
+    }
+    return lo < nsel && sel[lo] == b;
 }
 
 /* One step of block-wise 8-bit AdamW on rank r's shard.
@@ -360,8 +375,9 @@ static int selected(int64_t b, const int64_t* sel, int64_t nsel) {
  * grad_shard, master, m_q, v_q, param_shard: length S, shard coordinates.
  * m_scale, v_scale: one entry per block of the rank (block order above).
  * t: step number, >= 1.
- * sel / nsel: if sel is non-NULL only those block indices are processed
- * (used to check samples of very large shards); padding is then untouched.
+ * sel / nsel: if sel is non-NULL only those block indices (ascending) are
+ * processed (used to check samples of very large shards, and by callers
+ * that split the blocks over threads); padding is then untouched.
  */
 int ora_shard_step(const ora_tensor* T, int n, int m, int64_t S, int64_t r,
                    const uint16_t* const* grads, const int64_t* grad_base,

@@ -31,7 +31,8 @@ _STATUS = {0: "VE_OK", 1: "VE_ERR_INVALID_ARG", 2: "VE_ERR_LAYOUT", 3: "VE_ERR_O
 # every symbol include/ve.h declares
 EXPORTS = ("ve_plan_load", "ve_plan_free", "ve_plan_query", "ve_dbuffer_copy_in",
            "ve_shard_adam8bit_step", "ve_dbuffer_slice", "ve_dbuffer_group_op", "ve_plan_layout",
-           "ve_muon_workspace_bytes", "ve_muon_newton_schulz", "ve_gemm_bf16_nt", "ve_last_error")
+           "ve_muon_workspace_bytes", "ve_muon_newton_schulz", "ve_gemm_bf16_nt", "ve_stream_copy",
+           "ve_last_error")
 
 # ve_group_op
 GROUP_ZERO, GROUP_SCALE, GROUP_ACCUMULATE = 0, 1, 2
@@ -80,6 +81,7 @@ def lib() -> C.CDLL:
         L.ve_muon_newton_schulz.argtypes = [P, P, C.c_int64, C.c_int64, C.c_int32, C.c_float, P, C.c_int64, P]
         L.ve_gemm_bf16_nt.argtypes = [P, C.c_int64, P, C.c_int64, P, C.c_int64, P, C.c_int64, P, C.c_int64,
                                       C.c_int64, C.c_int64, C.c_int64, C.c_float, C.c_float, C.c_int32, P]
+        L.ve_stream_copy.argtypes = [P, P, C.c_int64, P]
         for name in EXPORTS[:-1]:
             getattr(L, name).restype = C.c_int
         _lib = L
@@ -189,7 +191,11 @@ class Plan:
                                         C.c_void_p(bucket.data_ptr()), _stream_handle(stream)))
 
     def step(self, rank: int, states, hparams: dict, step: int, stream=None):
-        """``ve_shard_adam8bit_step`` over a :class:`StateTable`."""
+        """``ve_shard_adam8bit_step`` over a :class:`StateTable` built for the
+        same plan and ``rank`` (its scale arrays are sized to that rank's
+        block count and its gradient tables checked for that rank's pieces)."""
+        if states.plan is not self or states.rank != rank:
+            raise ValueError("state table was built for another plan or rank")
         hp = AdamHParams(float(hparams["lr"]), float(hparams["beta1"]), float(hparams["beta2"]),
                          float(hparams["eps"]), float(hparams["weight_decay"]))
         _check(lib().ve_shard_adam8bit_step(self._h, int(rank), C.c_void_p(states.table.data_ptr()),
@@ -275,6 +281,18 @@ def gemm_bf16_nt(P, Q, C=None, CT=None, D=None, alpha: float = 1.0, beta: float 
                                  M, N, K, float(alpha), float(beta), int(bool(symmetric)), _stream_handle(stream)))
 
 
+def stream_copy(dst, src, stream=None):
+    """``ve_stream_copy``: copy device tensor ``src`` into ``dst`` (same
+    number of bytes, contiguous, 16-byte aligned) -- the streaming reference."""
+    nbytes = src.numel() * src.element_size()
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst: contiguous device tensors")
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same size in bytes")
+    _check(lib().ve_stream_copy(C.c_void_p(dst.data_ptr()), C.c_void_p(src.data_ptr()), nbytes,
+                                _stream_handle(stream)))
+
+
 def plan_load(specs, fsdp_size, shard_elems, device=0) -> Plan:
     return Plan(specs, fsdp_size, shard_elems, device)
 
@@ -344,6 +362,7 @@ class StateTable:
             self.keep.append(st)
         self.table = torch.tensor(rows, dtype=torch.int64, device=device).reshape(-1)
         self.n = len(rows)
+        self.plan, self.rank = plan, int(rank)
 
     def __len__(self):
         return self.n

@@ -155,6 +155,10 @@ ve_status fail(ve_status st, const char* fmt, ...) __attribute__((format(printf,
 hipError_t launch_group(const RunArgs& r, int op, float alpha, const ve_group_operand* ops, int n_ops,
                         hipStream_t s);
 
+// Streaming copy of `vectors` 16-byte vectors with `grid` workgroups of 256
+// threads (ve_stream.hip).
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t vectors, int grid, hipStream_t s);
+
 // (threads, groups per thread) pairs instantiated for the workgroup path.
 bool wg_config_supported(int threads, int groups_per_thread);
 

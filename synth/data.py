@@ -80,18 +80,62 @@ def _torch_gen(device, seed_words):
     return g
 
 
-def device_grad(cfg: Config, layout: Layout, bucket: int, k: int, device, step: int = 0):
+# Tensors drawn together in one flat buffer: at most this many elements per
+# draw (bounds the temporaries), each tensor starting on a 256-byte boundary
+# (the GPU step takes its vector path only for 16-byte-aligned gradients).
+_FLAT_CHUNK = 1 << 28
+_FLAT_ALIGN = 128
+
+
+def device_grads(cfg: Config, layout: Layout, bucket: int, ks, device, step: int = 0):
+    """bf16 gradients (flat int16 device views) of tensors ``ks`` of one
+    bucket, drawn a few hundred million elements per launch instead of one
+    launch per tensor (a bucket of 10,000 tensors is a handful of launches).
+    Returns {k: view}; the views of one draw share one allocation."""
     import torch
-    t = layout.tensors[k]
-    g = _torch_gen(device, [cfg.seed, bucket * 1009 + step, layout.order[k], _KIND_GRAD, 7])
-    if cfg.grad_dist == "normal":
-        x = torch.randn(t.numel, generator=g, device=device, dtype=torch.float32)
-    else:
-        z = torch.randn(4, t.numel, generator=g, device=device, dtype=torch.float32)
-        x = z[0] / torch.sqrt((z[1] ** 2 + z[2] ** 2 + z[3] ** 2) / 3.0)
-        del z
-    x.mul_(cfg.grad_scale)
-    return x.to(torch.bfloat16).view(torch.int16)
+    ks = list(ks)
+    out = {}
+    limit = _FLAT_CHUNK // (4 if cfg.grad_dist != "normal" else 1)
+    i = 0
+    while i < len(ks):
+        group, total = [], 0
+        while i < len(ks):
+            n = layout.tensors[ks[i]].numel
+            pad = -n % _FLAT_ALIGN
+            if group and total + n > limit:
+                break
+            group.append((ks[i], total, n))
+            total += n + pad
+            i += 1
+        g = _torch_gen(device, [cfg.seed, bucket * 1009 + step, layout.order[group[0][0]], _KIND_GRAD, 11])
+        if cfg.grad_dist == "normal":
+            x = torch.randn(total, generator=g, device=device, dtype=torch.float32)
+        else:
+            z = torch.randn(4, total, generator=g, device=device, dtype=torch.float32)
+            x = z[0] / torch.sqrt((z[1] ** 2 + z[2] ** 2 + z[3] ** 2) / 3.0)
+            del z
+        x.mul_(cfg.grad_scale)
+        flat = x.to(torch.bfloat16).view(torch.int16)
+        del x
+        for k, o, n in group:
+            out[k] = flat[o:o + n]
+    return out
+
+
+def host_piece_grads(cfg: Config, layout: Layout, bucket: int, rank: int, step: int = 0):
+    """bf16 gradients of the pieces rank ``rank`` holds (the only gradient
+    elements its step reads), for the oracle: (grads, bases) with grads[k]
+    the uint16 bits of tensor elements [bases[k], bases[k] + len) or None.
+    Each piece has its own seeded stream, so a rank's inputs are drawn
+    without generating the whole tensors."""
+    grads, bases = [None] * len(layout.tensors), [0] * len(layout.tensors)
+    for k, lo, hi, _dst in layout.chunk_intervals(rank):
+        rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, bucket * 1009 + step, layout.order[k],
+                                                            _KIND_GRAD, rank]))
+        g = (_draw(rng, hi - lo, cfg.grad_dist) * cfg.grad_scale).astype(np.float32)
+        grads[k] = f32_to_bf16_bits(g)
+        bases[k] = lo
+    return grads, bases
 
 
 def device_master(cfg: Config, layout: Layout, bucket: int, rank: int, device, mask=None):

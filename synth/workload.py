@@ -3,13 +3,13 @@
 For each of the ``n_buckets`` identical buckets: the per-parameter bf16
 gradients of the tensors that have a piece on the rank (others are None --
 the shard step never reads them) and the rank's fp32 master shard.  Values
-come from seeded torch generators on the device.
+come from seeded torch generators on the device, a few draws per bucket.
 """
 
 from __future__ import annotations
 
 from .configs import Config
-from .data import device_grad, device_master
+from .data import device_grads, device_master
 from .layout import Layout
 
 
@@ -26,8 +26,14 @@ def device_buckets(cfg: Config, lay: Layout, rank: int, device, n_buckets: int |
     mask = torch.from_numpy(lay.valid_mask(rank)).to(device)
     out = []
     for b in range(n_buckets):
-        grads = [device_grad(cfg, lay, b, k, device, step).view(torch.int16) if k in on_rank else None
-                 for k in range(len(lay.tensors))]
+        drawn = device_grads(cfg, lay, b, sorted(on_rank), device, step)
+        grads = [drawn.get(k) for k in range(len(lay.tensors))]
         master = device_master(cfg, lay, b, rank, device, mask=mask)
         out.append((grads, master))
     return out
+
+
+def whole_bucket_grads(cfg: Config, lay: Layout, device, bucket: int = 0, step: int = 0):
+    """Every tensor's bf16 gradient of one bucket (flat int16 views)."""
+    drawn = device_grads(cfg, lay, bucket, range(len(lay.tensors)), device, step)
+    return [drawn[k] for k in range(len(lay.tensors))]

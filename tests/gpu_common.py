@@ -4,6 +4,8 @@ parity gates."""
 
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 import oracle
@@ -91,14 +93,46 @@ def bf16_of(master: np.ndarray) -> np.ndarray:
 
 
 class Tally:
-    """Accumulates code mismatches across calls (the fraction gate is global)."""
+    """Code mismatches of one workload, counted per moment array (m_q and v_q
+    apart): each array may differ by one step in at most CODE_MAX_FRAC of its
+    elements.  check() gates each array and reports the measured fractions
+    (stdout, and a line appended to $VE_PARITY_LOG when that is set)."""
 
-    def __init__(self):
-        self.elems = 0
-        self.mismatch = 0
+    KEYS = ("m_q", "v_q")
+
+    def __init__(self, name=""):
+        self.name = name
+        self.elems = {k: 0 for k in self.KEYS}
+        self.diff = {k: 0 for k in self.KEYS}
+
+    def add(self, key, d):
+        """``d``: |gpu - oracle| of one comparison's codes."""
+        self.elems[key] += int(d.size)
+        self.diff[key] += int((d != 0).sum())
+
+    @property
+    def mismatch(self):
+        return sum(self.diff.values())
+
+    def fractions(self):
+        return {k: self.diff[k] / max(self.elems[k], 1) for k in self.KEYS}
+
+    def report(self):
+        fr = self.fractions()
+        line = (f"[parity] {self.name}: m_q {self.diff['m_q']}/{self.elems['m_q']} = {fr['m_q']:.3e}, "
+                f"v_q {self.diff['v_q']}/{self.elems['v_q']} = {fr['v_q']:.3e} codes off by one "
+                f"(gate {CODE_MAX_FRAC:.0e} each)")
+        print(line, flush=True)
+        path = os.environ.get("VE_PARITY_LOG")
+        if path:
+            with open(path, "a") as fh:
+                fh.write(line + "\n")
+        return line
 
     def check(self):
-        assert self.mismatch <= CODE_MAX_FRAC * max(self.elems, 1), (self.mismatch, self.elems)
+        self.report()
+        for k in self.KEYS:
+            assert self.diff[k] <= CODE_MAX_FRAC * max(self.elems[k], 1), (self.name, k, self.diff[k], self.elems[k])
 
 
 def block_ids(lay, rank) -> np.ndarray:
@@ -155,8 +189,7 @@ def compare(got: dict, want: dict, valid: np.ndarray, lr: float, tally: Tally, w
     for key in ("m_q", "v_q"):
         d = np.abs(got[key][valid].astype(np.int16) - want[key][valid].astype(np.int16))
         assert d.size == 0 or d.max() <= 1, f"{key} differs by {d.max()} {where}"
-        tally.elems += d.size
-        tally.mismatch += int((d != 0).sum())
+        tally.add(key, d)
         assert np.array_equal(got[key][~valid], want[key][~valid]), f"{key} padding touched {where}"
     assert got["v_q"].min() >= 0
     # scales: within the fp32 evaluation bound of the moments, plus one ulp

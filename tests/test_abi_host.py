@@ -177,3 +177,19 @@ def test_muon_workspace_and_argument_checks():
     assert gm(p, 4, p, 8, None, 0, p, 8, None, 0, 8, 8, 8, 1.0, 0.0, 0, None) == ve_.VE_ERR_INVALID_ARG
     assert gm(p, 8, p, 8, None, 0, p, 8, None, 0, 8, 4, 8, 1.0, 0.0, 1, None) == ve_.VE_ERR_INVALID_ARG
     assert gm(p, 8, p, 8, p, 4, p, 8, None, 0, 8, 8, 8, 1.0, 0.5, 0, None) == ve_.VE_ERR_INVALID_ARG
+
+
+def test_stream_copy_rejects_bad_arguments_without_a_device():
+    L = ve.lib()
+    buf = C.create_string_buffer(64)
+    base = C.addressof(buf)
+    a16 = (base + 15) // 16 * 16
+    P = C.c_void_p
+    assert L.ve_stream_copy(P(a16), P(a16 + 32), 0, None) == ve.VE_OK          # empty: nothing to do
+    assert L.ve_stream_copy(P(a16), P(a16 + 32), -16, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_stream_copy(None, P(a16), 16, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_stream_copy(P(a16 + 1), P(a16 + 32), 16, None) == ve.VE_ERR_INVALID_ARG
+    assert b"multiples of 16" in L.ve_last_error()
+    assert L.ve_stream_copy(P(a16), P(a16 + 32), 24, None) == ve.VE_ERR_INVALID_ARG
+    assert L.ve_stream_copy(P(a16), P(a16 + 16), 32, None) == ve.VE_ERR_INVALID_ARG
+    assert b"overlap" in L.ve_last_error()

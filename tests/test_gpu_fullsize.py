@@ -43,28 +43,38 @@ def _block_positions(lay, rank, coord):
     return (dst + rows * t.cols + cols - lo).reshape(-1)
 
 
-@pytest.mark.parametrize("name", ["llama", "gptoss", "deepseek", "adversarial"])
-def test_full_size_sampled(name):
+# The benchmark's rank with every bucket in one call, then with two buckets:
+# the rank that straddles two tensors of different block geometry
+# (LLaMA 35: the end of `down` and rows of q; DeepSeek 42: gate/up panels
+# then down panels) and the last rank (padding at the bucket's tail).
+FULL_RANKS = [("llama", "largest"), ("gptoss", "largest"), ("deepseek", "largest"), ("adversarial", "largest"),
+              ("llama", 35), ("llama", "last"), ("gptoss", "last"), ("deepseek", 42), ("deepseek", "last"),
+              ("adversarial", "last")]
+
+
+@pytest.mark.parametrize("name,which", FULL_RANKS)
+def test_full_size_sampled(name, which):
     import torch
     import ragged_shard_optimizer_amd as ve
     cfg, lay = layout_of(name)
-    rank = lay.largest_rank()
+    rank = lay.largest_rank() if which == "largest" else (lay.fsdp - 1 if which == "last" else which)
     spec, m, S = lay.spec_array(), lay.fsdp, lay.shard
     hp = hp32()
     plan = ve.Plan(spec, m, S, device=0)
     _, nb, _ = plan.query(rank)
-    _say(f"[gpu] full-size {name}: rank {rank}, {cfg.n_buckets} buckets, S={S}, blocks={nb}")
-    buckets = device_buckets(cfg, lay, rank, DEV)
+    n_buckets = cfg.n_buckets if which == "largest" else min(2, cfg.n_buckets)
+    _say(f"[gpu] full-size {name}: rank {rank}, {n_buckets} buckets, S={S}, blocks={nb}")
+    buckets = device_buckets(cfg, lay, rank, DEV, n_buckets=n_buckets)
     states = [ve.new_state(plan, rank, ve.grad_pointer_table(g, DEV), master) for g, master in buckets]
     table = ve.state_table(plan, rank, states)
     coords = rank_block_coords(lay, rank)
     assert len(coords) == nb
     rng = np.random.default_rng(0)
     sel = sorted({0, nb - 1} | set(rng.choice(nb, min(nb, 10), replace=False).tolist()))
-    sample_b = sorted({0, cfg.n_buckets // 2, cfg.n_buckets - 1})
+    sample_b = sorted({0, n_buckets // 2, n_buckets - 1})
     pieces = list(lay.chunk_intervals(rank))
     mask = torch.from_numpy(lay.valid_mask(rank)).to(DEV)
-    tally = Tally()
+    tally = Tally(f"full-size {name} rank {rank}")
     for t in (1, 2):
         pre = {b: _download(states[b], nb) for b in sample_b}
         _say(f"[gpu] full-size {name}: step {t}, {len(states)} states in one call")
@@ -94,8 +104,7 @@ def test_full_size_sampled(name):
                 for key in ("m_q", "v_q"):
                     d = np.abs(got[key][pos].astype(np.int16) - want[key][pos].astype(np.int16))
                     assert d.max() <= 1, (name, key, blk)
-                    tally.elems += d.size
-                    tally.mismatch += int((d != 0).sum())
+                    tally.add(key, d)
                 # scales within the fp32 evaluation bound of the block's moments
                 g = (got["grad_shard"][pos].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
                 pb = pre[b]
@@ -116,10 +125,10 @@ def test_adversarial_whole_bucket_copy_in():
     moved): every tensor lands at its offset bit for bit, all padding zero."""
     import torch
     import ragged_shard_optimizer_amd as ve
-    from synth.data import device_grad
+    from synth.workload import whole_bucket_grads
     cfg, lay = layout_of("adversarial")
     plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
-    grads = [device_grad(cfg, lay, 0, k, DEV) for k in range(len(lay.tensors))]
+    grads = whole_bucket_grads(cfg, lay, DEV)
     gt = ve.grad_pointer_table(grads, DEV)
     bucket = torch.full((lay.bucket_elems,), -1, dtype=torch.int16, device=DEV)
     _say(f"[gpu] whole-bucket copy-in: {lay.bucket_elems} elements")

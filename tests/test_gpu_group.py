@@ -186,3 +186,20 @@ def test_group_empty_batch_is_a_no_op():
     plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
     assert ve.lib().ve_dbuffer_group_op(plan.handle, 0, ZERO, 0.0, None, 0, None) == ve.VE_OK
     plan.close()
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 16 * 1000 + 16, (1 << 24) + 48])
+def test_stream_copy_bit_exact(nbytes):
+    """The streaming reference copies every byte (grid-stride tail included)
+    and nothing past the end."""
+    import torch
+    import ragged_shard_optimizer_amd as ve
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(nbytes)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda:0", generator=g)
+    dst = torch.full((nbytes + 4096,), 0xA5, dtype=torch.uint8, device="cuda:0")
+    print(f"[gpu] stream copy {nbytes} bytes", flush=True)
+    ve.stream_copy(dst[:nbytes], src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src)
+    assert bool((dst[nbytes:] == 0xA5).all())

@@ -178,6 +178,11 @@ def test_one_step_within_propagated_bound(shape):
     assert not bad.any(), (int(bad.sum()), float(np.abs(got - want).max()))
 
 
+NS5_ULPS = 8.0
+NS5_FROB = 1.5e-2
+NS5_SV = 0.012
+
+
 @pytest.mark.parametrize("shape", [(256, 512), (512, 256), (300, 300), (128, 1000)])
 def test_five_steps(shape):
     Gb = _bf16_host(shape, 13)
@@ -185,13 +190,28 @@ def test_five_steps(shape):
     _say(f"[gpu] newton-schulz steps=5 {shape}")
     got = _run_ns(Gb, 5)
     want = muon.newton_schulz(G, steps=5)
-    rel = np.linalg.norm(got - want) / np.linalg.norm(want)
-    assert rel <= 0.03, rel
+    # The elementwise bound of one step compounds absolute values and is
+    # useless after two steps.  Both sides round at the same points; they
+    # differ only where the fp32 accumulation order flips a rounding, and
+    # the iteration amplifies such a flip by at most max|p'(s)| ~ 3.8 per
+    # step on [0, 1.2].  Gate: the largest difference within NS5_ULPS bf16
+    # ulps of the largest entry, and the relative Frobenius difference within
+    # NS5_FROB.  Measured on MI355X over the four shapes below: 2-5 ulps and
+    # 2.7e-3-7.4e-3, singular values 0.005-0.007 from the exact iteration's
+    # (the oracle's own bf16 result: 0.008); the gates are about 1.6-2x those.
+    top = float(np.abs(want).max())
+    ulps = float(np.abs(got - want).max() / ulp_bf16(np.array([top]))[0])
+    rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
     # the structure of the result: the singular values follow the quintic map
     exact = muon.newton_schulz(G, steps=5, rounding=False)
     s_got = np.linalg.svd(got, compute_uv=False)
     s_ex = np.linalg.svd(exact, compute_uv=False)
-    assert np.abs(s_got - s_ex).max() <= 0.05
+    sv = float(np.abs(s_got - s_ex).max())
+    _say(f"[gpu] newton-schulz steps=5 {shape}: max diff {ulps:.2f} bf16 ulps of max|X|, rel Frobenius {rel:.2e}, "
+         f"singular values within {sv:.4f} of the exact iteration")
+    assert ulps <= NS5_ULPS, ulps
+    assert rel <= NS5_FROB, rel
+    assert sv <= NS5_SV, sv
 
 
 # Split products: a product whose last round of 256 x 256 tiles is short

@@ -70,7 +70,7 @@ SMALL = ["toy_mix", "toy_r1", "toy_r4", "toy_r16", "toy_tile", "llama_mini", "ll
 @pytest.mark.parametrize("name", SMALL)
 def test_step_parity(name):
     cfg, lay = layout_of(name)
-    tally = Tally()
+    tally = Tally(name)
     _run_parity(cfg, lay, _ranks(lay), cfg.steps if name.startswith("toy") else 2, tally)
     tally.check()
 
@@ -128,7 +128,7 @@ def test_copy_in_rejects_short_gradient_per_table():
 @pytest.mark.parametrize("case", list(EDGE))
 def test_edge_layouts(case):
     cfg, lay = EDGE[case]()
-    tally = Tally()
+    tally = Tally(cfg.name)
     _run_parity(cfg, lay, list(range(lay.fsdp)), 3, tally)
     tally.check()
 
@@ -153,7 +153,7 @@ def test_workgroup_access_forms(shape, monkeypatch):
     lay = plan_p0(FORM_TENSORS, 2)
     assert max(t.block_rows * t.block_cols for t in FORM_TENSORS) <= 4 * shape[0] * shape[1]
     cfg = Config("forms", list(FORM_TENSORS), fsdp=2, grad_scale=1e-3, steps=2)
-    tally = Tally()
+    tally = Tally(cfg.name)
     _run_parity(cfg, lay, [0, 1], 2, tally)
     tally.check()
 
@@ -167,7 +167,7 @@ def test_rank_with_two_block_shapes(name, rank):
     cfg, lay = layout_of(name)
     sizes = {lay.tensors[k].block_rows * lay.tensors[k].cols for k, *_ in lay.chunk_intervals(rank)}
     assert len([b for b in sizes if b > 256]) > 1  # two workgroup-path block sizes
-    tally = Tally()
+    tally = Tally(cfg.name)
     _run_parity(cfg, lay, [rank], 2, tally)
     tally.check()
 
@@ -175,7 +175,7 @@ def test_rank_with_two_block_shapes(name, rank):
 def test_one_element_blocks_codes_exact():
     # 1-element blocks: every nonzero code is +-127 and the scale is |m|/127
     cfg, lay = _explicit("unit", [TensorDef("a", 999, 1, 1, 1), TensorDef("b", 21, 17, 1, 1)], [0, 1008], 2, 768)
-    tally = Tally()
+    tally = Tally(cfg.name)
     _run_parity(cfg, lay, [0, 1], 3, tally)
     assert tally.mismatch == 0
 
@@ -241,4 +241,31 @@ def test_batched_states_equal_single_calls_and_deterministic():
         a, b = p.download(), q.download()
         for k in a:
             assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+    plan.close()
+
+
+def test_state_table_of_another_rank_or_plan_is_rejected():
+    """A state table is sized and checked for one plan and rank; the binding
+    refuses it for another before anything is launched (the outputs keep
+    their canaries)."""
+    import torch
+    ve = _ve()
+    cfg, lay = layout_of("toy_mix")
+    plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
+    other = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
+    prob = RankProblem(ve, cfg, lay, plan, 1)
+    prob.set_grads(1)
+    before = prob.download()
+    hp = hp32()
+    with pytest.raises(ValueError, match="another plan or rank"):
+        plan.step(2, prob.table, hp, 1)
+    with pytest.raises(ValueError, match="another plan or rank"):
+        other.step(1, prob.table, hp, 1)
+    torch.cuda.synchronize()
+    after = prob.download()
+    for k in before:
+        assert np.array_equal(before[k].view(np.uint8), after[k].view(np.uint8)), k
+    plan.step(1, prob.table, hp, 1)  # the matching plan and rank still run
+    torch.cuda.synchronize()
+    other.close()
     plan.close()

@@ -98,3 +98,77 @@ def test_flop_count():
     assert muon.flops(2, 3, steps=1) == 44
     assert muon.flops(3, 2, steps=1) == 44
     assert muon.flops(8192, 28672) == 5 * (3 * 8192 ** 2 * 28672 + 8192 ** 3)
+
+
+# ---------------------------------------------------------------------------
+# Pins of the product oracle gemm_nt (C = bf16(alpha P Q^T + beta D)): values
+# the arithmetic fixes without reusing numpy's matmul as the reference.
+
+def _int_mat(shape, seed, lo=-4, hi=4):
+    return np.random.default_rng(seed).integers(lo, hi + 1, size=shape).astype(np.float64)
+
+
+def _loops_nt(P, Q):
+    """Plain triple loop over Python integers: C[i][j] = sum_k P[i][k] Q[j][k]."""
+    M, K = P.shape
+    N = Q.shape[0]
+    return [[sum(int(P[i, k]) * int(Q[j, k]) for k in range(K)) for j in range(N)] for i in range(M)]
+
+
+def test_gemm_nt_small_integers_exact():
+    # entries in [-4, 4] and K = 16 keep every sum within +-256: exact in
+    # fp32 and in bf16, so C must equal the integer product; M, N, K distinct
+    # so a transposed operand cannot line up
+    P, Q = _int_mat((5, 16), 11), _int_mat((7, 16), 12)
+    want = np.array(_loops_nt(P, Q), dtype=np.float64)
+    got = muon.gemm_nt(P, Q)
+    assert got.shape == (5, 7)
+    assert np.array_equal(got, want)
+
+
+def test_gemm_nt_identity_and_permutation():
+    X = muon.bf16_bits_to_f64(muon.f64_to_bf16_bits(_rand((6, 9), 13)))
+    assert np.array_equal(muon.gemm_nt(X, np.eye(9)), X)          # X I^T = X
+    perm = np.array([3, 0, 8, 1, 7, 2, 6, 4, 5])
+    Pm = np.zeros((9, 9))
+    Pm[np.arange(9), perm] = 1.0                                    # row j picks column perm[j]
+    got = muon.gemm_nt(X, Pm)
+    assert np.array_equal(got, X[:, perm])                          # C[i, j] = X[i, perm[j]]
+    assert np.array_equal(muon.gemm_nt(np.eye(6), X.T.copy()), X)  # I (X^T)^T = X
+
+
+def test_gemm_nt_alpha_beta_powers_of_two():
+    P, Q = _int_mat((4, 4), 21, -2, 2), _int_mat((3, 4), 22, -2, 2)
+    D = _int_mat((4, 3), 23, -4, 4)
+    base = np.array(_loops_nt(P, Q), dtype=np.float64)   # integers in [-16, 16]
+    for alpha, beta in ((0.125, 4.0), (-2.0, 0.5), (1.0, 0.0), (0.0, -1.0)):
+        want = alpha * base + beta * D
+        # every result is a multiple of 1/8 below 32 in magnitude: at most 8
+        # significant bits, so bf16 holds it exactly and no rounding happens
+        assert np.all(want * 8 == np.round(want * 8)) and np.abs(want).max() < 32
+        assert np.array_equal(muon.gemm_nt(P, Q, D, alpha=alpha, beta=beta), want), (alpha, beta)
+    # without D, beta plays no part
+    assert np.array_equal(muon.gemm_nt(P, Q, None, alpha=2.0, beta=3.0), 2.0 * base)
+
+
+def test_gemm_nt_double_rounding_decides():
+    # exact 1 + 2^-8 + 2^-30: fp64 -> fp32 gives the bf16 tie 1 + 2^-8 (the
+    # 2^-30 is below half an fp32 ulp), which rounds to even: 1.0.  A single
+    # rounding straight to bf16 would give 1 + 2^-7.
+    P = np.array([[1.0, 2.0 ** -8, 2.0 ** -30]])
+    Q = np.ones((1, 3))
+    assert muon.gemm_nt(P, Q)[0, 0] == 1.0
+    # 1 + 2^-8 + 2^-20 survives fp32 above the tie and rounds up
+    P2 = np.array([[1.0, 2.0 ** -8, 2.0 ** -20]])
+    assert muon.gemm_nt(P2, Q)[0, 0] == 1.0 + 2.0 ** -7
+    # the same through beta * D: D = 2^-30, beta 1
+    C = muon.gemm_nt(np.array([[1.0, 2.0 ** -8]]), np.ones((1, 2)), D=np.array([[2.0 ** -30]]), beta=1.0)
+    assert C[0, 0] == 1.0
+
+
+def test_gemm_nt_alpha_is_taken_in_fp32():
+    # alpha = 0.1 reaches the kernel as the fp32 number nearest 0.1
+    P = np.array([[1.0]])
+    a32 = float(np.float32(0.1))
+    want = muon._bf16_round(np.array([a32]))[0]
+    assert muon.gemm_nt(P, P, alpha=0.1)[0, 0] == want
