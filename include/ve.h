@@ -251,6 +251,19 @@ ve_status ve_muon_workspace_bytes(int64_t rows, int64_t cols, int64_t* bytes);
 ve_status ve_muon_newton_schulz(const uint16_t* G, uint16_t* out, int64_t rows, int64_t cols, int32_t steps,
                                 float eps, void* workspace, int64_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * iteration as ve_muon_newton_schulz, bit for bit, with its workspace in a
+ * static device array of 200 MiB that each GPU the library runs on holds
+ * until the process ends (so any matrix whose ve_muon_workspace_bytes is at
+ * most 200 MiB, e.g. 2048 x 7168 or 3,400 x 3,400).  G and out as above; the
+ * call allocates nothing.  Calls on one GPU share that array: calls that
+ * overlap on one GPU (two streams or threads) race.  Errors: as
+ * ve_muon_newton_schulz; a larger workspace need gives VE_ERR_UNSUPPORTED;
+ * no current device gives VE_ERR_DEVICE. */
+ve_status ve_muon_newton_schulz_noalloc(const uint16_t* G, uint16_t* out, int64_t rows, int64_t cols,
+                                        int32_t steps, float eps, void* stream);
+
 /* The product kernel the iteration runs on: C = bf16(alpha * P Q^T + beta * D)
  * with P (M x K), Q (N x K), D and C (M x N) and CT = C^T (N x M), all bf16
  * row-major device arrays with leading dimensions ld* (>= the row length).

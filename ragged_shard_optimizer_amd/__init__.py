@@ -31,8 +31,8 @@ _STATUS = {0: "VE_OK", 1: "VE_ERR_INVALID_ARG", 2: "VE_ERR_LAYOUT", 3: "VE_ERR_O
 # every symbol include/ve.h declares
 EXPORTS = ("ve_plan_load", "ve_plan_free", "ve_plan_query", "ve_dbuffer_copy_in",
            "ve_shard_adam8bit_step", "ve_dbuffer_slice", "ve_dbuffer_group_op", "ve_plan_layout",
-           "ve_muon_workspace_bytes", "ve_muon_newton_schulz", "ve_gemm_bf16_nt", "ve_stream_copy",
-           "ve_last_error")
+           "ve_muon_workspace_bytes", "ve_muon_newton_schulz", "ve_muon_newton_schulz_noalloc",
+           "ve_gemm_bf16_nt", "ve_stream_copy", "ve_last_error")
 
 # ve_group_op
 GROUP_ZERO, GROUP_SCALE, GROUP_ACCUMULATE = 0, 1, 2
@@ -82,6 +82,7 @@ def lib() -> C.CDLL:
         L.ve_gemm_bf16_nt.argtypes = [P, C.c_int64, P, C.c_int64, P, C.c_int64, P, C.c_int64, P, C.c_int64,
                                       C.c_int64, C.c_int64, C.c_int64, C.c_float, C.c_float, C.c_int32, P]
         L.ve_stream_copy.argtypes = [P, P, C.c_int64, P]
+        L.ve_muon_newton_schulz_noalloc.argtypes = [P, P, C.c_int64, C.c_int64, C.c_int32, C.c_float, P]
         for name in EXPORTS[:-1]:
             getattr(L, name).restype = C.c_int
         _lib = L
@@ -259,6 +260,20 @@ def muon_newton_schulz(G, out, steps: int = 5, eps: float = 1e-7, workspace=None
     _require_buffer(workspace, need, 1, "workspace")
     _check(lib().ve_muon_newton_schulz(_ptr_of(G), _ptr_of(out), rows, cols, int(steps), float(eps),
                                        _ptr_of(workspace), workspace.numel(), _stream_handle(stream)))
+    return out
+
+
+def muon_newton_schulz_noalloc(G, out, steps: int = 5, eps: float = 1e-7, stream=None):
+    """``ve_muon_newton_schulz_noalloc``: as :func:`muon_newton_schulz`, with
+    the library's static device scratch as the workspace (nothing is
+    allocated, here or in the library)."""
+    if G.dim() != 2 or tuple(out.shape) != tuple(G.shape):
+        raise ValueError("G and out: 2-D tensors of the same shape")
+    rows, cols = G.shape
+    _require_buffer(G, rows * cols, 2, "G")
+    _require_buffer(out, rows * cols, 2, "out")
+    _check(lib().ve_muon_newton_schulz_noalloc(_ptr_of(G), _ptr_of(out), rows, cols, int(steps), float(eps),
+                                               _stream_handle(stream)))
     return out
 
 

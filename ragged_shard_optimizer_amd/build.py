@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build", "libve.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("ve_host.cpp", "ve_planner.cpp", "ve_muon_host.cpp", "ve_kernels.hip", "ve_group.hip",
-                                           "ve_muon.hip", "ve_stream.hip")]
+                                           "ve_muon.hip", "ve_stream.hip",
+                                           "ve_muon_static.hip")]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
