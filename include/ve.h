@@ -191,6 +191,25 @@ typedef struct {
 ve_status ve_dbuffer_group_op(const ve_plan* plan, int32_t rank, int32_t op, float alpha,
                               const ve_group_operand* operands, int32_t n_operands, void* stream);
 
+/* Launch options (process-wide tuning knobs for measurement; the defaults
+ * are the measured choices).  Each option starts from its environment
+ * variable, read once, else from its default:
+ *   "wg_threads" (VE_WG_THREADS, 0) and "wg_gpt" (VE_WG_GPT, 0): pin the
+ *       step's workgroup shape (threads, 4-element groups per thread) for
+ *       blocks that fit it, when that shape is built; 0 = chosen by block size;
+ *   "gemm_split" (VE_GEMM_SPLIT, 1): 0 = never cut a product's short last
+ *       round of tiles along K;
+ *   "gemm_cfg" (VE_GEMM_CFG, -1): pin a product configuration (0, 2: register
+ *       staged 128^2 / 256^2 tiles; 6, 9: direct-to-LDS 4 waves of 128^2 /
+ *       8 waves of 128x64); -1 = chosen by shape;
+ *   "gemm_xcd" (VE_GEMM_XCD, 1): 0 = plain tile order instead of the
+ *       XCD-aware one.
+ * ve_set_option changes a value for every later call of the process
+ * (calls already queued are unaffected); ve_get_option reads it.  Errors:
+ * an unknown name or a NULL value pointer gives VE_ERR_INVALID_ARG. */
+ve_status ve_set_option(const char* name, int64_t value);
+ve_status ve_get_option(const char* name, int64_t* value);
+
 /* Streaming reference (not part of the method): copy `bytes` bytes from
  * `src` to `dst` (device pointers, both 16-byte aligned, bytes a multiple
  * of 16, not overlapping) with 16-byte non-temporal accesses on `stream`.

@@ -32,7 +32,7 @@ _STATUS = {0: "VE_OK", 1: "VE_ERR_INVALID_ARG", 2: "VE_ERR_LAYOUT", 3: "VE_ERR_O
 EXPORTS = ("ve_plan_load", "ve_plan_free", "ve_plan_query", "ve_dbuffer_copy_in",
            "ve_shard_adam8bit_step", "ve_dbuffer_slice", "ve_dbuffer_group_op", "ve_plan_layout",
            "ve_muon_workspace_bytes", "ve_muon_newton_schulz", "ve_muon_newton_schulz_noalloc",
-           "ve_gemm_bf16_nt", "ve_stream_copy", "ve_last_error")
+           "ve_gemm_bf16_nt", "ve_stream_copy", "ve_set_option", "ve_get_option", "ve_last_error")
 
 # ve_group_op
 GROUP_ZERO, GROUP_SCALE, GROUP_ACCUMULATE = 0, 1, 2
@@ -82,6 +82,8 @@ def lib() -> C.CDLL:
         L.ve_gemm_bf16_nt.argtypes = [P, C.c_int64, P, C.c_int64, P, C.c_int64, P, C.c_int64, P, C.c_int64,
                                       C.c_int64, C.c_int64, C.c_int64, C.c_float, C.c_float, C.c_int32, P]
         L.ve_stream_copy.argtypes = [P, P, C.c_int64, P]
+        L.ve_set_option.argtypes = [C.c_char_p, C.c_int64]
+        L.ve_get_option.argtypes = [C.c_char_p, P]
         L.ve_muon_newton_schulz_noalloc.argtypes = [P, P, C.c_int64, C.c_int64, C.c_int32, C.c_float, P]
         for name in EXPORTS[:-1]:
             getattr(L, name).restype = C.c_int
@@ -306,6 +308,37 @@ def stream_copy(dst, src, stream=None):
         raise ValueError("src and dst must have the same size in bytes")
     _check(lib().ve_stream_copy(C.c_void_p(dst.data_ptr()), C.c_void_p(src.data_ptr()), nbytes,
                                 _stream_handle(stream)))
+
+
+def set_option(name: str, value: int):
+    """``ve_set_option``: a process-wide launch option (see include/ve.h)."""
+    _check(lib().ve_set_option(name.encode(), int(value)))
+
+
+def get_option(name: str) -> int:
+    v = C.c_int64()
+    _check(lib().ve_get_option(name.encode(), C.byref(v)))
+    return v.value
+
+
+class options:
+    """Context manager: set launch options for a block of code and restore
+    the previous values afterwards, e.g. ``with options(gemm_split=0): ...``."""
+
+    def __init__(self, **values):
+        self.values = values
+        self.saved = {}
+
+    def __enter__(self):
+        for k, v in self.values.items():
+            self.saved[k] = get_option(k)
+            set_option(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self.saved.items():
+            set_option(k, v)
+        return False
 
 
 def plan_load(specs, fsdp_size, shard_elems, device=0) -> Plan:

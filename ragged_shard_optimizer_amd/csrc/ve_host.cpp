@@ -11,11 +11,13 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -27,7 +29,38 @@ using namespace ve;
 
 namespace {
 thread_local std::string g_err;
+
+struct OptionDef {
+    const char* name;
+    const char* env;
+    int64_t dflt;
+};
+constexpr OptionDef kOptionDefs[kNumOptions] = {
+    {"wg_threads", "VE_WG_THREADS", 0}, {"wg_gpt", "VE_WG_GPT", 0}, {"gemm_split", "VE_GEMM_SPLIT", 1},
+    {"gemm_cfg", "VE_GEMM_CFG", -1},    {"gemm_xcd", "VE_GEMM_XCD", 1},
+};
+std::atomic<int64_t> g_options[kNumOptions];
+std::once_flag g_options_once;
+
+void seed_options() {
+    for (int i = 0; i < kNumOptions; ++i) {
+        const char* e = std::getenv(kOptionDefs[i].env);
+        g_options[i].store(e ? std::atoll(e) : kOptionDefs[i].dflt, std::memory_order_relaxed);
+    }
+}
+
+int option_index(const char* name) {
+    if (!name) return -1;
+    for (int i = 0; i < kNumOptions; ++i)
+        if (std::strcmp(name, kOptionDefs[i].name) == 0) return i;
+    return -1;
+}
 }  // namespace
+
+int64_t ve::option(Option o) {
+    std::call_once(g_options_once, seed_options);
+    return g_options[o].load(std::memory_order_relaxed);
+}
 
 ve_status ve::fail(ve_status st, const char* fmt, ...) {
     char buf[512];
@@ -293,26 +326,6 @@ int64_t set_inline(StepArgs& a, const RankTables& rt, const HostWork& w, size_t 
     return a.work.total;
 }
 
-// Launch-shape knobs for measurement, read from the environment once per
-// process (the defaults are the measured choices): VE_WG_THREADS and
-// VE_WG_GPT pin the workgroup shape of the step.
-struct Tuning {
-    int wg_threads = 0, wg_gpt = 0;
-};
-
-const Tuning& tuning() {
-    static const Tuning t = [] {
-        Tuning r;
-        auto num = [](const char* name, int& v) {
-            if (const char* e = std::getenv(name)) v = std::atoi(e);
-        };
-        num("VE_WG_THREADS", r.wg_threads);
-        num("VE_WG_GPT", r.wg_gpt);
-        return r;
-    }();
-    return t;
-}
-
 // Workgroup path shape: threads and 4-element groups per thread for blocks
 // of up to `groups` groups (each run of segments with one shape is a launch).
 // Measured on MI355X over the model workloads:
@@ -324,12 +337,13 @@ const Tuning& tuning() {
 //   larger: 1024 threads x 14 / 16;
 //   up to 2,048 groups: the largest workgroup that gives each thread at
 //     least 6 groups (fewer leave the per-block prologue exposed), else 256.
-// VE_WG_THREADS / VE_WG_GPT override it (launch-shape tuning).
+// The options wg_threads / wg_gpt pin it (launch-shape tuning) for blocks
+// that fit the pinned shape.
 void wg_shape(int32_t groups, int& threads, int& gpt) {
-    const Tuning& tn = tuning();
-    if (tn.wg_threads > 0 && tn.wg_gpt > 0) {
-        threads = tn.wg_threads;
-        gpt = tn.wg_gpt;
+    const int64_t ot = option(kOptWgThreads), og = option(kOptWgGpt);
+    if (ot > 0 && og > 0 && ot <= kWgMaxThreads && og <= 64) {
+        threads = (int)ot;
+        gpt = (int)og;
         if (wg_config_supported(threads, gpt) && (int64_t)threads * gpt >= groups) return;
     }
     auto fit = [&](int t, int min_g, int& g) {
@@ -395,6 +409,22 @@ ve_status launch_status(hipError_t e, const char* what) {
 extern "C" {
 
 const char* ve_last_error(void) { return g_err.c_str(); }
+
+ve_status ve_set_option(const char* name, int64_t value) {
+    const int i = option_index(name);
+    if (i < 0) return fail(VE_ERR_INVALID_ARG, "unknown option %s", name ? name : "(NULL)");
+    std::call_once(g_options_once, seed_options);
+    g_options[i].store(value, std::memory_order_relaxed);
+    return VE_OK;
+}
+
+ve_status ve_get_option(const char* name, int64_t* value) {
+    const int i = option_index(name);
+    if (i < 0) return fail(VE_ERR_INVALID_ARG, "unknown option %s", name ? name : "(NULL)");
+    if (!value) return fail(VE_ERR_INVALID_ARG, "value is NULL");
+    *value = option((Option)i);
+    return VE_OK;
+}
 
 ve_status ve_plan_load(const ve_tensor_spec* specs, int32_t n_tensors, int32_t fsdp_size, int64_t shard_elems,
                        int32_t device, ve_plan** out) {
@@ -627,6 +657,8 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
     }
     if (rt.small.prefix.back() > 0) {
         set_work(a, *plan, rt.small);
+        // few segments: hand them to the kernel inline (no table lookups)
+        if (rt.small.seg_idx.size() <= (size_t)kInlineSegs) set_inline(a, rt, rt.small, 0, rt.small.seg_idx.size());
         if (fuse_pad) a.pad = run_args(*plan, rt.pad);  // the padding fill rides along
         if ((st = launch_status(launch_step_small(a, n_states, s), "small-block step")) != VE_OK) return st;
         a.pad = RunArgs{};

@@ -147,6 +147,18 @@ hipError_t launch_runs_copy(const RunArgs& r, const uint16_t* const* grad_ptrs, 
 hipError_t launch_runs_pad(const RunArgs& r, const ve_shard_state* states, int n_states,
                            hipStream_t s);
 
+// Process-wide launch options (ve_set_option / ve_get_option; each starts
+// from its environment variable, read once, else its default).
+enum Option : int {
+    kOptWgThreads = 0,  // "wg_threads" (VE_WG_THREADS): step workgroup threads, 0 = by block size
+    kOptWgGpt,          // "wg_gpt" (VE_WG_GPT): step groups per thread, 0 = by block size
+    kOptGemmSplit,      // "gemm_split" (VE_GEMM_SPLIT): 0 = never split a product's short last round
+    kOptGemmCfg,        // "gemm_cfg" (VE_GEMM_CFG): product configuration, -1 = by shape
+    kOptGemmXcd,        // "gemm_xcd" (VE_GEMM_XCD): 0 = plain tile order instead of the XCD-aware one
+    kNumOptions
+};
+int64_t option(Option o);
+
 // Record the thread-local message ve_last_error() returns; returns `st`.
 ve_status fail(ve_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 

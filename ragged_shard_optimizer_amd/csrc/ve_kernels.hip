@@ -632,6 +632,19 @@ __global__ void __launch_bounds__(256) k_runs(RunArgs r, const uint16_t* const* 
     run_tile(r, blockIdx.x, grad_ptrs, out, states, mode, blockIdx.y);
 }
 
+// Code of a one-element block whose absmax is a = max(0, |x|) (the element
+// itself).  For a > 0 the general path computes rint(x * fl(127 / a)) and
+// clamps it: fl(127 / a) is within a relative 2^-24 of 127 / a and the
+// product adds one more rounding of the same size, so x * fl(127 / a) lies
+// within 127 * 2^-23 of +-127 (or is +-inf where 127 / a overflows); rint
+// and the clamp then give exactly +-127, with the sign of x.  For a == 0 (x
+// a signed zero, or a NaN that the max dropped) the general formula, with
+// the reciprocal 0, is kept as it is.  So the result equals the general
+// path's without its correctly rounded division.
+__device__ __forceinline__ uint32_t unit_code(float x, float a) {
+    return a > 0.f ? (x < 0.f ? 0x81u : 0x7fu) : quant_byte(x, 0.f);
+}
+
 // One-element blocks (kUnit): a lane takes one chunk, i.e. kSmallChunk
 // consecutive blocks, each with its own pair of scales.  A block's maximum is
 // its element's own |m1| (v1), so no lane exchange is needed.  Every value
@@ -682,10 +695,8 @@ __device__ __forceinline__ void step_unit(const StepArgs& a, const Seg& sg, cons
         const float d = __builtin_fmaf(__builtin_amdgcn_sqrtf(v1), a.sc.inv_sqrt_bc2, a.sc.eps);
         const float u = m1 * __builtin_amdgcn_rcpf(d);
         mst[i] = __builtin_fmaf(-a.sc.step_size, u, mst[i] * a.sc.decay);
-        const float im = am > 0.f ? 127.0f / am : 0.f;
-        const float iv = av > 0.f ? 127.0f / av : 0.f;
-        qm[i >> 2] |= quant_byte(m1, im) << (8 * (i & 3));
-        qv[i >> 2] |= quant_byte(v1, iv) << (8 * (i & 3));
+        qm[i >> 2] |= unit_code(m1, am) << (8 * (i & 3));
+        qv[i >> 2] |= unit_code(v1, av) << (8 * (i & 3));
         nm[i] = am / 127.0f;
         nv[i] = av / 127.0f;
     }
@@ -708,6 +719,10 @@ __device__ __forceinline__ void step_unit(const StepArgs& a, const Seg& sg, cons
     }
 }
 
+// INLINE: the launch's segments are in the kernel arguments (at most
+// kInlineSegs of them), so a wave finds its segment without the chain of
+// dependent loads of the binary search in device memory.
+template <bool INLINE>
 __global__ void __launch_bounds__(256) k_step_small(StepArgs a) {
     if ((int64_t)blockIdx.x >= a.pad_wg0) {  // a padding tile of the same launch
         run_tile(a.pad, (int64_t)blockIdx.x - a.pad_wg0, nullptr, nullptr, a.states, 1, blockIdx.y);
@@ -719,8 +734,16 @@ __global__ void __launch_bounds__(256) k_step_small(StepArgs a) {
     const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
     if (gw >= a.work.total) return;  // whole waves; the kernel has no barrier
     int64_t local;
-    const Seg sg = find_global(a, gw, local);
-    const ve_shard_state st = a.states[blockIdx.y];
+    Seg sg;
+    if constexpr (INLINE) sg = find_inline(a, gw, local);
+    else sg = find_global(a, gw, local);
+    ve_shard_state st;
+    {
+        const uint64_t* src = reinterpret_cast<const uint64_t*>(a.states + blockIdx.y);
+        uint64_t* dst = reinterpret_cast<uint64_t*>(&st);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dst[i] = sload(src + i);
+    }
     if (sg.cls == kUnit) {
         step_unit(a, sg, st, local, lane);
         return;
@@ -1120,7 +1143,9 @@ static inline unsigned grid_x(int64_t n) { return (unsigned)n; }
 hipError_t launch_step_small(const StepArgs& a0, int n_states, hipStream_t s) {
     StepArgs a = a0;
     a.pad_wg0 = (a.work.total + 3) / 4;
-    hipLaunchKernelGGL(k_step_small, dim3(grid_x(a.pad_wg0 + a.pad.n_tiles), n_states), dim3(256), 0, s, a);
+    const dim3 grid(grid_x(a.pad_wg0 + a.pad.n_tiles), n_states);
+    if (a.n_inline > 0) hipLaunchKernelGGL(k_step_small<true>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_step_small<false>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -793,11 +793,10 @@ hipError_t launch_gemm_t(GemmArgs g, hipStream_t s) {
 // (each slice writes fp32 accumulators), and a reduce launch sums the slices
 // in order and runs the epilogue.  Only over long contractions (at least 8
 // steps per slice).  Returns the slice count (1: no split) and the number of
-// tiles launched whole.  VE_GEMM_SPLIT=0 turns it off (read at every launch).
+// tiles launched whole.  The option gemm_split = 0 turns it off.
 inline int tail_split(int64_t tiles, int64_t nk, bool has_partial, int64_t& full) {
     full = tiles;
-    const char* e = getenv("VE_GEMM_SPLIT");
-    if (!has_partial || (e && atoi(e) == 0) || nk < 16) return 1;
+    if (!has_partial || option(kOptGemmSplit) == 0 || nk < 16) return 1;
     const int64_t whole = tiles / kCUs * kCUs, tail = tiles - whole;
     if (tail == 0 || (whole > 0 && tail * 4 > kCUs)) return 1;
     const int64_t ks = std::min<int64_t>(std::min<int64_t>(kCUs / tail, nk / 8), 32);
@@ -867,15 +866,9 @@ hipError_t launch_gemm_cfg(GemmArgs g, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-// VE_GEMM_CFG (environment) pins one configuration for tuning; otherwise
-// large tiles are used when they still give every CU several tiles.
-int gemm_cfg_override() {
-    static const int idx = [] {
-        const char* e = getenv("VE_GEMM_CFG");
-        return e ? atoi(e) : -1;
-    }();
-    return idx;
-}
+// The option gemm_cfg pins one configuration for tuning; otherwise large
+// tiles are used when they still give every CU several tiles.
+int gemm_cfg_override() { return (int)option(kOptGemmCfg); }
 
 // The direct-to-LDS kernel with 8 waves of 128 x 64 where it applies (K a
 // multiple of 64, 16-byte operand rows) and the product has at least two
@@ -911,11 +904,7 @@ int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127)
 int norm_blocks() { return kNormBlocks; }
 
 hipError_t launch_gemm_nt(GemmArgs g, hipStream_t s) {
-    static const bool remap = [] {
-        const char* e = getenv("VE_GEMM_XCD");
-        return e ? atoi(e) != 0 : true;
-    }();
-    g.xcd_remap = remap;
+    g.xcd_remap = option(kOptGemmXcd) != 0;
     const int cfg = gemm_cfg_override();
     switch (cfg >= 0 ? cfg : gemm_cfg_auto(g)) {
 #define VE_GEMM_CASE(ID, BM, BN, BK, WM, WN) \

@@ -193,3 +193,15 @@ def test_stream_copy_rejects_bad_arguments_without_a_device():
     assert L.ve_stream_copy(P(a16), P(a16 + 32), 24, None) == ve.VE_ERR_INVALID_ARG
     assert L.ve_stream_copy(P(a16), P(a16 + 16), 32, None) == ve.VE_ERR_INVALID_ARG
     assert b"overlap" in L.ve_last_error()
+
+
+def test_options_round_trip_and_restore():
+    before = {k: ve.get_option(k) for k in ("wg_threads", "wg_gpt", "gemm_split", "gemm_cfg", "gemm_xcd")}
+    assert before["gemm_split"] in (0, 1) and before["gemm_xcd"] in (0, 1)
+    with ve.options(wg_threads=512, gemm_split=0):
+        assert ve.get_option("wg_threads") == 512 and ve.get_option("gemm_split") == 0
+    assert {k: ve.get_option(k) for k in before} == before
+    L = ve.lib()
+    assert L.ve_set_option(b"no_such_option", 1) == ve.VE_ERR_INVALID_ARG
+    assert b"unknown option" in L.ve_last_error()
+    assert L.ve_get_option(b"wg_gpt", None) == ve.VE_ERR_INVALID_ARG

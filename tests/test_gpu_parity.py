@@ -147,14 +147,15 @@ FORM_TENSORS = [
 
 
 @pytest.mark.parametrize("shape", [(256, 8), (512, 4), (1024, 2), (1024, 8), (512, 16)])
-def test_workgroup_access_forms(shape, monkeypatch):
-    monkeypatch.setenv("VE_WG_THREADS", str(shape[0]))
-    monkeypatch.setenv("VE_WG_GPT", str(shape[1]))
+def test_workgroup_access_forms(shape):
+    ve = _ve()
     lay = plan_p0(FORM_TENSORS, 2)
     assert max(t.block_rows * t.block_cols for t in FORM_TENSORS) <= 4 * shape[0] * shape[1]
     cfg = Config("forms", list(FORM_TENSORS), fsdp=2, grad_scale=1e-3, steps=2)
     tally = Tally(cfg.name)
-    _run_parity(cfg, lay, [0, 1], 2, tally)
+    with ve.options(wg_threads=shape[0], wg_gpt=shape[1]):
+        assert (ve.get_option("wg_threads"), ve.get_option("wg_gpt")) == shape
+        _run_parity(cfg, lay, [0, 1], 2, tally)
     tally.check()
 
 
