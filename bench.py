@@ -420,14 +420,21 @@ def _workload_alg(workload, buckets=None):
     return alg, nbk, nv, nb, lay.shard
 
 
-def _step_dispatches(rows, name_key, grid_key):
+def _grid(r):
+    """Work-items of a dispatch (counter rows give Grid_Size, trace rows X/Y/Z)."""
+    if "Grid_Size" in r:
+        return int(r["Grid_Size"])
+    return int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+
+
+def _step_dispatches(rows):
     """The step-kernel rows of the launch that covers every bucket: kernels
     named k_step_*, at the largest grid among them."""
-    st = [r for r in rows if "k_step" in r[name_key]]
+    st = [r for r in rows if "k_step" in r["Kernel_Name"]]
     if not st:
         raise SystemExit("no k_step_* kernel in the profile")
-    big = max(int(r[grid_key]) for r in st)
-    return [r for r in st if int(r[grid_key]) == big]
+    big = max(_grid(r) for r in st)
+    return [r for r in st if _grid(r) == big]
 
 
 def summarize_counters(args):
@@ -449,8 +456,8 @@ def summarize_counters(args):
 
     fx, fc = calib(f_rows)
     wx, wc = calib(w_rows)
-    fs = _step_dispatches(f_rows, "Kernel_Name", "Grid_Size")
-    ws = _step_dispatches(w_rows, "Kernel_Name", "Grid_Size")
+    fs = _step_dispatches(f_rows)
+    ws = _step_dispatches(w_rows)
     kernel = fs[0]["Kernel_Name"]
     fk = statistics.mean(float(r["Counter_Value"]) for r in fs)
     wk = statistics.mean(float(r["Counter_Value"]) for r in ws)
@@ -472,11 +479,48 @@ def summarize_counters(args):
     base = os.path.join(ROOT, "profiles", f"shard_step_{args.workload}")
     with open(base + "_hbm_counters.txt", "w") as fh:
         fh.write("\n".join(txt) + "\n")
+    summarize_group_counters(args, f_rows, w_rows, fx, wx, fc, wc, copy_kib, nbk, nv, S)
     with open(base + "_traffic.json", "w") as fh:
         json.dump({"kernel": kernel, "kernel_source_hash": h, "hbm_bytes_per_launch": rb + wb, "read_bytes": rb,
                    "write_bytes": wb, "alg_bytes_per_launch": float(alg), "fetch_factor": fx, "write_factor": wx,
                    "summary": f"profiles/shard_step_{args.workload}_hbm_counters.txt"}, fh, indent=1)
     print("\n".join(txt))
+
+
+def summarize_group_counters(args, f_rows, w_rows, fx, wx, fc, wc, copy_kib, nbk, nv, S):
+    """The DBuffer group operations' HBM bytes per launch, when the counter
+    runs included them (all buckets' rank chunks per launch)."""
+    import statistics
+    kinds = {"zero": "k_group<0>", "scale": "k_group<1>", "accumulate": "k_group<2>"}
+    if not any(kinds["zero"] in r["Kernel_Name"] for r in f_rows):
+        return
+    h = kernel_source_hash(GROUP_SOURCES)
+    out = [f"# HBM traffic of the DBuffer group operations, {args.workload} workload, all buckets' rank chunks "
+           "per launch (rocprofv3 --pmc)", f"kernel sources hash: {h}", "",
+           "commands (run from the repository root on the GPU box), one pass per counter:",
+           "  " + args.command_fetch, "  " + args.command_write, "",
+           f"calibration: FETCH_SIZE x {fx:.4f}, WRITE_SIZE x {wx:.4f} (the streaming copy of {copy_kib:.0f} KiB "
+           f"reads {fc:.1f} / {wc:.1f} KiB)", ""]
+    names, hb, ab = {}, {}, {}
+    for op, key in kinds.items():
+        fr = [r for r in f_rows if key in r["Kernel_Name"]]
+        wr = [r for r in w_rows if key in r["Kernel_Name"]]
+        if not fr or not wr:
+            continue
+        rb = statistics.mean(float(r["Counter_Value"]) for r in fr) * fx * 1024
+        wb = statistics.mean(float(r["Counter_Value"]) for r in wr) * wx * 1024
+        per = GROUP_BYTES[op]
+        alg = nbk * (S * per if op == "zero" else per * nv + GROUP_PAD_BYTES * (S - nv))
+        names[op], hb[op], ab[op] = fr[0]["Kernel_Name"], rb + wb, float(alg)
+        out += [f"{op}: {fr[0]['Kernel_Name']} ({len(fr)} / {len(wr)} dispatches)",
+                f"  HBM bytes per launch: read {rb / 1e9:.4f} GB + write {wb / 1e9:.4f} GB = {(rb + wb) / 1e9:.4f} GB; "
+                f"algorithmic {alg / 1e9:.4f} GB -> measured / algorithmic = {(rb + wb) / alg:.4f}", ""]
+    base = os.path.join(ROOT, "profiles", f"dbuffer_group_{args.workload}")
+    with open(base + "_hbm_counters.txt", "w") as fh:
+        fh.write("\n".join(out).rstrip() + "\n")
+    with open(base + "_traffic.json", "w") as fh:
+        json.dump({"kernels": names, "kernel_source_hash": h, "hbm_bytes_per_launch": hb, "alg_bytes_per_launch": ab,
+                   "summary": f"profiles/dbuffer_group_{args.workload}_hbm_counters.txt"}, fh, indent=1)
 
 
 def summarize_trace(args):
@@ -485,7 +529,7 @@ def summarize_trace(args):
     import statistics
     stats = _csv_rows(os.path.join(args.trace_dir, "run_kernel_stats.csv"))
     trace = _csv_rows(os.path.join(args.trace_dir, "run_kernel_trace.csv"))
-    st = _step_dispatches(trace, "Kernel_Name", "Grid_Size")
+    st = _step_dispatches(trace)
     kernel = st[0]["Kernel_Name"]
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in st]
     avg = statistics.mean(durs)
