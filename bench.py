@@ -245,8 +245,9 @@ def time_muon(torch, ve, dev, rows=8192, cols=28672, steps=3, warmup=1, name="LL
 
 def time_planner(ve, sizes=(64, 256, 1024)):
     """The structure-aware planner (host) on the models the pages evaluate it
-    on: whole-model padding and planning time per FSDP size, each distinct
-    bucket planned once."""
+    on, per FSDP size: whole-model padding and planning time with one bucket
+    per layer (each distinct bucket planned once), and with the layers
+    grouped into buckets by ve_plan_buckets."""
     import numpy as np
     from synth.models import MODELS, PLANNER_GRANULARITIES
     out = {}
@@ -268,9 +269,20 @@ def time_planner(ve, sizes=(64, 256, 1024)):
                     alloc += m * S
                     lb_pad += m * lb - total
                     lb_alloc += m * lb
+                secs = time.perf_counter() - t0
+                units = [np.array([[t.rows, t.cols, t.block_rows] for t in b], dtype=np.int64) for b in buckets]
+                t1 = time.perf_counter()
+                grouped = ve.plan_buckets(units, m)
+                gsecs = time.perf_counter() - t1
+                total = sum(int((u[:, 0] * u[:, 1]).sum()) for u in units)
+                galloc = sum(m * S for *_, S in grouped)
                 out[f"{name} rows/unit {g} fsdp {m}"] = {
-                    "padding_pct": round(100 * pad / alloc, 4), "lower_bound_pct": round(100 * lb_pad / lb_alloc, 4),
-                    "seconds": round(time.perf_counter() - t0, 4)}
+                    "per_layer_padding_pct": round(100 * pad / alloc, 4),
+                    "per_layer_lower_bound_pct": round(100 * lb_pad / lb_alloc, 4),
+                    "per_layer_seconds": round(secs, 4),
+                    "grouped_padding_pct": round(100 * (galloc - total) / galloc, 4),
+                    "grouped_buckets": len(grouped), "layer_buckets": len(buckets),
+                    "grouped_seconds": round(gsecs, 4)}
     log(f"[bench] planner: {len(out)} model/granularity/FSDP cases")
     return out
 

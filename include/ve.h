@@ -243,6 +243,28 @@ ve_status ve_stream_copy(void* dst, const void* src, int64_t bytes, void* stream
 ve_status ve_plan_layout(ve_tensor_spec* specs, int32_t n_tensors, int32_t fsdp_size, int64_t align,
                          int64_t* shard_elems, int64_t* lower_bound);
 
+/* Grouping of a model's tensors into buckets (talk notes, "2. Structure-
+ * aware planning algorithm": RaggedShard tensors are grouped into
+ * communication buffers; Dutch summary, "2B").  Host only.  specs[n_tensors]
+ * lists the model's tensors in model order (rows, cols, block_rows read;
+ * offset written); unit_of[k] numbers the wrapper unit (e.g. the decoder
+ * layer) tensor k belongs to, 0, 1, 2, ... in tensor order.  A bucket is a
+ * run of consecutive units, laid out by the rules of ve_plan_layout; a
+ * dynamic program over the split points picks the runs that minimise,
+ * first, the summed padding above `tolerance` (a fraction of each bucket),
+ * then the number of buckets, largest first.  A run holds at most
+ * `max_units` units and, when it holds several, at most twice the elements
+ * of the largest unit.  Outputs: bucket_of[k] (bucket of tensor k),
+ * specs[k].offset (offset inside its bucket), shard_elems[b] (S of bucket
+ * b; the caller provides one entry per unit), *n_buckets.  Errors: NULL
+ * arguments, n_tensors < 1, fsdp_size < 1, align outside [1, 2^20],
+ * max_units < 1, tolerance outside [0, 1), a unit numbering that is not
+ * 0, 1, 2, ... or a non-positive shape give VE_ERR_INVALID_ARG; sizes
+ * beyond 2^52 / fsdp_size elements give VE_ERR_UNSUPPORTED. */
+ve_status ve_plan_buckets(ve_tensor_spec* specs, const int32_t* unit_of, int32_t n_tensors, int32_t fsdp_size,
+                          int64_t align, int32_t max_units, double tolerance, int32_t* bucket_of,
+                          int64_t* shard_elems, int32_t* n_buckets);
+
 /* Muon's Newton-Schulz orthogonalisation of one gathered 2-D matrix, the
  * dense work of the root rank in distributed Muon (talk notes, "Case study:
  * 8-bit Adam and distributed Muon": the full matrix is gathered on one rank,

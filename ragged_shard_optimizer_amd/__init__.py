@@ -30,7 +30,7 @@ _STATUS = {0: "VE_OK", 1: "VE_ERR_INVALID_ARG", 2: "VE_ERR_LAYOUT", 3: "VE_ERR_O
 
 # every symbol include/ve.h declares
 EXPORTS = ("ve_plan_load", "ve_plan_free", "ve_plan_query", "ve_dbuffer_copy_in",
-           "ve_shard_adam8bit_step", "ve_dbuffer_slice", "ve_dbuffer_group_op", "ve_plan_layout",
+           "ve_shard_adam8bit_step", "ve_dbuffer_slice", "ve_dbuffer_group_op", "ve_plan_layout", "ve_plan_buckets",
            "ve_muon_workspace_bytes", "ve_muon_newton_schulz", "ve_muon_newton_schulz_noalloc",
            "ve_gemm_bf16_nt", "ve_stream_copy", "ve_set_option", "ve_get_option", "ve_last_error")
 
@@ -77,6 +77,7 @@ def lib() -> C.CDLL:
         L.ve_dbuffer_slice.argtypes = [P, C.c_int32, C.c_int32, P, P, P]
         L.ve_dbuffer_group_op.argtypes = [P, C.c_int32, C.c_int32, C.c_float, P, C.c_int32, P]
         L.ve_plan_layout.argtypes = [P, C.c_int32, C.c_int32, C.c_int64, P, P]
+        L.ve_plan_buckets.argtypes = [P, P, C.c_int32, C.c_int32, C.c_int64, C.c_int32, C.c_double, P, P, P]
         L.ve_muon_workspace_bytes.argtypes = [C.c_int64, C.c_int64, P]
         L.ve_muon_newton_schulz.argtypes = [P, P, C.c_int64, C.c_int64, C.c_int32, C.c_float, P, C.c_int64, P]
         L.ve_gemm_bf16_nt.argtypes = [P, C.c_int64, P, C.c_int64, P, C.c_int64, P, C.c_int64, P, C.c_int64,
@@ -233,6 +234,36 @@ def plan_layout(shapes, fsdp_size: int, align: int = 16):
     _check(lib().ve_plan_layout(arr, len(sh), int(fsdp_size), int(align), C.byref(S), C.byref(lb)))
     specs = np.array([[a.rows, a.cols, a.block_rows, a.block_cols, a.offset] for a in arr], dtype=np.int64)
     return specs, S.value, lb.value
+
+
+def plan_buckets(units, fsdp_size: int, align: int = 16, max_units: int = 4, tolerance: float = 0.005):
+    """``ve_plan_buckets``: ``units`` is a list (model order) of int arrays
+    ``[n_k, >=3]`` of (rows, cols, block_rows[, block_cols]), one per wrapper
+    unit.  Returns a list of buckets, each ``(first_unit, end_unit, specs,
+    S)`` with ``specs`` int64 ``[n, 5]`` (rows, cols, block_rows,
+    block_cols, offset) of the bucket's tensors, ready for :class:`Plan`."""
+    shapes = [np.asarray(u, dtype=np.int64).reshape(-1, np.asarray(u).shape[-1]) for u in units]
+    if not shapes or any(sh.ndim != 2 or sh.shape[1] < 3 or len(sh) < 1 for sh in shapes):
+        raise ValueError("units: a non-empty list of [n, >=3] arrays of (rows, cols, block_rows[, block_cols])")
+    allsh = np.concatenate([sh[:, :3] for sh in shapes])
+    bcols = np.concatenate([sh[:, 3] if sh.shape[1] > 3 else sh[:, 1] for sh in shapes])
+    unit_of = np.concatenate([np.full(len(sh), i, dtype=np.int32) for i, sh in enumerate(shapes)])
+    n = len(allsh)
+    arr = (TensorSpec * n)()
+    for i in range(n):
+        arr[i] = TensorSpec(int(allsh[i, 0]), int(allsh[i, 1]), int(allsh[i, 2]), int(bcols[i]), 0)
+    bucket_of = np.zeros(n, dtype=np.int32)
+    S = np.zeros(len(shapes), dtype=np.int64)
+    nb = C.c_int32()
+    _check(lib().ve_plan_buckets(arr, C.c_void_p(unit_of.ctypes.data), n, int(fsdp_size), int(align),
+                                 int(max_units), float(tolerance), C.c_void_p(bucket_of.ctypes.data),
+                                 C.c_void_p(S.ctypes.data), C.byref(nb)))
+    specs = np.array([[a.rows, a.cols, a.block_rows, a.block_cols, a.offset] for a in arr], dtype=np.int64)
+    out = []
+    for b in range(nb.value):
+        idx = np.nonzero(bucket_of == b)[0]
+        out.append((int(unit_of[idx[0]]), int(unit_of[idx[-1]]) + 1, specs[idx], int(S[b])))
+    return out
 
 
 def muon_workspace_bytes(rows: int, cols: int) -> int:

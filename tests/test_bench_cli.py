@@ -27,8 +27,10 @@ def test_planner_leg_reports_padding_at_or_above_its_bound():
     out = bench.time_planner(ve, sizes=(64, 1024))
     assert len(out) == 2 * 2 * 2  # two models, two granularities, two FSDP sizes
     for key, v in out.items():
-        assert 0.0 <= v["lower_bound_pct"] <= v["padding_pct"] < 100.0, key
-        assert v["seconds"] < 5.0, key
+        assert 0.0 <= v["per_layer_lower_bound_pct"] <= v["per_layer_padding_pct"] < 100.0, key
+        assert 0.0 <= v["grouped_padding_pct"] < 3.0, key
+        assert v["grouped_buckets"] <= v["layer_buckets"]
+        assert v["per_layer_seconds"] < 5.0 and v["grouped_seconds"] < 5.0, key
 
 
 def test_group_op_byte_counts():
