@@ -21,18 +21,30 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ve_oracle.c")
-_LIB = os.path.join(_HERE, "_build", "libve_oracle.so")
+_PLAIN = os.path.join(_HERE, "_build", "libve_oracle.so")
+_SAN = os.path.join(_HERE, "_build", "libve_oracle_san.so")
+# VE_SANITIZED=1 selects the AddressSanitizer + UBSan build (same runtime as
+# the library's sanitized build, so both can share one process)
+_LIB = _SAN if os.environ.get("VE_SANITIZED") == "1" else _PLAIN
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (no FMA contraction, IEEE semantics)."""
-    if force or not os.path.exists(_LIB):
-        os.makedirs(os.path.dirname(_LIB), exist_ok=True)
-        tmp = _LIB + f".tmp{os.getpid()}"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off",
-                               "-fno-fast-math", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (no FMA contraction, IEEE semantics); with
+    ``sanitize``, with clang and AddressSanitizer + UBSan."""
+    out = _SAN if sanitize else _PLAIN
+    if force or not os.path.exists(out):
+        os.makedirs(os.path.dirname(out), exist_ok=True)
+        tmp = out + f".tmp{os.getpid()}"
+        if sanitize:
+            cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off",
+                   "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+                   "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        else:
+            cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off",
+                   "-fno-fast-math", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, out)
+    return out
 
 
 class _Tensor(C.Structure):
@@ -52,7 +64,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
+            build(sanitize=_LIB == _SAN)
         L = C.CDLL(_LIB)
         P = C.c_void_p
         L.ora_last_error.restype = C.c_char_p

@@ -22,7 +22,8 @@ import weakref
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "_build", "libve.so")
+# VE_SANITIZED=1 selects the host-sanitized build (build --sanitize)
+LIB_PATH = os.path.join(_HERE, "_build", "libve_san.so" if os.environ.get("VE_SANITIZED") == "1" else "libve.so")
 
 VE_OK, VE_ERR_INVALID_ARG, VE_ERR_LAYOUT, VE_ERR_OOM, VE_ERR_DEVICE, VE_ERR_UNSUPPORTED = range(6)
 _STATUS = {0: "VE_OK", 1: "VE_ERR_INVALID_ARG", 2: "VE_ERR_LAYOUT", 3: "VE_ERR_OOM",
