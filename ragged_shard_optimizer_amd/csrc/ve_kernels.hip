@@ -498,6 +498,13 @@ __device__ __forceinline__ void load_master_fast(float (&mst)[4], const FastRsrc
     mst[3] = __int_as_float(v.w);
 }
 
+// The gradient-slice copy is stored here, or in phase 2 when LATE.
+__device__ __forceinline__ void store_grad_copy(const In<4>& x, const FastRsrc& f, const ChunkAddr& a) {
+    __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int32_t)x.g[0], (int32_t)x.g[1]}, f.grad_shard, (int)a.v2,
+                                          (int)a.s2, kBufNT);
+}
+
+template <bool LATE>
 __device__ __forceinline__ void phase1_fast_k(const In<4>& x, float (&mst)[4], const FastRsrc& f,
                                               const ChunkAddr& a, float sm, float sv, const StepScalars& sc,
                                               float& am, float& av, float (&km)[4], float (&kv)[4]) {
@@ -506,20 +513,22 @@ __device__ __forceinline__ void phase1_fast_k(const In<4>& x, float (&mst)[4], c
     const i32x4 mv = {__float_as_int(mst[0]), __float_as_int(mst[1]), __float_as_int(mst[2]), __float_as_int(mst[3])};
     __builtin_amdgcn_raw_buffer_store_b128(mv, f.master, (int)a.v4, (int)a.s4, kBufNT);
     __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int32_t)p0, (int32_t)p1}, f.param, (int)a.v2, (int)a.s2, kBufNT);
-    __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int32_t)x.g[0], (int32_t)x.g[1]}, f.grad_shard, (int)a.v2,
-                                          (int)a.s2, kBufNT);
+    if constexpr (!LATE) store_grad_copy(x, f, a);
 }
 
+template <bool LATE>
 __device__ __forceinline__ void phase1_fast(const In<4>& x, float (&mst)[4], const FastRsrc& f,
                                             const ChunkAddr& a, float sm, float sv, const StepScalars& sc,
                                             float& am, float& av) {
     float km[4], kv[4];
-    phase1_fast_k(x, mst, f, a, sm, sv, sc, am, av, km, kv);
+    phase1_fast_k<LATE>(x, mst, f, a, sm, sv, sc, am, av, km, kv);
 }
 
 // Phase 2 from moments kept in registers since phase 1.
-__device__ __forceinline__ void phase2_fast_kept(const float (&km)[4], const float (&kv)[4], const FastRsrc& f,
-                                                 const ChunkAddr& a, float im, float iv) {
+template <bool LATE>
+__device__ __forceinline__ void phase2_fast_kept(const In<4>& x, const float (&km)[4], const float (&kv)[4],
+                                                 const FastRsrc& f, const ChunkAddr& a, float im, float iv) {
+    if constexpr (LATE) store_grad_copy(x, f, a);
     uint32_t qm = 0, qv = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -530,8 +539,10 @@ __device__ __forceinline__ void phase2_fast_kept(const float (&km)[4], const flo
     __builtin_amdgcn_raw_buffer_store_b32((int32_t)qv, f.v_q, (int)a.v1, (int)a.s1, kBufNT);
 }
 
+template <bool LATE>
 __device__ __forceinline__ void phase2_fast(const In<4>& x, const FastRsrc& f, const ChunkAddr& a, float sm,
                                             float sv, float im, float iv, const StepScalars& sc) {
+    if constexpr (LATE) store_grad_copy(x, f, a);
     uint32_t qm[1], qv[1];
     quantise(x, sm, sv, im, iv, sc, qm, qv);
     __builtin_amdgcn_raw_buffer_store_b32((int32_t)qm[0], f.m_q, (int)a.v1, (int)a.s1, kBufNT);
@@ -976,6 +987,17 @@ struct WgKeep {
     static constexpr bool value = VE_KEEP_MOMENTS == 1 || (VE_KEEP_MOMENTS == 2 && T == 1024 && GPT <= 8);
 };
 
+// Whether a FAST block stores its gradient-slice copy in phase 2 (from the
+// held input registers) instead of in phase 1.  Same bytes, moved from the
+// store-heavy phase 1 into the VALU-bound phase 2.
+#ifndef VE_LATE_COPY
+#define VE_LATE_COPY 2  // 0: never, 1: always, 2: 1024-thread shapes of up to 8 groups
+#endif
+template <int T, int GPT>
+struct WgLateCopy {
+    static constexpr bool value = VE_LATE_COPY == 1 || (VE_LATE_COPY == 2 && T == 1024 && GPT <= 8);
+};
+
 // One block: phase 1 (inputs already issued), the absmax reduction, phase 2.
 template <int T, int GPT, int MA, int MODE>
 __device__ __forceinline__ void wg_block(In<kWgChunk> (&x)[GPT], float (&mst)[MA + 1][kWgChunk],
@@ -983,6 +1005,7 @@ __device__ __forceinline__ void wg_block(In<kWgChunk> (&x)[GPT], float (&mst)[MA
                                          const StepScalars& sc) {
     constexpr int CH = kWgChunk;
     constexpr bool KEEP = MODE != kWgGeneral && WgKeep<T, GPT>::value;
+    constexpr bool LATE = WgLateCopy<T, GPT>::value;
     const int tid = threadIdx.x;
     const int nch = it.geo.nchunks;
     float am = 0.f, av = 0.f;
@@ -993,10 +1016,10 @@ __device__ __forceinline__ void wg_block(In<kWgChunk> (&x)[GPT], float (&mst)[MA
         if constexpr (MODE != kWgGeneral) {
             if (c + MA < GPT) load_master_fast(mst[(c + MA) % (MA + 1)], it.fb, wg_addr<T, GPT, MODE>(it, off, c + MA));
             if constexpr (KEEP)
-                phase1_fast_k(x[c], mst[c % (MA + 1)], it.fb, wg_addr<T, GPT, MODE>(it, off, c), it.sm, it.sv, sc, am,
+                phase1_fast_k<LATE>(x[c], mst[c % (MA + 1)], it.fb, wg_addr<T, GPT, MODE>(it, off, c), it.sm, it.sv, sc, am,
                               av, km[c], kv[c]);
             else
-                phase1_fast(x[c], mst[c % (MA + 1)], it.fb, wg_addr<T, GPT, MODE>(it, off, c), it.sm, it.sv, sc, am, av);
+                phase1_fast<LATE>(x[c], mst[c % (MA + 1)], it.fb, wg_addr<T, GPT, MODE>(it, off, c), it.sm, it.sv, sc, am, av);
             // keep the groups in program order (hoisting later groups' work
             // would run out of registers)
             __builtin_amdgcn_sched_barrier(0);
@@ -1038,13 +1061,13 @@ __device__ __forceinline__ void wg_block(In<kWgChunk> (&x)[GPT], float (&mst)[MA
     for (int c = 0; c < GPT; ++c) {
         const int ci = wg_slot_chunk<T, GPT>(it, c);
         if constexpr (KEEP) {
-            phase2_fast_kept(km[c], kv[c], it.fb, wg_addr<T, GPT, MODE>(it, off, c), im, iv);
+            phase2_fast_kept<LATE>(x[c], km[c], kv[c], it.fb, wg_addr<T, GPT, MODE>(it, off, c), im, iv);
             __builtin_amdgcn_sched_barrier(0);
             continue;
         }
         make_opaque(x[c]);
         if constexpr (MODE != kWgGeneral) {
-            phase2_fast(x[c], it.fb, wg_addr<T, GPT, MODE>(it, off, c), it.sm, it.sv, im, iv, sc);
+            phase2_fast<LATE>(x[c], it.fb, wg_addr<T, GPT, MODE>(it, off, c), it.sm, it.sv, im, iv, sc);
             __builtin_amdgcn_sched_barrier(0);
         } else if (ci < nch) {
             const ChunkPos cp = chunk_pos<CH>(it.geo, it.sg.shard_base, ci);
