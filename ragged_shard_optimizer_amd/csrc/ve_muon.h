@@ -28,6 +28,7 @@ struct GemmArgs {
     int32_t tiles_n;                 // set by the launcher
     bool vec_p, vec_q, vec_d, vec_c, vec_ct;  // rows allow 16-byte accesses
     bool xcd_remap;                  // set by the launcher: XCD-aware tile order
+    bool sym_blocked;                // set by the launcher: symmetric tiles in 8 x 8 super-blocks (with the remap)
     // Tail split (set by the launcher): a launch covers logical tiles from
     // tile_base; with ksplit > 1 each tile's K steps are cut into ksplit
     // slices whose fp32 accumulators go to `partial` (the caller's scratch,

@@ -108,10 +108,42 @@ __device__ __forceinline__ u32x4 load8(const uint16_t* base, int64_t ld, int64_t
 // contiguous slice of the tile sequence.  A full product walks groups of 8
 // tile rows column by column, so the operand panels a slice touches are few
 // and stay in its L2.  A symmetric product launches only the tiles on or
-// above the diagonal, row by row, so every slice carries the same work.
-// Tile (ti, tj) of logical tile index t: the upper triangle row by row for
-// symmetric products, else groups of 8 tile rows walked column by column.
+// above the diagonal: with the remap in 8 x 8 super-blocks (so that a slice
+// touches few panels), else row by row.
+// Tile (ti, tj) of logical tile index t.
 __device__ __forceinline__ void tile_at(const GemmArgs& g, int t, int& ti, int& tj) {
+    if (g.symmetric && g.sym_blocked) {
+        // super-blocks of 8 x 8 tiles on or above the diagonal, row by row;
+        // inside one, tiles row by row (the triangle on the diagonal)
+        constexpr int SB = 8;
+        const int n = g.tiles_n, ns = (n + SB - 1) / SB;
+        int rem = t;
+        for (int I = 0; I < ns; ++I) {
+            const int ri = min(SB, n - SB * I);
+            for (int J = I; J < ns; ++J) {
+                const int cj = min(SB, n - SB * J);
+                const int cnt = I == J ? ri * (ri + 1) / 2 : ri * cj;
+                if (rem < cnt) {
+                    if (I < J) {
+                        ti = SB * I + rem / cj;
+                        tj = SB * J + rem % cj;
+                        return;
+                    }
+                    int r = 0;
+                    while (rem >= ri - r) {
+                        rem -= ri - r;
+                        ++r;
+                    }
+                    ti = SB * I + r;
+                    tj = SB * I + r + rem;
+                    return;
+                }
+                rem -= cnt;
+            }
+        }
+        ti = tj = 0;  // not reached: t < tiles_total
+        return;
+    }
     if (g.symmetric) {
         // row r of the upper triangle holds tiles_n - r tiles
         int r = 0, rem = t;
@@ -711,9 +743,38 @@ __device__ __forceinline__ void dma_epilogue(const GemmArgs& g, f32x16 (&acc)[CF
 }
 
 // Partial sums of squares of n bf16 values, in fp64, one per workgroup.
+// Per-workgroup partial sums of squares in fp64, in a fixed order (the same
+// grid every call).  Aligned inputs stream as 16-byte vectors (eight bf16),
+// four in flight per thread.
+__device__ __forceinline__ double sumsq8(double s, u32x4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const double lo = (double)__uint_as_float(w[i] << 16), hi = (double)__uint_as_float(w[i] & 0xffff0000u);
+        s = __builtin_fma(lo, lo, s);
+        s = __builtin_fma(hi, hi, s);
+    }
+    return s;
+}
+
 __global__ void __launch_bounds__(256) k_sumsq(const uint16_t* x, int64_t n, double* partial) {
     double s = 0.0;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t stride = (int64_t)gridDim.x * 256, t0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    int64_t tail0 = 0;
+    if (((uintptr_t)x & 15) == 0) {
+        const u32x4* xv = (const u32x4*)x;
+        const int64_t nv = n / 8;
+        int64_t i = t0;
+        for (; i + 3 * stride < nv; i += 4 * stride) {
+            const u32x4 a = __builtin_nontemporal_load(xv + i), b = __builtin_nontemporal_load(xv + i + stride);
+            const u32x4 c = __builtin_nontemporal_load(xv + i + 2 * stride);
+            const u32x4 d = __builtin_nontemporal_load(xv + i + 3 * stride);
+            s = sumsq8(sumsq8(sumsq8(sumsq8(s, a), b), c), d);
+        }
+        for (; i < nv; i += stride) s = sumsq8(s, __builtin_nontemporal_load(xv + i));
+        tail0 = nv * 8;
+    }
+    for (int64_t i = tail0 + t0; i < n; i += stride) {
         const double v = (double)from_bf16(x[i]);
         s = __builtin_fma(v, v, s);
     }
@@ -764,6 +825,52 @@ __global__ void __launch_bounds__(256) k_normalize(const uint16_t* G, int64_t ro
     for (int cc = tr; cc < 64; cc += 4) {
         const int64_t c = c0 + cc, r = r0 + tc;
         if (c < cols && r < rows) transposed[c * rows + r] = tileT[cc][tc];
+    }
+}
+
+// The same with 16-byte accesses, when rows and cols are multiples of 8 and
+// every pointer is 16-byte aligned: a thread scales 8 consecutive elements of
+// a row (one vector load, one vector store straight), and writes 8
+// consecutive elements of a transposed row gathered from the LDS tile.
+__global__ void __launch_bounds__(256) k_normalize_v(const uint16_t* G, int64_t rows, int64_t cols,
+                                                     const float* scale_p, uint16_t* straight, uint16_t* transposed,
+                                                     int tiles_c) {
+    __shared__ uint32_t tile[64][33];  // 64 rows of 64 bf16 (pairs), padded against bank conflicts
+    const float scale = *scale_p;
+    const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * 64, c0 = (int64_t)(blockIdx.x % tiles_c) * 64;
+    const int t = threadIdx.x, cc = (t & 7) * 8;
+    for (int rr = t >> 3; rr < 64; rr += 32) {
+        const int64_t r = r0 + rr, c = c0 + cc;
+        u32x4 h = u32x4{0, 0, 0, 0};
+        if (r < rows && c < cols) {
+            const u32x4 v = __builtin_nontemporal_load((const u32x4*)(G + r * cols + c));
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                o[i] = pack_bf16x2(__uint_as_float(w[i] << 16) * scale, __uint_as_float(w[i] & 0xffff0000u) * scale);
+            h = u32x4{o[0], o[1], o[2], o[3]};
+            if (straight) *(u32x4*)(straight + r * cols + c) = h;
+        }
+        tile[rr][cc / 2 + 0] = h.x;
+        tile[rr][cc / 2 + 1] = h.y;
+        tile[rr][cc / 2 + 2] = h.z;
+        tile[rr][cc / 2 + 3] = h.w;
+    }
+    if (!transposed) return;
+    __syncthreads();
+    const int orr = (t & 7) * 8;  // tile rows gathered: transposed columns r0 + orr ..
+    for (int oc = t >> 3; oc < 64; oc += 32) {
+        const int64_t c = c0 + oc, r = r0 + orr;
+        if (c >= cols || r >= rows) continue;
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t a = tile[orr + 2 * i][oc >> 1], b = tile[orr + 2 * i + 1][oc >> 1];
+            const uint32_t ha = (oc & 1) ? a >> 16 : a & 0xffffu, hb = (oc & 1) ? b >> 16 : b & 0xffffu;
+            o[i] = ha | (hb << 16);
+        }
+        *(u32x4*)(transposed + c * rows + r) = u32x4{o[0], o[1], o[2], o[3]};
     }
 }
 
@@ -905,6 +1012,7 @@ int norm_blocks() { return kNormBlocks; }
 
 hipError_t launch_gemm_nt(GemmArgs g, hipStream_t s) {
     g.xcd_remap = option(kOptGemmXcd) != 0;
+    g.sym_blocked = g.xcd_remap;
     const int cfg = gemm_cfg_override();
     switch (cfg >= 0 ? cfg : gemm_cfg_auto(g)) {
 #define VE_GEMM_CASE(ID, BM, BN, BK, WM, WN) \
@@ -935,8 +1043,13 @@ hipError_t launch_normalize(const uint16_t* G, int64_t rows, int64_t cols, const
                             uint16_t* transposed, hipStream_t s) {
     const int tiles_c = (int)((cols + 63) / 64);
     const int64_t tiles = ((rows + 63) / 64) * tiles_c;
-    hipLaunchKernelGGL(k_normalize, dim3((unsigned)tiles), dim3(256), 0, s, G, rows, cols, scale, straight,
-                       transposed, tiles_c);
+    auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+    if (rows % 8 == 0 && cols % 8 == 0 && a16(G) && a16(straight) && a16(transposed))
+        hipLaunchKernelGGL(k_normalize_v, dim3((unsigned)tiles), dim3(256), 0, s, G, rows, cols, scale, straight,
+                           transposed, tiles_c);
+    else
+        hipLaunchKernelGGL(k_normalize, dim3((unsigned)tiles), dim3(256), 0, s, G, rows, cols, scale, straight,
+                           transposed, tiles_c);
     return hipGetLastError();
 }
 
