@@ -384,9 +384,16 @@ constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 // outstanding (expcnt and lgkmcnt left unconstrained).
 constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
 
-template <int WM_, int WN_, int BK_, int STAGES_>
+#ifndef VE_QWRITE_SUBSTEP
+#define VE_QWRITE_SUBSTEP 2  // sub-step of a step whose start writes the next step's Q to LDS
+#endif
+// QST: Q is staged through registers (global -> VGPR two steps ahead ->
+// LDS one step ahead, two LDS stages) while P keeps the direct LDS DMA in
+// STAGES stages, so that both operands' loads have two steps to land.
+template <int WM_, int WN_, int BK_, int STAGES_, bool QST_ = false>
 struct DmaCfg {
     static constexpr int BM = 256, BN = 256, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_;
+    static constexpr bool QST = QST_;
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, WAVES = WAVES_M * WAVES_N;
 #ifndef VE_EARLY_BARRIER
 #define VE_EARLY_BARRIER 1
@@ -401,7 +408,7 @@ struct DmaCfg {
     static constexpr int ROWS_PER_DMA = 1024 / (BK * 2);       // rows one wave instruction fills
     static constexpr int DMA_PER_OP = BM / ROWS_PER_DMA / WAVES;  // instructions per operand per thread
     static constexpr int STAGE_ELEMS = (BM + BN) * BK;
-    static constexpr int OP_BYTES = STAGES * STAGE_ELEMS * 2;
+    static constexpr int OP_BYTES = QST ? (STAGES * BM + 2 * BN) * BK * 2 : STAGES * STAGE_ELEMS * 2;
     static constexpr int PASS_ROWS = 64;
     static constexpr int LDC = BN + 4;
     static constexpr int SMEM = OP_BYTES > PASS_ROWS * LDC * 4 ? OP_BYTES : PASS_ROWS * LDC * 4;
@@ -414,9 +421,10 @@ struct DmaCfg {
     }
 };
 
-#define VE_DMA_CFGS(X) \
-    X(6, 128, 128, 64, 2) \
-    X(9, 128, 64, 64, 2)
+#define VE_DMA_CFGS(X)           \
+    X(6, 128, 128, 64, 2, false) \
+    X(9, 128, 64, 64, 2, false)  \
+    X(13, 128, 64, 64, 3, true)
 
 template <class CF, bool HAS_D, bool HAS_C, bool HAS_CT>
 __device__ __forceinline__ void dma_epilogue(const GemmArgs& g, f32x16 (&acc)[CF::TM][CF::TN], int ti, int tj,
@@ -475,6 +483,7 @@ __global__ void __launch_bounds__(CF::THREADS) k_gemm_nt_dma(GemmArgs g) {
                                              16, 0, 0);
         }
     };
+    if constexpr (!CF::QST) {
     auto dma_step = [&](int64_t kt) {
         uint16_t* st = ops + (int)(kt % S) * SE;
         dma_op(g.P, g.ldp, g.M, i0, st, (kbeg + kt) * BK);
@@ -581,6 +590,150 @@ __global__ void __launch_bounds__(CF::THREADS) k_gemm_nt_dma(GemmArgs g) {
                 __builtin_amdgcn_sched_group_barrier(kSchedMfma, kRestLast, 0);
             }
         }
+    }
+    } else {
+        // P: LDS DMA through a buffer resource based at the tile's first row
+        // (the MUBUF form: the compiler tracks it like an ordinary load,
+        // where the FLAT form makes it wait for every outstanding access
+        // before any use of a loaded register).  Q: each thread loads the
+        // 16-byte chunks the DMA would have written (same rows, same
+        // swizzled slots) into registers two steps ahead and writes them to
+        // LDS at the end of the step before their use.  Every step issues
+        // the same loads (past the last step they re-read valid data of the
+        // last step), so the wait counts are constants.
+        constexpr int SP = S, SQ = 2, PE = BM * BK, QE = BN * BK, DL = CF::DMA_PER_OP;
+        static_assert(SP == 3, "P stages");
+        static_assert(CF::ROWS_PER_DMA * CF::WAVES == 64 && CF::CHUNKS == 8, "one DMA round covers 64 rows");
+        uint16_t* pst = ops;            // [SP][PE]
+        uint16_t* qst = ops + SP * PE;  // [SQ][QE]
+        // Operand rows past M or N are past the end of the tile's buffer
+        // range: their loads return zeros (those outputs are never stored).
+        // Thread rows: lane row lrow of 8-row block (WAVES q + wave), whose
+        // swizzle does not depend on q; the offsets are recomputed per load
+        // from one per-lane base and a wave-uniform part.
+        const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(g.P + i0 * g.ldp), (short)0, (int)(uint32_t)((min(i0 + BM, g.M) - i0) * g.ldp * 2), 0x00020000);
+        const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(g.Q + j0 * g.ldq), (short)0, (int)(uint32_t)((min(j0 + BN, g.N) - j0) * g.ldq * 2), 0x00020000);
+        const int trow = wave * CF::ROWS_PER_DMA + lrow, tchunk = 8 * (lslot ^ CF::swz(trow));
+        const uint32_t pv0 = (uint32_t)((trow * g.ldp + tchunk) * 2), qv0 = (uint32_t)((trow * g.ldq + tchunk) * 2);
+        auto kcol = [&](int64_t kt) { return (kbeg + (kt < nk ? kt : nk - 1)) * BK; };
+        auto pstage = [&](int64_t kt) {
+            uint16_t* st = pst + (int)(kt % SP) * PE;
+            const uint32_t k2 = (uint32_t)(kcol(kt) * 2);
+#pragma unroll
+            for (int q = 0; q < DL; ++q) {
+                const int blk = CF::WAVES * q + wave;
+                uint32_t v = pv0 + k2 + (uint32_t)(q * 64 * g.ldp * 2);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    prs, (void __attribute__((address_space(3)))*)(st + blk * CF::ROWS_PER_DMA * BK), 16, (int)v, 0, 0, 0);
+            }
+        };
+        u32x4 qreg[2][DL];
+        auto qload = [&](int buf, int64_t kt) {
+            const uint32_t k2 = (uint32_t)(kcol(kt) * 2);
+#pragma unroll
+            for (int q = 0; q < DL; ++q)
+                qreg[buf][q] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, (int)(qv0 + k2 + (uint32_t)(q * 64 * g.ldq * 2)), 0, 0));
+        };
+        auto qwrite = [&](int buf, int64_t kt) {
+            uint16_t* st = qst + (int)(kt % SQ) * QE + trow * BK + lslot * 8;
+#pragma unroll
+            for (int q = 0; q < DL; ++q) *(u32x4*)(st + q * 64 * BK) = qreg[buf][q];
+        };
+        const int frow = lane & 31, fhalf = lane >> 5;
+        const int fs = CF::swz(lane & 15);
+        bf16x8 fa[2][TM], fb[2][TN];
+        auto frag = [&](int buf, int kk, int64_t kt) {
+            const uint16_t* cp = pst + (int)(kt % SP) * PE + (wr * WM + frow) * BK;
+            const uint16_t* cq = qst + (int)(kt % SQ) * QE + (wc * WN + frow) * BK;
+            const int slot = ((2 * kk + fhalf) ^ fs) * 8;
+#pragma unroll
+            for (int t = 0; t < TM; ++t) fa[buf][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)&cp[t * 32 * BK + slot]);
+#pragma unroll
+            for (int t = 0; t < TN; ++t) fb[buf][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)&cq[t * 32 * BK + slot]);
+        };
+        // Inside step kt (at its third sub-step): Q of step kt + 1 into its
+        // LDS stage, free since the barrier that ended step kt - 1 (the
+        // loads, issued two steps earlier, are complete when at most this
+        // step's 2 DL loads are younger; that also covers the P DMA of step
+        // kt + 1).  The end of step kt: every wave's LDS writes complete,
+        // then the barrier.
+        auto q_to_lds = [&](int buf, int64_t kt) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * DL));
+            qwrite(buf, kt + 1);
+        };
+        auto step_end = [&]() {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * DL) & ~0x0F00);  // and lgkmcnt(0)
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        auto mfma = [&](int buf, int a, int b) {
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][a], fb[buf][b], acc[a][b], 0, 0, 0);
+        };
+        // step kt computes from Q buffer parity qb = kt % 2 (the registers
+        // of Q(kt + 1) are in buffer qb ^ 1, those of Q(kt + 2) go to qb)
+        auto step = [&](int64_t kt, int qb) {
+            __builtin_amdgcn_sched_barrier(0);
+            pstage(kt + 2);    // into the P stage consumed at step kt - 1
+            qload(qb, kt + 2);  // Q(kt) left these registers at the end of step kt - 1
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kk = 0; kk < BK / 16; ++kk) {
+                if (kk == VE_QWRITE_SUBSTEP) q_to_lds(qb ^ 1, kt);
+                if (kk + 1 < BK / 16) frag((kk + 1) & 1, kk + 1, kt);
+                if (kk + 1 == BK / 16) {
+                    constexpr int post = TM + TN, pre = TM * TN - post;
+                    static_assert(pre >= 1, "early-barrier shape");
+#pragma unroll
+                    for (int i = 0; i < pre; ++i) mfma(kk & 1, i / TN, i % TN);
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, pre, 0);
+                    step_end();
+                    frag(0, 0, kt + 1);
+#pragma unroll
+                    for (int i = pre; i < TM * TN; ++i) mfma(kk & 1, i / TN, i % TN);
+#pragma unroll
+                    for (int i = 0; i < post; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    }
+                    continue;
+                }
+#pragma unroll
+                for (int a = 0; a < TM; ++a)
+#pragma unroll
+                    for (int b = 0; b < TN; ++b) mfma(kk & 1, a, b);
+#pragma unroll
+                for (int i = 0; i < TM + TN; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+                }
+                constexpr int kRest = TM * TN - (TM + TN);
+                if constexpr (kRest > 0) __builtin_amdgcn_sched_group_barrier(kSchedMfma, kRest, 0);
+            }
+        };
+        // prologue: Q(0), Q(1) into registers, P(0), P(1) by DMA; Q(0) to
+        // LDS; P(0) complete (only P(1) younger)
+        qload(0, 0);
+        qload(1, 1);
+        pstage(0);
+        pstage(1);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * DL));
+        qwrite(0, 0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(DL) & ~0x0F00);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        frag(0, 0, 0);
+        int64_t kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+            step(kt, 0);
+            step(kt + 1, 1);
+        }
+        if (kt < nk) step(kt, 0);
+        __builtin_amdgcn_s_waitcnt(0);  // loads past the last step land before LDS is reused
     }
     __syncthreads();
     if (g.ksplit > 1) {
@@ -958,7 +1111,11 @@ hipError_t launch_gemm_dma(GemmArgs g, hipStream_t s) {
 }
 
 template <class CF>
-bool dma_ok(const GemmArgs& g) { return g.vec_p && g.vec_q && g.K % CF::BK == 0; }
+bool dma_ok(const GemmArgs& g) {
+    // QST: a tile's P and Q rows are addressed with 32-bit byte offsets
+    return g.vec_p && g.vec_q && g.K % CF::BK == 0 &&
+           (!CF::QST || std::max(g.ldp, g.ldq) * 2 * CF::BM < (int64_t(1) << 31));
+}
 
 template <class CF>
 hipError_t launch_gemm_cfg(GemmArgs g, hipStream_t s) {
@@ -991,7 +1148,9 @@ int gemm_cfg_auto(const GemmArgs& g) {
     const int64_t active = g.symmetric ? tm * (tm + 1) / 2 : tm * tn;
     const bool dma = g.vec_p && g.vec_q && g.K % 64 == 0;
     if (!dma) return active >= 2 * kCUs ? 2 : 0;
-    if (active >= 2 * kCUs) return 9;
+    // the staged-Q form where its 32-bit row offsets reach, else the plain one
+    const int big = dma_ok<DmaCfg<128, 64, 64, 3, true>>(g) ? 13 : 9;
+    if (active >= 2 * kCUs) return big;
     const int64_t nk = g.K / 64;
     auto rounds = [](int64_t items) { return (double)((items + kCUs - 1) / kCUs); };
     int64_t full = active;
@@ -1002,7 +1161,7 @@ int gemm_cfg_auto(const GemmArgs& g) {
     const int64_t sm = (g.M + 127) / 128, sn = (g.N + 127) / 128;
     const int64_t tiles0 = g.symmetric ? sm * (sm + 1) / 2 : sm * sn;
     const double t0 = rounds(tiles0) * (double)nk * 0.45;
-    return t9 <= t0 ? 9 : 0;
+    return t9 <= t0 ? big : 0;
 }
 
 }  // namespace
@@ -1019,10 +1178,10 @@ hipError_t launch_gemm_nt(GemmArgs g, hipStream_t s) {
         case ID: return launch_gemm_cfg<Cfg<BM, BN, BK, WM, WN>>(g, s);
         VE_GEMM_CFGS(VE_GEMM_CASE)
 #undef VE_GEMM_CASE
-#define VE_DMA_CASE(ID, WM, WN, BK, ST)                                                    \
-        case ID:                                                                           \
-            return dma_ok<DmaCfg<WM, WN, BK, ST>>(g) ? launch_gemm_dma<DmaCfg<WM, WN, BK, ST>>(g, s) \
-                                                     : launch_gemm_cfg<Cfg<256, 256, 64, 128, 64>>(g, s);
+#define VE_DMA_CASE(ID, WM, WN, BK, ST, QS)                                                         \
+        case ID:                                                                                    \
+            return dma_ok<DmaCfg<WM, WN, BK, ST, QS>>(g) ? launch_gemm_dma<DmaCfg<WM, WN, BK, ST, QS>>(g, s) \
+                                                         : launch_gemm_cfg<Cfg<256, 256, 64, 128, 64>>(g, s);
         VE_DMA_CFGS(VE_DMA_CASE)
 #undef VE_DMA_CASE
         default: return hipErrorInvalidValue;
