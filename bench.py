@@ -39,6 +39,7 @@ def log(msg):
 
 STEP_SOURCES = ("ve_kernels.hip", "ve_device.h", "ve_internal.h", "ve_host.cpp")
 GROUP_SOURCES = ("ve_group.hip", "ve_device.h", "ve_internal.h", "ve_host.cpp")
+MUON_SOURCES = ("ve_muon.hip", "ve_muon.h", "ve_muon_host.cpp", "ve_device.h", "ve_internal.h")
 
 
 def kernel_source_hash(files=STEP_SOURCES):
@@ -566,6 +567,64 @@ def summarize_trace(args):
     print("\n".join(t))
 
 
+def summarize_muon(args):
+    """Per-call kernel times of the Newton-Schulz iterations bench.py times
+    (the LLaMA MLP matrix, then the routed-expert matrix) from a rocprofv3
+    --kernel-trace run: each call runs from its k_sumsq to the next one; the
+    first call of each shape is the warm-up and is left out."""
+    import collections
+    import re
+    import statistics
+    trace = sorted(_csv_rows(os.path.join(args.trace_dir, "run_kernel_trace.csv")),
+                   key=lambda r: int(r["Start_Timestamp"]))
+    muon_kernels = ("k_sumsq", "k_norm_scale", "k_normalize", "k_gemm", "k_split_sum")
+    calls, cur = [], None
+    for r in trace:
+        name = r["Kernel_Name"]
+        if "k_sumsq" in name:
+            cur = []
+            calls.append(cur)
+        elif cur is not None and not any(k in name for k in muon_kernels):
+            cur = None
+            continue
+        if cur is not None:
+            cur.append(r)
+    shapes = collections.OrderedDict()
+    for c in calls:
+        norm = next(r for r in c if "k_normalize" in r["Kernel_Name"])
+        shapes.setdefault(_grid(norm), []).append(c)
+    dims = [(8192, 28672, "LLaMA-3-70B MLP"), (2048, 7168, "DeepSeek-V3 routed expert")]
+    t = ["# Kernel trace of the Newton-Schulz iterations in bench.py (rocprofv3 --kernel-trace --stats)", "",
+         f"kernel sources hash: {kernel_source_hash(MUON_SOURCES)}", "",
+         "command (run from the repository root on the GPU box):", "  " + args.command, ""]
+    short = lambda n: re.sub(r"ve::\(anonymous namespace\)::", "", n)
+    for (grid, cs), (rows, cols, what) in zip(shapes.items(), dims):
+        timed = cs[1:] if len(cs) > 1 else cs
+        tot = [sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in c) / 1e3 for c in timed]
+        per = collections.OrderedDict()
+        for c in timed:
+            for r in c:
+                k = (short(r["Kernel_Name"])[:96], _grid(r))
+                per.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        fl = ns_flops(rows, cols)
+        avg = statistics.mean(tot)
+        t += [f"{rows} x {cols} ({what}), 5 steps: {len(timed)} timed calls, kernel time per call {avg:.1f} us "
+              f"(min {min(tot):.1f}, max {max(tot):.1f}); {fl / 1e12:.2f} TFLOP (minimal count) -> "
+              f"{fl / avg / 1e6:.1f} TFLOP/s = {fl / avg / 1e6 / MFMA_BF16_PEAK_TFLOPS * 100:.1f}% of 2.5 PFLOP/s", "",
+              f"  {'kernel':96s} {'grid':>9s} {'per call':>8s} {'avg us':>9s} {'us/call':>9s}"]
+        for (name, g), d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            t.append(f"  {name:96s} {g:9d} {len(d) / len(timed):8.0f} {statistics.mean(d):9.1f} "
+                     f"{sum(d) / len(timed):9.1f}")
+        t.append("")
+    if args.bench_log and os.path.exists(args.bench_log):
+        with open(args.bench_log) as fh:
+            keep = [ln.strip() for ln in fh if ln.startswith("[bench] muon")]
+        t += ["bench.py's own HIP-event timing in the same run:"] + ["  " + ln for ln in keep]
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(t) + "\n")
+    print("\n".join(t))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -582,7 +641,7 @@ def main():
     ap.add_argument("--copy-gib", type=float, default=1.0,
                     help="size of the streaming-reference copy that measures the copy ceiling (0: skip)")
     sm = ap.add_argument_group("profile summaries (no GPU needed)")
-    sm.add_argument("--summarize", choices=["counters", "trace"], default=None,
+    sm.add_argument("--summarize", choices=["counters", "trace", "muon"], default=None,
                     help="write a profiles/ summary from rocprofv3 output instead of benchmarking")
     sm.add_argument("--fetch-dir", help="counters: output folder of the FETCH_SIZE run")
     sm.add_argument("--write-dir", help="counters: output folder of the WRITE_SIZE run")
@@ -596,7 +655,7 @@ def main():
     args = ap.parse_args()
     if args.summarize:
         sys.path.insert(0, ROOT)
-        (summarize_counters if args.summarize == "counters" else summarize_trace)(args)
+        {"counters": summarize_counters, "trace": summarize_trace, "muon": summarize_muon}[args.summarize](args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the data-parallel step; --gpus {args.gpus} is not "
