@@ -603,7 +603,8 @@ __global__ void __launch_bounds__(CF::THREADS) k_gemm_nt_dma(GemmArgs g) {
         // last step), so the wait counts are constants.
         constexpr int SP = S, SQ = 2, PE = BM * BK, QE = BN * BK, DL = CF::DMA_PER_OP;
         static_assert(SP == 3, "P stages");
-        static_assert(CF::ROWS_PER_DMA * CF::WAVES == 64 && CF::CHUNKS == 8, "one DMA round covers 64 rows");
+        constexpr int RR = CF::ROWS_PER_DMA * CF::WAVES;  // rows one DMA round covers
+        static_assert(CF::CHUNKS == 8 && CF::WAVES % 2 == 0, "swizzle of a thread's rows independent of the round");
         uint16_t* pst = ops;            // [SP][PE]
         uint16_t* qst = ops + SP * PE;  // [SQ][QE]
         // Operand rows past M or N are past the end of the tile's buffer
@@ -624,7 +625,7 @@ __global__ void __launch_bounds__(CF::THREADS) k_gemm_nt_dma(GemmArgs g) {
 #pragma unroll
             for (int q = 0; q < DL; ++q) {
                 const int blk = CF::WAVES * q + wave;
-                uint32_t v = pv0 + k2 + (uint32_t)(q * 64 * g.ldp * 2);
+                uint32_t v = pv0 + k2 + (uint32_t)(q * RR * g.ldp * 2);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     prs, (void __attribute__((address_space(3)))*)(st + blk * CF::ROWS_PER_DMA * BK), 16, (int)v, 0, 0, 0);
             }
@@ -635,12 +636,12 @@ __global__ void __launch_bounds__(CF::THREADS) k_gemm_nt_dma(GemmArgs g) {
 #pragma unroll
             for (int q = 0; q < DL; ++q)
                 qreg[buf][q] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, (int)(qv0 + k2 + (uint32_t)(q * 64 * g.ldq * 2)), 0, 0));
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, (int)(qv0 + k2 + (uint32_t)(q * RR * g.ldq * 2)), 0, 0));
         };
         auto qwrite = [&](int buf, int64_t kt) {
             uint16_t* st = qst + (int)(kt % SQ) * QE + trow * BK + lslot * 8;
 #pragma unroll
-            for (int q = 0; q < DL; ++q) *(u32x4*)(st + q * 64 * BK) = qreg[buf][q];
+            for (int q = 0; q < DL; ++q) *(u32x4*)(st + q * RR * BK) = qreg[buf][q];
         };
         const int frow = lane & 31, fhalf = lane >> 5;
         const int fs = CF::swz(lane & 15);
