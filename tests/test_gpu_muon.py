@@ -371,3 +371,42 @@ def test_large_ragged_products_sampled(M, N, K, sym):
         want = muon.gemm_nt(Ph[i:i + 1], Qh[j:j + 1], Dh[i:i + 1, j:j + 1], 0.75, -0.5)
         bd = product_bound(Ph[i:i + 1], Qh[j:j + 1], Dh[i:i + 1, j:j + 1], 0.75, -0.5, C=want)
         assert abs(Ch[i, j] - want[0, 0]) <= bd[0, 0], (i, j, Ch[i, j], want[0, 0])
+
+
+# The large-tile product configurations: 6 (4 waves of 128 x 128, two LDS
+# stages), 9 (8 waves of 128 x 64, two stages) and 13 (8 waves, P in three
+# LDS stages, Q staged through registers; the default).  They feed the MFMAs
+# the same fragments in the same order, so their outputs agree bit for bit;
+# ragged edges (rows past M or N), a symmetric product and C^T included.
+@pytest.mark.parametrize("M,N,K,sym", [(7000, 7040, 1024, False), (2048, 2048, 7168, True), (300, 520, 640, False),
+                                       (1000, 300, 2880, False)])
+def test_product_configurations_agree(M, N, K, sym):
+    import torch
+    ve = _ve()
+    g = torch.Generator(device=DEV)
+    g.manual_seed(M * 3 + N + K)
+    P = torch.randn(M, K, generator=g, device=DEV).to(torch.bfloat16).view(torch.int16)
+    Q = P if sym else torch.randn(N, K, generator=g, device=DEV).to(torch.bfloat16).view(torch.int16)
+    D = torch.randn(M, N, generator=g, device=DEV).to(torch.bfloat16).view(torch.int16)
+    if sym:
+        D = (D.view(torch.bfloat16) + D.view(torch.bfloat16).t()).contiguous().view(torch.int16)
+    outs = {}
+    for cfg in (9, 6, 13):
+        C = _empty((M, N))
+        CT = None if sym else _empty((N, M))
+        _say(f"[gpu] product configuration {cfg}: M={M} N={N} K={K} symmetric={sym}")
+        with ve.options(gemm_cfg=cfg):
+            ve.gemm_bf16_nt(P, Q, C=C, CT=CT, D=D, alpha=0.75, beta=-0.5, symmetric=sym)
+        torch.cuda.synchronize()
+        outs[cfg] = (C, CT)
+    for cfg in (6, 13):
+        assert torch.equal(outs[cfg][0], outs[9][0]), cfg
+        if not sym:
+            assert torch.equal(outs[cfg][1], outs[9][1]), cfg
+    # and the default within the bound on sampled elements
+    Ph, Qh, Dh, Ch = _host(P), _host(Q), _host(D), _host(outs[13][0])
+    rng = np.random.default_rng(2)
+    for i, j in zip(np.concatenate([rng.integers(0, M, 60), [M - 1]]), np.concatenate([rng.integers(0, N, 60), [N - 1]])):
+        want = muon.gemm_nt(Ph[i:i + 1], Qh[j:j + 1], Dh[i:i + 1, j:j + 1], 0.75, -0.5)
+        bd = product_bound(Ph[i:i + 1], Qh[j:j + 1], Dh[i:i + 1, j:j + 1], 0.75, -0.5, C=want)
+        assert abs(Ch[i, j] - want[0, 0]) <= bd[0, 0], (i, j)
