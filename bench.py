@@ -489,7 +489,7 @@ def summarize_counters(args):
            f"  algorithmic bytes per launch ({nbk} buckets x ({BYTES_PER_ELEM} B x {nv} elements + "
            f"{BYTES_PER_BLOCK} B x {nb} blocks + {BYTES_PER_PAD} B x {S - nv} padding)) = {alg / 1e9:.4f} GB",
            f"  measured / algorithmic = {(rb + wb) / alg:.4f}"]
-    base = os.path.join(ROOT, "profiles", f"shard_step_{args.workload}")
+    base = os.path.join(args.profiles_dir, f"shard_step_{args.workload}")
     with open(base + "_hbm_counters.txt", "w") as fh:
         fh.write("\n".join(txt) + "\n")
     summarize_group_counters(args, f_rows, w_rows, fx, wx, fc, wc, copy_kib, nbk, nv, S)
@@ -528,7 +528,7 @@ def summarize_group_counters(args, f_rows, w_rows, fx, wx, fc, wc, copy_kib, nbk
         out += [f"{op}: {fr[0]['Kernel_Name']} ({len(fr)} / {len(wr)} dispatches)",
                 f"  HBM bytes per launch: read {rb / 1e9:.4f} GB + write {wb / 1e9:.4f} GB = {(rb + wb) / 1e9:.4f} GB; "
                 f"algorithmic {alg / 1e9:.4f} GB -> measured / algorithmic = {(rb + wb) / alg:.4f}", ""]
-    base = os.path.join(ROOT, "profiles", f"dbuffer_group_{args.workload}")
+    base = os.path.join(args.profiles_dir, f"dbuffer_group_{args.workload}")
     with open(base + "_hbm_counters.txt", "w") as fh:
         fh.write("\n".join(out).rstrip() + "\n")
     with open(base + "_traffic.json", "w") as fh:
@@ -652,6 +652,8 @@ def main():
     sm.add_argument("--bench-log", default=None, help="trace: bench.py's stderr of the profiled run")
     sm.add_argument("--out", default=None, help="trace: summary file to write")
     sm.add_argument("--top", type=int, default=16, help="trace: kernels listed")
+    sm.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"),
+                    help="counters: folder the summaries and traffic files are written to")
     args = ap.parse_args()
     if args.summarize:
         sys.path.insert(0, ROOT)
