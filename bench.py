@@ -479,7 +479,7 @@ def summarize_counters(args):
     h = kernel_source_hash(STEP_SOURCES)
     txt = [f"# HBM traffic of the fused shard step, {args.workload} workload (rocprofv3 --pmc)",
            f"kernel sources hash: {h}", "",
-           "commands (run from the repository root on the GPU box), one pass per counter:",
+           "commands (run from the repository root, on the machine with the GPU), one pass per counter:",
            "  " + args.command_fetch, "  " + args.command_write, "",
            f"calibration: the streaming copy (k_stream_copy) reads and writes {copy_kib:.0f} KiB per dispatch;",
            f"  it reads FETCH_SIZE {fc:.1f} KiB and WRITE_SIZE {wc:.1f} KiB -> FETCH_SIZE x {fx:.4f}, WRITE_SIZE x {wx:.4f}",
@@ -510,7 +510,7 @@ def summarize_group_counters(args, f_rows, w_rows, fx, wx, fc, wc, copy_kib, nbk
     h = kernel_source_hash(GROUP_SOURCES)
     out = [f"# HBM traffic of the DBuffer group operations, {args.workload} workload, all buckets' rank chunks "
            "per launch (rocprofv3 --pmc)", f"kernel sources hash: {h}", "",
-           "commands (run from the repository root on the GPU box), one pass per counter:",
+           "commands (run from the repository root, on the machine with the GPU), one pass per counter:",
            "  " + args.command_fetch, "  " + args.command_write, "",
            f"calibration: FETCH_SIZE x {fx:.4f}, WRITE_SIZE x {wx:.4f} (the streaming copy of {copy_kib:.0f} KiB "
            f"reads {fc:.1f} / {wc:.1f} KiB)", ""]
@@ -549,7 +549,7 @@ def summarize_trace(args):
     alg, nbk, nv, nb, S = _workload_alg(args.workload, args.buckets)
     t = [f"# Kernel trace of bench.py, {args.workload} workload (rocprofv3 --kernel-trace --stats)", "",
          f"kernel sources hash: {kernel_source_hash(STEP_SOURCES)}", "",
-         "command (run from the repository root on the GPU box):", "  " + args.command, "",
+         "command (run from the repository root, on the machine with the GPU):", "  " + args.command, "",
          f"{'kernel':72s} {'calls':>6s} {'avg us':>10s} {'min us':>10s} {'max us':>10s}"]
     for r in stats[:args.top]:
         t.append(f"{r['Name'][:72]:72s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
@@ -596,7 +596,7 @@ def summarize_muon(args):
     dims = [(8192, 28672, "LLaMA-3-70B MLP"), (2048, 7168, "DeepSeek-V3 routed expert")]
     t = ["# Kernel trace of the Newton-Schulz iterations in bench.py (rocprofv3 --kernel-trace --stats)", "",
          f"kernel sources hash: {kernel_source_hash(MUON_SOURCES)}", "",
-         "command (run from the repository root on the GPU box):", "  " + args.command, ""]
+         "command (run from the repository root, on the machine with the GPU):", "  " + args.command, ""]
     short = lambda n: re.sub(r"ve::\(anonymous namespace\)::", "", n)
     for (grid, cs), (rows, cols, what) in zip(shapes.items(), dims):
         timed = cs[1:] if len(cs) > 1 else cs
