@@ -37,7 +37,7 @@ struct OptionDef {
 };
 constexpr OptionDef kOptionDefs[kNumOptions] = {
     {"wg_threads", "VE_WG_THREADS", 0}, {"wg_gpt", "VE_WG_GPT", 0}, {"gemm_split", "VE_GEMM_SPLIT", 1},
-    {"gemm_cfg", "VE_GEMM_CFG", -1},    {"gemm_xcd", "VE_GEMM_XCD", 1},
+    {"gemm_cfg", "VE_GEMM_CFG", -1},    {"gemm_xcd", "VE_GEMM_XCD", 1},     {"wg_dynamic", "VE_WG_DYNAMIC", 1},
 };
 std::atomic<int64_t> g_options[kNumOptions];
 std::once_flag g_options_once;
@@ -130,6 +130,8 @@ struct ve_plan {
     HostRuns whole;              // rank == -1 copy-in
     char* dev = nullptr;         // one device allocation holding every table
     size_t dev_bytes = 0;
+    size_t off_sched = 0;        // per rank, kSchedStride bytes: the persistent step's two counters (zero at rest)
+    int n_cu = 0;                // compute units of `device`
 
     template <class T>
     const T* dptr(size_t off) const { return reinterpret_cast<const T*>(dev + off); }
@@ -458,6 +460,8 @@ ve_status ve_plan_load(const ve_tensor_spec* specs, int32_t n_tensors, int32_t f
             pack_runs(pk, rt.pad);
         }
         pack_runs(pk, P->whole);
+        // one 64-byte line of scheduler counters per rank, zero at load
+        P->off_sched = pk.put(std::vector<uint32_t>((size_t)fsdp_size * kSchedStride / sizeof(uint32_t), 0u));
         P->dev_bytes = std::max<size_t>(pk.buf.size(), 256);
         if (device == -1) {  // host-only plan: layout queries, no kernels
             *out = P;
@@ -467,6 +471,11 @@ ve_status ve_plan_load(const ve_tensor_spec* specs, int32_t n_tensors, int32_t f
         if (!g.ok) {
             delete P;
             return fail(VE_ERR_DEVICE, "hipSetDevice(%d) failed", device);
+        }
+        if (hipDeviceGetAttribute(&P->n_cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+            P->n_cu <= 0) {
+            delete P;
+            return fail(VE_ERR_DEVICE, "cannot read the compute-unit count of device %d", device);
         }
         if (hipMalloc((void**)&P->dev, P->dev_bytes) != hipSuccess) {
             delete P;
@@ -618,6 +627,7 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
     StepArgs a{};
     a.states = states;
     a.segs = plan->dptr<Seg>(rt.off_segs);
+    a.sched = reinterpret_cast<uint32_t*>(plan->dev + plan->off_sched + (size_t)rank * kSchedStride);
     const double b1 = hp->beta1, b2 = hp->beta2, lr = hp->lr;
     a.sc.beta1 = hp->beta1;
     a.sc.beta2 = hp->beta2;
@@ -651,7 +661,15 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
             const int64_t nb = set_inline(a, rt, rt.wg, i0, i1);
             i0 = i1;
             if (nb == 0) continue;
-            if ((st = launch_status(launch_step_wg(a, n_states, threads, gpt, s), "workgroup step")) != VE_OK)
+            // Row-block shapes of one workgroup per CU run persistent, with
+            // one workgroup per CU taking blocks from the rank's counters
+            // (launches on one stream run one after another, so they share
+            // them); tickets stay below 2^31.
+            int dyn_grid = 0;
+            if (option(kOptWgDynamic) != 0 && wg_dynamic_shape(threads, gpt) &&
+                nb * n_states + plan->n_cu < (int64_t(1) << 31))
+                dyn_grid = (int)std::min<int64_t>(plan->n_cu, nb * n_states);
+            if ((st = launch_status(launch_step_wg(a, n_states, threads, gpt, dyn_grid, s), "workgroup step")) != VE_OK)
                 return st;
         }
     }

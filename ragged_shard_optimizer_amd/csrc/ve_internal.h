@@ -21,6 +21,8 @@ constexpr int kWgChunk = 4;
 // workgroup.
 constexpr int kSmallMaxChunks = 64;
 constexpr int kWgMaxThreads = 1024;
+constexpr int kDynMinGpt = 14;  // persistent step form: 512-thread shapes from 14 groups per thread
+constexpr size_t kSchedStride = 64;  // bytes of scheduler counters per rank in a plan's device tables
 
 // Instantiated workgroup shapes (threads, 4-element groups per thread).  The
 // largest capacity, 1024 x 16 groups = 65,536 elements, bounds the blocks
@@ -127,6 +129,7 @@ struct StepArgs {
     StepScalars sc;
     RunArgs pad;                   // small-block path: padding tiles fused into the launch (n_tiles 0: none)
     int64_t pad_wg0;               // small-block path: first workgroup of the padding tiles
+    uint32_t* sched;               // workgroup path, persistent form: [next ticket, workgroups done], zero between launches
     int32_t n_inline;              // workgroup paths: segments given inline below
     int64_t inl_prefix[kInlineSegs + 1];  // work-item prefix, inl_prefix[0] = 0
     Seg inl_segs[kInlineSegs];
@@ -137,8 +140,11 @@ struct StepArgs {
 // Small-block step; a.pad's tiles (zero fill of grad_shard and param_shard)
 // run as extra workgroups of the same launch.
 hipError_t launch_step_small(const StepArgs& a, int n_states, hipStream_t s);
-hipError_t launch_step_wg(const StepArgs& a, int n_states, int threads, int groups_per_thread,
+// dyn_grid > 0 runs a shape that wg_dynamic_shape() accepts in its persistent
+// form with that many workgroups (one per CU), scheduled through a.sched.
+hipError_t launch_step_wg(const StepArgs& a, int n_states, int threads, int groups_per_thread, int dyn_grid,
                           hipStream_t s);
+bool wg_dynamic_shape(int threads, int groups_per_thread);
 hipError_t launch_step_huge(const StepArgs& a, int n_states, hipStream_t s);
 // Copy-in: out = bucket; grad pointers from `grad_ptrs`.
 hipError_t launch_runs_copy(const RunArgs& r, const uint16_t* const* grad_ptrs, uint16_t* out,
@@ -155,6 +161,7 @@ enum Option : int {
     kOptGemmSplit,      // "gemm_split" (VE_GEMM_SPLIT): 0 = never split a product's short last round
     kOptGemmCfg,        // "gemm_cfg" (VE_GEMM_CFG): product configuration, -1 = by shape
     kOptGemmXcd,        // "gemm_xcd" (VE_GEMM_XCD): 0 = plain tile order instead of the XCD-aware one
+    kOptWgDynamic,      // "wg_dynamic" (VE_WG_DYNAMIC): 0 = one-shot launches for the row-block shapes too
     kNumOptions
 };
 int64_t option(Option o);

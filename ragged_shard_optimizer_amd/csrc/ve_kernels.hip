@@ -919,8 +919,8 @@ __device__ __forceinline__ uint32_t tiled_off(const WgItem& it, int ci) {
 }
 
 // Byte offsets of register slot c's chunk.
-template <int T, int GPT, int MODE>
-__device__ __forceinline__ ChunkAddr wg_addr(const WgItem& it, const uint32_t (&off)[GPT], int c) {
+template <int T, int GPT, int MODE, class Item>
+__device__ __forceinline__ ChunkAddr wg_addr(const Item& it, const uint32_t (&off)[GPT], int c) {
     ChunkAddr a;
     if constexpr (MODE == kWgLinear) {
         const int k = (c + it.rot) % GPT;  // wave-uniform slot
@@ -1157,6 +1157,249 @@ __global__ void __launch_bounds__(256) k_step_huge(StepArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Persistent form for the shapes of one workgroup per CU (512 threads, 14 to
+// 24 groups per thread: row blocks of 28K to 49K elements).  The grid holds
+// one workgroup per CU and every workgroup takes its blocks from a ticket
+// counter, one relaxed device-scope add per block, so a CU that finishes
+// early takes the next block as the hardware dispatcher would, without the
+// gap between one workgroup's end and the next one's start.  A block that is
+// one contiguous FAST run is staged: the block before it on the same CU
+// brings its gradient and both code streams (4 of its 8 input bytes per
+// element, up to kDynSlots register slots of them) into LDS with
+// buffer-to-LDS loads issued in the middle of its own phase 2, so the CU
+// keeps HBM requests in flight through its reduction tail and the block
+// switch.  Measured on MI355X against the one-shot kernel, outputs
+// bit-identical: 28,672-element rows 5.47-5.52 -> 5.88 TB/s, 46,080-element
+// rows 5.28-5.31 -> 5.54 TB/s (dynamic tickets alone: 5.72 and 5.46).  A
+// persistent form with a static block order (block i on workgroup i mod
+// grid) ran 4% below the one-shot kernel, staged or not: the slowest CUs set
+// the end.
+//
+// sched[0] is the next ticket, sched[1] counts the workgroups that have left;
+// the last one resets both, so the next launch on the stream (or a graph
+// replay) starts from zero.  Launches that overlap in time must not share
+// the counters.
+#ifndef VE_DYN_SLOTS
+#define VE_DYN_SLOTS 16  // staged register slots (8 KiB of LDS each)
+#endif
+#ifndef VE_DYN_DMA_AT
+#define VE_DYN_DMA_AT 8  // phase-2 group before which the next block's loads go out
+#endif
+constexpr int kDynThreads = 512;
+
+template <int GPT>
+struct DynCfg {
+    static constexpr int PF = GPT < VE_DYN_SLOTS ? GPT : VE_DYN_SLOTS;  // staged slots
+    static constexpr int SPAN = PF * kDynThreads * kWgChunk;           // staged elements
+    static constexpr int LDS = 4 * SPAN;  // gradient (2 B) + m and v codes (1 B each) per element
+    static constexpr int DMA_AT = VE_DYN_DMA_AT < GPT ? VE_DYN_DMA_AT : GPT - 1;
+};
+
+// The fields of a block that the staged path uses (a WgItem's LINEAR subset:
+// fewer scalar registers held across the loop).
+struct DynItem {
+    FastRsrc fb;
+    Geo geo;
+    float sm, sv;
+    float* m_scale;
+    float* v_scale;
+    int rot;
+    uint32_t lane0, step;
+    bool staged_ok;  // one contiguous FAST run whose streams can go through LDS
+};
+
+template <int GPT>
+__device__ __forceinline__ DynItem dyn_item(const StepArgs& a, uint32_t w, uint32_t nx) {
+    const uint32_t y = __builtin_amdgcn_readfirstlane(w / nx);
+    const WgItem it = wg_item_at<GPT>(a, y, w - y * nx);
+    DynItem d;
+    d.fb = it.fb;
+    d.geo = it.geo;
+    d.sm = it.sm;
+    d.sv = it.sv;
+    d.m_scale = it.m_scale;
+    d.v_scale = it.v_scale;
+    d.rot = it.rot;
+    d.lane0 = it.lane0;
+    d.step = it.step;
+    // the 16-byte LDS loads need each stream's span to be a multiple of 16 bytes
+    d.staged_ok = it.mode == kWgLinear && it.geo.nruns == 1 && (it.geo.run & 15) == 0;
+    return d;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Stage block `nt`'s first PF register slots (in its rotated slot order) into
+// LDS: slot c's gradient at [c * 4 KiB], its m codes at [2 SPAN + c * 2 KiB],
+// its v codes at [3 SPAN + c * 2 KiB].  Wave w moves the 1 KiB piece w of
+// every slot (pieces 0-3 gradient, 4-5 m codes, 6-7 v codes), 16 bytes per
+// lane; reads past the block's span return zeros, which no lane uses.
+template <int GPT>
+__device__ __forceinline__ void dyn_stage(const DynItem& nt, uint8_t* sb) {
+    constexpr int T = kDynThreads;
+    constexpr int PF = DynCfg<GPT>::PF, SPAN = DynCfg<GPT>::SPAN;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const __amdgpu_buffer_rsrc_t r = wave < 4 ? nt.fb.grad : (wave < 6 ? nt.fb.m_q : nt.fb.v_q);
+    const int piece = wave < 4 ? wave : (wave < 6 ? wave - 4 : wave - 6);
+    const int esz = wave < 4 ? 2 : 1;
+    const int base = wave < 4 ? 0 : (wave < 6 ? 2 * SPAN : 3 * SPAN);
+#pragma unroll
+    for (int c = 0; c < PF; ++c) {
+        const int k = (c + nt.rot) % GPT;
+        const int src = (k * T * kWgChunk) * esz + piece * 1024 + lane * 16;
+        const int dst = base + c * T * kWgChunk * esz + piece * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(sb + dst), 16, src, 0, 0, kBufNT);
+    }
+}
+
+// One staged or unstaged block: phase 1, absmax, phase 2.  The next ticket is
+// taken during phase 1 and the next block staged during phase 2 when
+// possible; returns the next ticket and sets stage_next.
+template <int GPT, bool STAGED>
+__device__ __forceinline__ uint32_t dyn_block(const DynItem& it, const StepArgs& A, uint32_t nx, uint32_t nitems,
+                                              bool& stage_next, uint32_t* s_next, uint8_t* sb,
+                                              float (&red)[2][kDynThreads / 64]) {
+    constexpr int T = kDynThreads;
+    constexpr int CH = kWgChunk;
+    constexpr int MODE = kWgLinear;
+    constexpr int PF = DynCfg<GPT>::PF, SPAN = DynCfg<GPT>::SPAN, DMA_AT = DynCfg<GPT>::DMA_AT;
+    constexpr int MA = WgAhead<GPT, MODE>::value;
+    constexpr bool LATE = WgLateCopy<T, GPT>::value;
+    const StepScalars& sc = A.sc;
+    const int tid = threadIdx.x;
+    In<CH> x[GPT];
+    float mst[MA + 1][CH];
+    const uint32_t off[GPT] = {};  // unused by LINEAR addressing
+#pragma unroll
+    for (int c = 0; c < GPT; ++c) {
+        const ChunkAddr ad = wg_addr<T, GPT, MODE>(it, off, c);
+        if (!STAGED || c >= PF) load_in_fast(x[c], it.fb, ad);
+        if (c < MA) load_master_fast(mst[c % (MA + 1)], it.fb, ad);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    uint32_t ticket = 0;
+    if (tid == 0) ticket = atomicAdd(A.sched, 1u);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (STAGED) {
+#pragma unroll
+        for (int c = 0; c < PF; ++c) {
+            // a lane without a chunk takes zeros, as the range-checked loads give it
+            const int k = (c + it.rot) % GPT;
+            const bool ok = tid < it.geo.nchunks - k * T;
+            const uint2 g = *(const uint2*)(sb + c * T * 8 + tid * 8);
+            const uint32_t m = *(const uint32_t*)(sb + 2 * SPAN + c * T * 4 + tid * 4);
+            const uint32_t v = *(const uint32_t*)(sb + 3 * SPAN + c * T * 4 + tid * 4);
+            x[c].g[0] = ok ? g.x : 0u;
+            x[c].g[1] = ok ? g.y : 0u;
+            x[c].m[0] = ok ? m : 0u;
+            x[c].v[0] = ok ? v : 0u;
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float am = 0.f, av = 0.f;
+#pragma unroll
+    for (int c = 0; c < GPT; ++c) {
+        if (c + MA < GPT) load_master_fast(mst[(c + MA) % (MA + 1)], it.fb, wg_addr<T, GPT, MODE>(it, off, c + MA));
+        phase1_fast<LATE>(x[c], mst[c % (MA + 1)], it.fb, wg_addr<T, GPT, MODE>(it, off, c), it.sm, it.sv, sc, am,
+                          av);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    am = wave_max(am);
+    av = wave_max(av);
+    if ((tid & 63) == 0) {
+        red[0][tid >> 6] = am;
+        red[1][tid >> 6] = av;
+    }
+    if (tid == 0) *s_next = ticket;
+    lds_barrier();
+    const uint32_t wn = *s_next;
+    const bool more = wn < nitems;
+    const DynItem nt = dyn_item<GPT>(A, more ? wn : 0u, nx);
+    stage_next = more && nt.staged_ok;
+    am = 0.f;
+    av = 0.f;
+#pragma unroll
+    for (int i = 0; i < T / 64; ++i) {
+        am = fmaxf(am, red[0][i]);
+        av = fmaxf(av, red[1][i]);
+    }
+    const float im = am > 0.f ? 127.0f / am : 0.f;
+    const float iv = av > 0.f ? 127.0f / av : 0.f;
+    if (tid == 0) {
+        ((VE_GLOBAL float*)it.m_scale)[it.geo.blk] = am / 127.0f;
+        ((VE_GLOBAL float*)it.v_scale)[it.geo.blk] = av / 127.0f;
+    }
+#pragma unroll
+    for (int c = 0; c < GPT; ++c) {
+        if (c == DMA_AT) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (stage_next) dyn_stage<GPT>(nt, sb);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        make_opaque(x[c]);
+        phase2_fast<LATE>(x[c], it.fb, wg_addr<T, GPT, MODE>(it, off, c), it.sm, it.sv, im, iv, sc);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return wn;
+}
+
+template <int GPT>
+__global__ void __launch_bounds__(kDynThreads) k_step_dyn(StepArgs a, uint32_t nx, uint32_t nitems) {
+    constexpr int T = kDynThreads;
+    constexpr int GROUP_STORES = WgLateCopy<T, GPT>::value ? 3 : 2;  // phase-2 stores per group
+    constexpr int AFTER_DMA = GROUP_STORES * (GPT - DynCfg<GPT>::DMA_AT);
+    static_assert(AFTER_DMA <= 63, "vmcnt holds at most 63");
+    __shared__ float s_red[2][T / 64];
+    __shared__ uint32_t s_next;
+    __shared__ __attribute__((aligned(16))) uint8_t s_buf[DynCfg<GPT>::LDS];
+    if (threadIdx.x == 0) s_next = atomicAdd(a.sched, 1u);
+    __syncthreads();
+    uint32_t w = s_next;
+    bool staged = false;
+    while (w < nitems) {
+        const DynItem it = dyn_item<GPT>(a, w, nx);
+        uint32_t wn;
+        if (it.staged_ok) {
+            __builtin_amdgcn_sched_barrier(0);
+            // This wave's staging loads went out before its last AFTER_DMA
+            // stores: wait for them (not for the stores), then for every wave.
+            // The barrier also separates the previous block's reads of s_red
+            // and s_next from this block's writes.
+            if (staged) __builtin_amdgcn_s_waitcnt(0x0F70 | (AFTER_DMA & 15) | (((AFTER_DMA >> 4) & 3) << 14));
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            bool sn;
+            if (staged) wn = dyn_block<GPT, true>(it, a, nx, nitems, sn, &s_next, s_buf, s_red);
+            else wn = dyn_block<GPT, false>(it, a, nx, nitems, sn, &s_next, s_buf, s_red);
+            staged = sn;
+        } else {
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_s_barrier();
+            if (threadIdx.x == 0) s_next = atomicAdd(a.sched, 1u);  // read after wg_one's barrier
+            const uint32_t y = __builtin_amdgcn_readfirstlane(w / nx);
+            const WgItem gi = wg_item_at<GPT>(a, y, w - y * nx);
+            if (gi.mode == kWgLinear) wg_one<T, GPT, kWgLinear>(gi, s_red, a.sc);
+            else if (gi.mode == kWgTiled) wg_one<T, GPT, kWgTiled>(gi, s_red, a.sc);
+            else wg_one<T, GPT, kWgGeneral>(gi, s_red, a.sc);
+            wn = s_next;
+            staged = false;
+        }
+        w = wn;
+    }
+    // Every ticket this workgroup will take is taken; the last workgroup out
+    // resets the counters for the next launch.
+    if (threadIdx.x == 0) {
+        const uint32_t left = atomicAdd(a.sched + 1, 1u);
+        if (left == gridDim.x - 1) {
+            atomicExch(a.sched, 0u);
+            atomicExch(a.sched + 1, 0u);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1173,7 +1416,15 @@ hipError_t launch_step_small(const StepArgs& a0, int n_states, hipStream_t s) {
 }
 
 template <int T, int GPT>
-static hipError_t launch_wg_t(const StepArgs& a, int n_states, hipStream_t s) {
+static hipError_t launch_wg_t(const StepArgs& a, int n_states, int dyn_grid, hipStream_t s) {
+    if constexpr (T == kDynThreads && GPT >= kDynMinGpt) {
+        if (dyn_grid > 0) {
+            const int64_t items = a.work.total * n_states;
+            hipLaunchKernelGGL((k_step_dyn<GPT>), dim3((unsigned)dyn_grid), dim3(T), 0, s, a, (uint32_t)a.work.total,
+                               (uint32_t)items);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((k_step_wg<T, GPT>), dim3(grid_x(a.work.total), n_states), dim3(T), 0, s, a);
     return hipGetLastError();
 }
@@ -1185,8 +1436,10 @@ bool wg_config_supported(int threads, int gpt) {
     return false;
 }
 
-hipError_t launch_step_wg(const StepArgs& a, int n_states, int threads, int gpt, hipStream_t s) {
-#define VE_WG_CASE(T, G) if (threads == T && gpt == G) return launch_wg_t<T, G>(a, n_states, s);
+bool wg_dynamic_shape(int threads, int gpt) { return threads == kDynThreads && gpt >= kDynMinGpt; }
+
+hipError_t launch_step_wg(const StepArgs& a, int n_states, int threads, int gpt, int dyn_grid, hipStream_t s) {
+#define VE_WG_CASE(T, G) if (threads == T && gpt == G) return launch_wg_t<T, G>(a, n_states, dyn_grid, s);
     VE_WG_SHAPES(VE_WG_CASE)
 #undef VE_WG_CASE
     return hipErrorInvalidValue;

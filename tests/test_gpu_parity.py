@@ -146,7 +146,7 @@ FORM_TENSORS = [
 ]
 
 
-@pytest.mark.parametrize("shape", [(256, 8), (512, 4), (1024, 2), (1024, 8), (512, 16)])
+@pytest.mark.parametrize("shape", [(256, 8), (512, 4), (1024, 2), (1024, 8), (512, 16), (512, 24)])
 def test_workgroup_access_forms(shape):
     ve = _ve()
     lay = plan_p0(FORM_TENSORS, 2)
@@ -157,6 +157,71 @@ def test_workgroup_access_forms(shape):
         assert (ve.get_option("wg_threads"), ve.get_option("wg_gpt")) == shape
         _run_parity(cfg, lay, [0, 1], 2, tally)
     tally.check()
+
+
+# The row-block shapes of one workgroup per CU (512 threads, 14 to 24 groups
+# per thread) run persistent: each workgroup takes blocks from the rank's
+# ticket counter and brings the next contiguous block's gradient and codes
+# into LDS during its own phase 2.  Enough blocks that every workgroup runs
+# many of them, with staged rows (spans of a multiple of 16 elements),
+# contiguous rows that are not staged, tiles and general blocks mixed in one
+# launch; three steps in a row also check that each launch leaves the
+# counters at zero for the next.
+DYN_TENSORS = [
+    TensorDef("rows", 1536, 2048, 2, 2048),      # 4,096-element rows: staged
+    TensorDef("rows8", 1200, 1000, 5, 1000),     # 5,000-element rows: 5,000 % 16 = 8, not staged
+    TensorDef("tile", 512, 512, 64, 128),        # 64x128 tiles
+    TensorDef("odd", 50, 102, 25, 102),          # partial last chunk: general form
+]
+
+
+@pytest.mark.parametrize("shape", [(512, 14), (512, 16), (512, 20), (512, 24)])
+def test_persistent_row_shapes(shape):
+    ve = _ve()
+    lay = plan_p0(DYN_TENSORS, 2)
+    assert max(t.block_rows * t.block_cols for t in DYN_TENSORS) <= 4 * shape[0] * shape[1]
+    cfg = Config("dyn", list(DYN_TENSORS), fsdp=2, grad_scale=1e-3, steps=3)
+    tally = Tally(cfg.name)
+    with ve.options(wg_threads=shape[0], wg_gpt=shape[1], wg_dynamic=1):
+        _run_parity(cfg, lay, [0, 1], 3, tally)
+    tally.check()
+
+
+def test_persistent_equals_one_shot():
+    """Three buckets in one call, persistent form against the one-shot
+    launch (wg_dynamic=0) on copies of the same states: bit-identical over
+    two steps."""
+    import torch
+    ve = _ve()
+    lay = plan_p0(DYN_TENSORS, 2)
+    cfg = Config("dyn", list(DYN_TENSORS), fsdp=2, grad_scale=1e-3, steps=2)
+    plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
+    hp = hp32()
+    r = 1
+    sets = []
+    for _ in range(2):
+        probs = [RankProblem(ve, cfg, lay, plan, r, bucket=b) for b in range(3)]
+        states = []
+        for p in probs:
+            p.set_grads(1)
+            st = {k: b.view for k, b in p.buf.items()}
+            st["grad_table"] = p.gt
+            states.append(st)
+        sets.append((probs, ve.state_table(plan, r, states)))
+    _say("[gpu] dyn x3 persistent vs one-shot, 512 x 16")
+    with ve.options(wg_threads=512, wg_gpt=16):
+        for t in (1, 2):
+            with ve.options(wg_dynamic=1):
+                plan.step(r, sets[0][1], hp, t)
+            with ve.options(wg_dynamic=0):
+                plan.step(r, sets[1][1], hp, t)
+    torch.cuda.synchronize()
+    for p, q in zip(sets[0][0], sets[1][0]):
+        a, b = p.download(), q.download()
+        for k in a:
+            assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+        assert p.guards_intact() and q.guards_intact()
+    plan.close()
 
 
 # A rank holding the end of one tensor and rows of another with smaller
