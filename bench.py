@@ -440,14 +440,29 @@ def _grid(r):
     return int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
 
 
-def _step_dispatches(rows):
-    """The step-kernel rows of the launch that covers every bucket: kernels
-    named k_step_*, at the largest grid among them."""
+def _step_dispatches(rows, weight):
+    """The step-kernel rows of the launch that covers every bucket: among
+    kernels named k_step_*, the one with the largest total `weight` (duration
+    or counter value), at its largest grid (a persistent kernel's grid does
+    not grow with the work, so the grid alone cannot pick it)."""
     st = [r for r in rows if "k_step" in r["Kernel_Name"]]
     if not st:
         raise SystemExit("no k_step_* kernel in the profile")
-    big = max(_grid(r) for r in st)
-    return [r for r in st if _grid(r) == big]
+    tot = {}
+    for r in st:
+        tot[r["Kernel_Name"]] = tot.get(r["Kernel_Name"], 0.0) + weight(r)
+    name = max(tot, key=tot.get)
+    mine = [r for r in st if r["Kernel_Name"] == name]
+    big = max(_grid(r) for r in mine)
+    return [r for r in mine if _grid(r) == big]
+
+
+def _duration(r):
+    return float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+
+
+def _counter(r):
+    return float(r["Counter_Value"])
 
 
 def summarize_counters(args):
@@ -469,8 +484,8 @@ def summarize_counters(args):
 
     fx, fc = calib(f_rows)
     wx, wc = calib(w_rows)
-    fs = _step_dispatches(f_rows)
-    ws = _step_dispatches(w_rows)
+    fs = _step_dispatches(f_rows, _counter)
+    ws = _step_dispatches(w_rows, _counter)
     kernel = fs[0]["Kernel_Name"]
     fk = statistics.mean(float(r["Counter_Value"]) for r in fs)
     wk = statistics.mean(float(r["Counter_Value"]) for r in ws)
@@ -542,8 +557,11 @@ def summarize_trace(args):
     import statistics
     stats = _csv_rows(os.path.join(args.trace_dir, "run_kernel_stats.csv"))
     trace = _csv_rows(os.path.join(args.trace_dir, "run_kernel_trace.csv"))
-    st = _step_dispatches(trace)
+    st = sorted(_step_dispatches(trace, _duration), key=lambda r: int(r["Start_Timestamp"]))
     kernel = st[0]["Kernel_Name"]
+    if args.skip_first >= len(st):
+        raise SystemExit(f"--skip-first {args.skip_first} leaves none of {len(st)} step dispatches")
+    skipped, st = len(st[:args.skip_first]), st[args.skip_first:]
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in st]
     avg = statistics.mean(durs)
     alg, nbk, nv, nb, S = _workload_alg(args.workload, args.buckets)
@@ -555,7 +573,9 @@ def summarize_trace(args):
         t.append(f"{r['Name'][:72]:72s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
                  f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f}")
     t += ["", f"step: {kernel}",
-          f"  all-bucket launches: average {avg:.1f} us over {len(durs)} dispatches (min {min(durs):.1f}, "
+          f"  all-bucket launches: average {avg:.1f} us over {len(durs)} dispatches"
+          + (f" (the first {skipped}, bench.py's warm-up steps, left out)" if skipped else "")
+          + f" (min {min(durs):.1f}, "
           f"max {max(durs):.1f}); algorithmic bytes per launch {alg / 1e9:.4f} GB -> {alg / avg / 1e3:.1f} GB/s "
           f"= {alg / avg / 1e3 / HBM_PEAK_GBS * 100:.1f}% of 8 TB/s"]
     if args.bench_log and os.path.exists(args.bench_log):
@@ -650,6 +670,8 @@ def main():
     sm.add_argument("--trace-dir", help="trace: output folder of the --kernel-trace --stats run")
     sm.add_argument("--command", default="", help="trace: the profiled command, for the record")
     sm.add_argument("--bench-log", default=None, help="trace: bench.py's stderr of the profiled run")
+    sm.add_argument("--skip-first", type=int, default=0,
+                    help="trace: leave out the first N step dispatches (the profiled run's --warmup)")
     sm.add_argument("--out", default=None, help="trace: summary file to write")
     sm.add_argument("--top", type=int, default=16, help="trace: kernels listed")
     sm.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"),

@@ -113,6 +113,7 @@ typedef struct {
  * fail.  VE_ERR_UNSUPPORTED: a block of more than 2^30 elements.
  * device == -1 builds a host-only plan: validation, ve_plan_query and
  * ve_dbuffer_slice work, kernel entry points return VE_ERR_INVALID_ARG.
+ * The device tables also hold 64 bytes of step scheduler counters per rank.
  * On success *out owns the tables until ve_plan_free. */
 ve_status ve_plan_load(const ve_tensor_spec* specs, int32_t n_tensors, int32_t fsdp_size,
                        int64_t shard_elems, int32_t device, ve_plan** out);
@@ -145,7 +146,12 @@ ve_status ve_dbuffer_copy_in(const ve_plan* plan, int32_t rank, const uint16_t* 
  * moments with a new absmax scale (scale = amax/127, code =
  * clamp(rint(x*127/amax), -127, 127); amax 0 gives scale 0 and code 0).
  * Padding of grad_shard and param_shard is written 0; master and the codes
- * at padding are not touched. */
+ * at padding are not touched.
+ * Blocks of the row-block shapes are handed out to persistent workgroups by
+ * two counters that the plan holds per rank (zero between launches): calls
+ * for one plan and rank must not overlap in time (issue them on one stream,
+ * or order the streams); calls for different ranks or plans may.  With the
+ * option "wg_dynamic" at 0 the step uses no counters. */
 ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_shard_state* states,
                                  int32_t n_states, const ve_adam_hparams* hp, int64_t step,
                                  void* stream);
@@ -201,9 +207,15 @@ ve_status ve_dbuffer_group_op(const ve_plan* plan, int32_t rank, int32_t op, flo
  *       round of tiles along K;
  *   "gemm_cfg" (VE_GEMM_CFG, -1): pin a product configuration (0, 2: register
  *       staged 128^2 / 256^2 tiles; 6, 9: direct-to-LDS 4 waves of 128^2 /
- *       8 waves of 128x64); -1 = chosen by shape;
+ *       8 waves of 128x64; 13: 8 waves of 128x64, P direct to LDS in three
+ *       stages, Q through registers); -1 = chosen by shape;
  *   "gemm_xcd" (VE_GEMM_XCD, 1): 0 = plain tile order instead of the
- *       XCD-aware one.
+ *       XCD-aware one;
+ *   "wg_dynamic" (VE_WG_DYNAMIC, 1): 0 = the step's row-block shapes
+ *       (512 threads, 14 to 24 groups per thread) launch one workgroup per
+ *       block instead of one persistent workgroup per CU taking blocks from
+ *       the plan's per-rank counters (same results, slower; no restriction
+ *       on overlapping calls, see ve_shard_adam8bit_step).
  * ve_set_option changes a value for every later call of the process
  * (calls already queued are unaffected); ve_get_option reads it.  Errors:
  * an unknown name or a NULL value pointer gives VE_ERR_INVALID_ARG. */

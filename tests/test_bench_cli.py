@@ -94,6 +94,32 @@ def test_summarize_trace_averages_the_all_bucket_step_launches(tmp_path):
     assert f"{alg / 1100.0 / 1e3:.1f} GB/s" in txt
 
 
+def test_summarize_trace_picks_the_persistent_step_kernel_by_time(tmp_path):
+    """A persistent step kernel's grid is one workgroup per CU whatever the
+    work; a short small-block launch of the same step has a larger grid.
+    The step kernel is the one with the most time."""
+    dyn = "void ve::(anonymous namespace)::k_step_dyn<16>(ve::StepArgs, unsigned int, unsigned int)"
+    small = "void ve::(anonymous namespace)::k_step_small<true>(ve::StepArgs)"
+    rows = []
+    for i in range(3):
+        rows.append(_trace_row(dyn, 3000 * i, 1600 + 100 * i, 256 * 512))
+        rows.append(_trace_row(small, 3000 * i + 2000, 8, 4096 * 256))
+    _write_csv(str(tmp_path / "kt" / "run_kernel_trace.csv"), rows)
+    _write_csv(str(tmp_path / "kt" / "run_kernel_stats.csv"),
+               [{"Name": dyn, "Calls": 3, "AverageNs": 1700000, "MinNs": 1600000, "MaxNs": 1800000},
+                {"Name": small, "Calls": 3, "AverageNs": 8000, "MinNs": 8000, "MaxNs": 8000}])
+    out = tmp_path / "s.txt"
+    _summarize("trace", "--workload", "llama", "--trace-dir", str(tmp_path / "kt"), "--command", "cmd",
+               "--out", str(out))
+    txt = out.read_text()
+    assert "step: " + dyn in txt
+    assert "average 1700.0 us over 3 dispatches" in txt
+    # the warm-up dispatches can be left out (bench.py's --warmup)
+    _summarize("trace", "--workload", "llama", "--trace-dir", str(tmp_path / "kt"), "--command", "cmd",
+               "--out", str(out), "--skip-first", "1")
+    assert "average 1750.0 us over 2 dispatches (the first 1" in out.read_text()
+
+
 def test_summarize_counters_calibrates_against_the_streaming_copy(tmp_path):
     import json
     import bench
