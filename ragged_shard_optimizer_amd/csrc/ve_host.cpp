@@ -333,9 +333,12 @@ int64_t set_inline(StepArgs& a, const RankTables& rt, const HostWork& w, size_t 
 // Measured on MI355X over the model workloads:
 //   2,049 .. 4,096 groups (128x128 tiles): 1024 threads x 4 (two resident
 //     workgroups per CU) beat 512 x 8 by ~2%;
-//   4,097 .. 12,288 groups (row blocks of 16K..48K elements): 512 threads
-//     with 16 (up to 8,192 groups), 20 or 24 groups each beat 1024 threads
-//     by 1-2%, even with idle lanes in the last slot;
+//   4,097 .. 12,288 groups (row blocks of 16K..48K elements), persistent
+//     form: the shape with the fewest idle lanes, then the most threads.
+//     28,672-element rows: 1024 x 7 5.95 TB/s, 512 x 14 5.90, 512 x 16 and
+//     768 x 10 5.85; 46,080-element rows: 768 x 15 5.61, 512 x 24 5.57.
+//     With the persistent form off (option wg_dynamic = 0): 512 threads
+//     with 16, 20 or 24 groups, which beat 1024 threads there by 1-2%;
 //   larger: 1024 threads x 14 / 16;
 //   up to 2,048 groups: the largest workgroup that gives each thread at
 //     least 6 groups (fewer leave the per-block prologue exposed), else 256.
@@ -358,6 +361,24 @@ void wg_shape(int32_t groups, int& threads, int& gpt) {
         threads = 1024;
         gpt = g;
         return;
+    }
+    if (groups > 4096 && groups <= 12288 && option(kOptWgDynamic) != 0) {
+        // idle fraction (t * g - groups) / (t * g), compared as fractions
+        int64_t bt = 0, bg = 0;
+        auto better = [&](int64_t t, int64_t gg) {
+            if (bt == 0) return true;
+            const int64_t a = (t * gg - groups) * (bt * bg), b = (bt * bg - groups) * (t * gg);
+            return a < b || (a == b && t > bt);
+        };
+#define VE_WG_CASE(T, G) \
+        if (dyn_shape(T, G) && (int64_t)(T) * (G) >= groups && better(T, G)) { bt = T; bg = G; }
+        VE_WG_SHAPES(VE_WG_CASE)
+#undef VE_WG_CASE
+        if (bt > 0) {
+            threads = (int)bt;
+            gpt = (int)bg;
+            return;
+        }
     }
     if (groups > 4096 && groups <= 12288 && fit(512, 16, g)) {
         threads = 512;

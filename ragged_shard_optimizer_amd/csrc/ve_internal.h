@@ -21,7 +21,12 @@ constexpr int kWgChunk = 4;
 // workgroup.
 constexpr int kSmallMaxChunks = 64;
 constexpr int kWgMaxThreads = 1024;
-constexpr int kDynMinGpt = 14;  // persistent step form: 512-thread shapes from 14 groups per thread
+// Workgroup shapes of the step that run in the persistent form (one
+// workgroup per CU taking blocks from a ticket counter).
+constexpr bool dyn_shape(int threads, int gpt) {
+    // (1024 x 12 and more spill registers in that form)
+    return (threads == 512 && gpt >= 14) || threads == 768 || (threads == 1024 && gpt >= 7 && gpt <= 10);
+}
 constexpr size_t kSchedStride = 64;  // bytes of scheduler counters per rank in a plan's device tables
 
 // Instantiated workgroup shapes (threads, 4-element groups per thread).  The
@@ -31,7 +36,8 @@ constexpr size_t kSchedStride = 64;  // bytes of scheduler counters per rank in 
     X(256, 1) X(256, 2) X(256, 4) X(256, 8) X(256, 12) X(256, 16) X(256, 24) X(256, 32)         \
     X(512, 2) X(512, 4) X(512, 6) X(512, 8) X(512, 10) X(512, 12) X(512, 14) X(512, 16)         \
     X(512, 20) X(512, 24)                                                                       \
-    X(1024, 2) X(1024, 4) X(1024, 6) X(1024, 8) X(1024, 10) X(1024, 12) X(1024, 14) X(1024, 16)
+    X(768, 10) X(768, 15)                                                                       \
+    X(1024, 2) X(1024, 4) X(1024, 6) X(1024, 7) X(1024, 8) X(1024, 10) X(1024, 12) X(1024, 14) X(1024, 16)
 constexpr int64_t kWgMaxGroups = 1024 * 16;
 // The workgroup-path kernels take their segment table in the kernel
 // arguments (read through the scalar cache), so a workgroup finds its block

@@ -1158,8 +1158,9 @@ __global__ void __launch_bounds__(256) k_step_huge(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Persistent form for the shapes of one workgroup per CU (512 threads, 14 to
-// 24 groups per thread: row blocks of 28K to 49K elements).  The grid holds
+// Persistent form for the shapes of one workgroup per CU (dyn_shape(): 512
+// threads from 14 groups per thread, 768 threads, 1024 threads with 7 to 10:
+// row blocks of 28K elements and more).  The grid holds
 // one workgroup per CU and every workgroup takes its blocks from a ticket
 // counter, one relaxed device-scope add per block, so a CU that finishes
 // early takes the next block as the hardware dispatcher would, without the
@@ -1181,19 +1182,31 @@ __global__ void __launch_bounds__(256) k_step_huge(StepArgs a) {
 // replay) starts from zero.  Launches that overlap in time must not share
 // the counters.
 #ifndef VE_DYN_SLOTS
-#define VE_DYN_SLOTS 16  // staged register slots (8 KiB of LDS each)
+#define VE_DYN_SLOTS 16  // at most this many staged register slots (T x 16 bytes of LDS each)
 #endif
 #ifndef VE_DYN_DMA_AT
 #define VE_DYN_DMA_AT 8  // phase-2 group before which the next block's loads go out
 #endif
-constexpr int kDynThreads = 512;
+#ifndef VE_DYN_LDS_KIB
+#define VE_DYN_LDS_KIB 156  // staging budget of the 160 KiB of LDS
+#endif
+constexpr int kDynLdsBytes = VE_DYN_LDS_KIB * 1024;
 
-template <int GPT>
+template <int T, int GPT>
 struct DynCfg {
-    static constexpr int PF = GPT < VE_DYN_SLOTS ? GPT : VE_DYN_SLOTS;  // staged slots
-    static constexpr int SPAN = PF * kDynThreads * kWgChunk;           // staged elements
-    static constexpr int LDS = 4 * SPAN;  // gradient (2 B) + m and v codes (1 B each) per element
+    static constexpr int SLOT_BYTES = T * kWgChunk * 4;  // gradient (2 B) + m and v codes (1 B each) per element
+    static constexpr int FIT = kDynLdsBytes / SLOT_BYTES;
+    static constexpr int PF0 = GPT < VE_DYN_SLOTS ? GPT : VE_DYN_SLOTS;
+    static constexpr int PF = PF0 < FIT ? PF0 : FIT;  // staged slots
+    static constexpr int SPAN = PF * T * kWgChunk;    // staged elements
+    static constexpr int LDS = PF * SLOT_BYTES;
     static constexpr int DMA_AT = VE_DYN_DMA_AT < GPT ? VE_DYN_DMA_AT : GPT - 1;
+    // master loads in flight ahead of their update: 8 from 12 groups per
+    // thread (more spill registers at 768 threads), else 6 (1024 x 7: 0.4%
+    // faster than 4), at most GPT
+    static constexpr int MA0 = GPT >= 12 ? 8 : 6;
+    static constexpr int MA = MA0 < GPT ? MA0 : GPT;
+    static_assert(T % 256 == 0, "waves split evenly into gradient, m and v pieces");
 };
 
 // The fields of a block that the staged path uses (a WgItem's LINEAR subset:
@@ -1231,20 +1244,22 @@ __device__ __forceinline__ DynItem dyn_item(const StepArgs& a, uint32_t w, uint3
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Stage block `nt`'s first PF register slots (in its rotated slot order) into
-// LDS: slot c's gradient at [c * 4 KiB], its m codes at [2 SPAN + c * 2 KiB],
-// its v codes at [3 SPAN + c * 2 KiB].  Wave w moves the 1 KiB piece w of
-// every slot (pieces 0-3 gradient, 4-5 m codes, 6-7 v codes), 16 bytes per
-// lane; reads past the block's span return zeros, which no lane uses.
-template <int GPT>
+// LDS: slot c's gradient at [c * T * 8], its m codes at [2 SPAN + c * T * 4],
+// its v codes at [3 SPAN + c * T * 4].  A slot is T / 64 pieces of 1 KiB, one
+// per wave: the first half of the waves move its gradient, the next quarter
+// its m codes, the last quarter its v codes, 16 bytes per lane; reads past
+// the block's span return zeros, which no lane uses.
+template <int T, int GPT>
 __device__ __forceinline__ void dyn_stage(const DynItem& nt, uint8_t* sb) {
-    constexpr int T = kDynThreads;
-    constexpr int PF = DynCfg<GPT>::PF, SPAN = DynCfg<GPT>::SPAN;
+    constexpr int W = T / 64;
+    constexpr int PF = DynCfg<T, GPT>::PF, SPAN = DynCfg<T, GPT>::SPAN;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const __amdgpu_buffer_rsrc_t r = wave < 4 ? nt.fb.grad : (wave < 6 ? nt.fb.m_q : nt.fb.v_q);
-    const int piece = wave < 4 ? wave : (wave < 6 ? wave - 4 : wave - 6);
-    const int esz = wave < 4 ? 2 : 1;
-    const int base = wave < 4 ? 0 : (wave < 6 ? 2 * SPAN : 3 * SPAN);
+    const bool gw = wave < W / 2, mw = !gw && wave < 3 * W / 4;
+    const __amdgpu_buffer_rsrc_t r = gw ? nt.fb.grad : (mw ? nt.fb.m_q : nt.fb.v_q);
+    const int piece = gw ? wave : (mw ? wave - W / 2 : wave - 3 * W / 4);
+    const int esz = gw ? 2 : 1;
+    const int base = gw ? 0 : (mw ? 2 * SPAN : 3 * SPAN);
 #pragma unroll
     for (int c = 0; c < PF; ++c) {
         const int k = (c + nt.rot) % GPT;
@@ -1257,15 +1272,14 @@ __device__ __forceinline__ void dyn_stage(const DynItem& nt, uint8_t* sb) {
 // One staged or unstaged block: phase 1, absmax, phase 2.  The next ticket is
 // taken during phase 1 and the next block staged during phase 2 when
 // possible; returns the next ticket and sets stage_next.
-template <int GPT, bool STAGED>
+template <int T, int GPT, bool STAGED>
 __device__ __forceinline__ uint32_t dyn_block(const DynItem& it, const StepArgs& A, uint32_t nx, uint32_t nitems,
                                               bool& stage_next, uint32_t* s_next, uint8_t* sb,
-                                              float (&red)[2][kDynThreads / 64]) {
-    constexpr int T = kDynThreads;
+                                              float (&red)[2][T / 64]) {
     constexpr int CH = kWgChunk;
     constexpr int MODE = kWgLinear;
-    constexpr int PF = DynCfg<GPT>::PF, SPAN = DynCfg<GPT>::SPAN, DMA_AT = DynCfg<GPT>::DMA_AT;
-    constexpr int MA = WgAhead<GPT, MODE>::value;
+    constexpr int PF = DynCfg<T, GPT>::PF, SPAN = DynCfg<T, GPT>::SPAN, DMA_AT = DynCfg<T, GPT>::DMA_AT;
+    constexpr int MA = DynCfg<T, GPT>::MA;
     constexpr bool LATE = WgLateCopy<T, GPT>::value;
     const StepScalars& sc = A.sc;
     const int tid = threadIdx.x;
@@ -1335,7 +1349,7 @@ __device__ __forceinline__ uint32_t dyn_block(const DynItem& it, const StepArgs&
     for (int c = 0; c < GPT; ++c) {
         if (c == DMA_AT) {
             __builtin_amdgcn_sched_barrier(0);
-            if (stage_next) dyn_stage<GPT>(nt, sb);
+            if (stage_next) dyn_stage<T, GPT>(nt, sb);
             __builtin_amdgcn_sched_barrier(0);
         }
         make_opaque(x[c]);
@@ -1345,15 +1359,14 @@ __device__ __forceinline__ uint32_t dyn_block(const DynItem& it, const StepArgs&
     return wn;
 }
 
-template <int GPT>
-__global__ void __launch_bounds__(kDynThreads) k_step_dyn(StepArgs a, uint32_t nx, uint32_t nitems) {
-    constexpr int T = kDynThreads;
+template <int T, int GPT>
+__global__ void __launch_bounds__(T) k_step_dyn(StepArgs a, uint32_t nx, uint32_t nitems) {
     constexpr int GROUP_STORES = WgLateCopy<T, GPT>::value ? 3 : 2;  // phase-2 stores per group
-    constexpr int AFTER_DMA = GROUP_STORES * (GPT - DynCfg<GPT>::DMA_AT);
+    constexpr int AFTER_DMA = GROUP_STORES * (GPT - DynCfg<T, GPT>::DMA_AT);
     static_assert(AFTER_DMA <= 63, "vmcnt holds at most 63");
     __shared__ float s_red[2][T / 64];
     __shared__ uint32_t s_next;
-    __shared__ __attribute__((aligned(16))) uint8_t s_buf[DynCfg<GPT>::LDS];
+    __shared__ __attribute__((aligned(16))) uint8_t s_buf[DynCfg<T, GPT>::LDS];
     if (threadIdx.x == 0) s_next = atomicAdd(a.sched, 1u);
     __syncthreads();
     uint32_t w = s_next;
@@ -1371,8 +1384,8 @@ __global__ void __launch_bounds__(kDynThreads) k_step_dyn(StepArgs a, uint32_t n
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
             bool sn;
-            if (staged) wn = dyn_block<GPT, true>(it, a, nx, nitems, sn, &s_next, s_buf, s_red);
-            else wn = dyn_block<GPT, false>(it, a, nx, nitems, sn, &s_next, s_buf, s_red);
+            if (staged) wn = dyn_block<T, GPT, true>(it, a, nx, nitems, sn, &s_next, s_buf, s_red);
+            else wn = dyn_block<T, GPT, false>(it, a, nx, nitems, sn, &s_next, s_buf, s_red);
             staged = sn;
         } else {
             __builtin_amdgcn_s_waitcnt(0);
@@ -1417,11 +1430,11 @@ hipError_t launch_step_small(const StepArgs& a0, int n_states, hipStream_t s) {
 
 template <int T, int GPT>
 static hipError_t launch_wg_t(const StepArgs& a, int n_states, int dyn_grid, hipStream_t s) {
-    if constexpr (T == kDynThreads && GPT >= kDynMinGpt) {
+    if constexpr (dyn_shape(T, GPT)) {
         if (dyn_grid > 0) {
             const int64_t items = a.work.total * n_states;
-            hipLaunchKernelGGL((k_step_dyn<GPT>), dim3((unsigned)dyn_grid), dim3(T), 0, s, a, (uint32_t)a.work.total,
-                               (uint32_t)items);
+            hipLaunchKernelGGL((k_step_dyn<T, GPT>), dim3((unsigned)dyn_grid), dim3(T), 0, s, a,
+                               (uint32_t)a.work.total, (uint32_t)items);
             return hipGetLastError();
         }
     }
@@ -1436,7 +1449,7 @@ bool wg_config_supported(int threads, int gpt) {
     return false;
 }
 
-bool wg_dynamic_shape(int threads, int gpt) { return threads == kDynThreads && gpt >= kDynMinGpt; }
+bool wg_dynamic_shape(int threads, int gpt) { return dyn_shape(threads, gpt); }
 
 hipError_t launch_step_wg(const StepArgs& a, int n_states, int threads, int gpt, int dyn_grid, hipStream_t s) {
 #define VE_WG_CASE(T, G) if (threads == T && gpt == G) return launch_wg_t<T, G>(a, n_states, dyn_grid, s);

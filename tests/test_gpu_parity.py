@@ -146,7 +146,8 @@ FORM_TENSORS = [
 ]
 
 
-@pytest.mark.parametrize("shape", [(256, 8), (512, 4), (1024, 2), (1024, 8), (512, 16), (512, 24)])
+@pytest.mark.parametrize("shape", [(256, 8), (512, 4), (1024, 2), (1024, 8), (512, 16), (512, 24), (768, 15),
+                                   (1024, 7)])
 def test_workgroup_access_forms(shape):
     ve = _ve()
     lay = plan_p0(FORM_TENSORS, 2)
@@ -159,8 +160,9 @@ def test_workgroup_access_forms(shape):
     tally.check()
 
 
-# The row-block shapes of one workgroup per CU (512 threads, 14 to 24 groups
-# per thread) run persistent: each workgroup takes blocks from the rank's
+# The row-block shapes of one workgroup per CU (512 threads with 14 to 24
+# groups per thread, 768 threads, 1024 threads with 7 to 10) run persistent:
+# each workgroup takes blocks from the rank's
 # ticket counter and brings the next contiguous block's gradient and codes
 # into LDS during its own phase 2.  Enough blocks that every workgroup runs
 # many of them, with staged rows (spans of a multiple of 16 elements),
@@ -175,7 +177,8 @@ DYN_TENSORS = [
 ]
 
 
-@pytest.mark.parametrize("shape", [(512, 14), (512, 16), (512, 20), (512, 24)])
+@pytest.mark.parametrize("shape", [(512, 14), (512, 16), (512, 20), (512, 24), (768, 10), (768, 15), (1024, 7),
+                                   (1024, 10)])
 def test_persistent_row_shapes(shape):
     ve = _ve()
     lay = plan_p0(DYN_TENSORS, 2)
