@@ -682,15 +682,13 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
             const int64_t nb = set_inline(a, rt, rt.wg, i0, i1);
             i0 = i1;
             if (nb == 0) continue;
-            // Row-block shapes of one workgroup per CU run persistent, with
-            // one workgroup per CU taking blocks from the rank's counters
-            // (launches on one stream run one after another, so they share
-            // them); tickets stay below 2^31.
-            int dyn_grid = 0;
-            if (option(kOptWgDynamic) != 0 && wg_dynamic_shape(threads, gpt) &&
-                nb * n_states + plan->n_cu < (int64_t(1) << 31))
-                dyn_grid = (int)std::min<int64_t>(plan->n_cu, nb * n_states);
-            if ((st = launch_status(launch_step_wg(a, n_states, threads, gpt, dyn_grid, s), "workgroup step")) != VE_OK)
+            // Row-block shapes run persistent, the resident workgroups taking
+            // blocks from the rank's counters (launches on one stream run one
+            // after another, so they share them); tickets stay below 2^31.
+            const bool dyn = option(kOptWgDynamic) != 0 && wg_dynamic_shape(threads, gpt) &&
+                             nb * n_states + (int64_t)kDynMaxPerCu * plan->n_cu < (int64_t(1) << 31);
+            if ((st = launch_status(launch_step_wg(a, n_states, threads, gpt, dyn ? plan->n_cu : 0, s),
+                                    "workgroup step")) != VE_OK)
                 return st;
         }
     }

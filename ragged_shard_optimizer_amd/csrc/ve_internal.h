@@ -146,10 +146,12 @@ struct StepArgs {
 // Small-block step; a.pad's tiles (zero fill of grad_shard and param_shard)
 // run as extra workgroups of the same launch.
 hipError_t launch_step_small(const StepArgs& a, int n_states, hipStream_t s);
-// dyn_grid > 0 runs a shape that wg_dynamic_shape() accepts in its persistent
-// form with that many workgroups (one per CU), scheduled through a.sched.
-hipError_t launch_step_wg(const StepArgs& a, int n_states, int threads, int groups_per_thread, int dyn_grid,
+// dyn_cu > 0 (the device's CU count) runs a shape that wg_dynamic_shape()
+// accepts in its persistent form, as many workgroups as the CUs hold at once
+// (at most kDynMaxPerCu per CU), scheduled through a.sched.
+hipError_t launch_step_wg(const StepArgs& a, int n_states, int threads, int groups_per_thread, int dyn_cu,
                           hipStream_t s);
+constexpr int kDynMaxPerCu = 8;
 bool wg_dynamic_shape(int threads, int groups_per_thread);
 hipError_t launch_step_huge(const StepArgs& a, int n_states, hipStream_t s);
 // Copy-in: out = bucket; grad pointers from `grad_ptrs`.

@@ -1429,12 +1429,21 @@ hipError_t launch_step_small(const StepArgs& a0, int n_states, hipStream_t s) {
 }
 
 template <int T, int GPT>
-static hipError_t launch_wg_t(const StepArgs& a, int n_states, int dyn_grid, hipStream_t s) {
+static hipError_t launch_wg_t(const StepArgs& a, int n_states, int dyn_cu, hipStream_t s) {
     if constexpr (dyn_shape(T, GPT)) {
-        if (dyn_grid > 0) {
+        if (dyn_cu > 0) {
+            // resident workgroups per CU of the persistent kernel (its LDS and
+            // registers decide), read once per process
+            static const int occ = [] {
+                int n = 0;
+                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_step_dyn<T, GPT>, T, 0) != hipSuccess || n < 1)
+                    n = 1;
+                return n < kDynMaxPerCu ? n : kDynMaxPerCu;
+            }();
             const int64_t items = a.work.total * n_states;
-            hipLaunchKernelGGL((k_step_dyn<T, GPT>), dim3((unsigned)dyn_grid), dim3(T), 0, s, a,
-                               (uint32_t)a.work.total, (uint32_t)items);
+            const int64_t grid = std::min<int64_t>(items, (int64_t)dyn_cu * occ);
+            hipLaunchKernelGGL((k_step_dyn<T, GPT>), dim3((unsigned)grid), dim3(T), 0, s, a, (uint32_t)a.work.total,
+                               (uint32_t)items);
             return hipGetLastError();
         }
     }
