@@ -227,6 +227,47 @@ def test_persistent_equals_one_shot():
     plan.close()
 
 
+def test_persistent_step_replays_in_a_captured_graph():
+    """Each persistent launch's last workgroup resets the rank's counters, so
+    a captured step replays: three replays, with eager steps of another
+    bucket on the same plan and rank in between, each bit-identical to an
+    eager step of a twin bucket."""
+    import torch
+    ve = _ve()
+    lay = plan_p0(DYN_TENSORS, 2)
+    cfg = Config("dyn", list(DYN_TENSORS), fsdp=2, grad_scale=1e-3, steps=2)
+    plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
+    hp = hp32()
+    r = 1
+    # cap and twin: two copies of bucket 0's state and gradients
+    cap, twin, other = (RankProblem(ve, cfg, lay, plan, r, bucket=b) for b in (0, 0, 1))
+    cap.set_grads(1)
+    twin.set_grads(1)
+    other.set_grads(2)
+    torch.cuda.synchronize()
+    a, b = cap.download(), twin.download()
+    assert all(np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)) for k in a)
+    with ve.options(wg_threads=512, wg_gpt=16, wg_dynamic=1):
+        _say("[gpu] dyn 512 x 16 step captured in a graph")
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        with torch.cuda.graph(g, stream=side):
+            plan.step(r, cap.table, hp, 3)
+        torch.cuda.synchronize()
+        for i in range(3):
+            _say(f"[gpu] replay {i}")
+            g.replay()
+            plan.step(r, twin.table, hp, 3)
+            plan.step(r, other.table, hp, 4 + i)
+            torch.cuda.synchronize()
+            a, b = cap.download(), twin.download()
+            for k in a:
+                assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), (i, k)
+    assert cap.guards_intact() and twin.guards_intact() and other.guards_intact()
+    del g
+    plan.close()
+
+
 # A rank holding the end of one tensor and rows of another with smaller
 # blocks takes one launch per block shape (llama_mini rank 4: 3,584- and
 # 1,024-element rows; llama_rowblk rank 20: 28,672-element rows of `down`,
