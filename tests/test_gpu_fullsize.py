@@ -120,6 +120,39 @@ def test_full_size_sampled(name, which):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("name", ["llama", "gptoss"])
+def test_full_size_persistent_equals_one_shot(name):
+    """Every element of every bucket on the benchmark's rank: the persistent,
+    ticket-scheduled step (the default for these row blocks) against the
+    one-shot launch (wg_dynamic = 0) on copies of the same states, two steps,
+    bit-identical.  The sampled test above checks the persistent form against
+    the oracle at these sizes; this one reaches every block it schedules."""
+    import torch
+    import ragged_shard_optimizer_amd as ve
+    cfg, lay = layout_of(name)
+    rank = lay.largest_rank()
+    plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
+    hp = hp32()
+    buckets = device_buckets(cfg, lay, rank, DEV)
+    _say(f"[gpu] full-size {name}: rank {rank}, {len(buckets)} buckets, persistent vs one-shot")
+    dyn = [ve.new_state(plan, rank, ve.grad_pointer_table(g, DEV), m) for g, m in buckets]
+    one = [ve.new_state(plan, rank, ve.grad_pointer_table(g, DEV), m.clone()) for g, m in buckets]
+    t_dyn, t_one = ve.state_table(plan, rank, dyn), ve.state_table(plan, rank, one)
+    keys = ("grad_shard", "master", "m_q", "v_q", "m_scale", "v_scale", "param_shard")
+    for t in (1, 2):
+        with ve.options(wg_dynamic=1):
+            plan.step(rank, t_dyn, hp, t)
+        with ve.options(wg_dynamic=0):
+            plan.step(rank, t_one, hp, t)
+        torch.cuda.synchronize()
+        for b, (x, y) in enumerate(zip(dyn, one)):
+            for k in keys:
+                assert torch.equal(x[k], y[k]), (name, t, b, k)
+    del dyn, one, t_dyn, t_one, buckets
+    plan.close()
+    torch.cuda.empty_cache()
+
+
 def test_adversarial_whole_bucket_copy_in():
     """Copy-in of the whole adversarial bucket (10,000 tensors, ~2.9 GB
     moved): every tensor lands at its offset bit for bit, all padding zero."""
