@@ -42,11 +42,40 @@ GROUP_SOURCES = ("ve_group.hip", "ve_device.h", "ve_internal.h", "ve_host.cpp")
 MUON_SOURCES = ("ve_muon.hip", "ve_muon.h", "ve_muon_host.cpp", "ve_device.h", "ve_internal.h")
 
 
+def strip_comments(src: str) -> str:
+    """C/C++ source without its comments, each run of blank space made one
+    space: what the compiler sees, up to layout.  String and character
+    literals are kept as they are."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(files=STEP_SOURCES):
+    """Hash of the kernel sources with comments and layout removed, so that
+    a profile stays valid across comment edits and is dropped by any code
+    change."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "ragged_shard_optimizer_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "ragged_shard_optimizer_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(strip_comments(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

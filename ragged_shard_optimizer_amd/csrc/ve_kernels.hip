@@ -19,6 +19,10 @@
 //   phase 2  recompute the moments from the registers, quantise with the new
 //            scale, write the codes.
 //
+// Row blocks of 16K to 49K elements run a persistent form of the wg class
+// (k_step_dyn): one workgroup per CU takes blocks from a ticket counter and
+// stages the next block's gradient and codes in LDS during its own phase 2.
+//
 // Block-size classes (decided per rank segment at plan load):
 //   small  <= 64 chunks of kSmallChunk (4) elements: a group of G (power of
 //          two) lanes of one wave owns a block, one chunk per lane, 64/G
@@ -1158,22 +1162,24 @@ __global__ void __launch_bounds__(256) k_step_huge(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Persistent form for the shapes of one workgroup per CU (dyn_shape(): 512
-// threads from 14 groups per thread, 768 threads, 1024 threads with 7 to 10:
-// row blocks of 28K elements and more).  The grid holds
-// one workgroup per CU and every workgroup takes its blocks from a ticket
-// counter, one relaxed device-scope add per block, so a CU that finishes
-// early takes the next block as the hardware dispatcher would, without the
-// gap between one workgroup's end and the next one's start.  A block that is
-// one contiguous FAST run is staged: the block before it on the same CU
-// brings its gradient and both code streams (4 of its 8 input bytes per
-// element, up to kDynSlots register slots of them) into LDS with
-// buffer-to-LDS loads issued in the middle of its own phase 2, so the CU
-// keeps HBM requests in flight through its reduction tail and the block
-// switch.  Measured on MI355X against the one-shot kernel, outputs
-// bit-identical: 28,672-element rows 5.47-5.52 -> 5.88 TB/s, 46,080-element
-// rows 5.28-5.31 -> 5.54 TB/s (dynamic tickets alone: 5.72 and 5.46).  A
-// persistent form with a static block order (block i on workgroup i mod
+// Persistent form for the row-block shapes (dyn_shape(): 512 threads from 14
+// groups per thread, 768 threads, 1024 threads with 7 to 10: row blocks of
+// 16K to 49K elements).  The grid holds as many workgroups as the CUs keep
+// resident (one per CU here: the LDS staging area takes 114-156 KiB) and
+// every workgroup takes its blocks from a ticket counter, one relaxed
+// device-scope add per block, so a CU that finishes early takes the next
+// block as the hardware dispatcher would, without the gap between one
+// workgroup's end and the next one's start.  A block that is one contiguous
+// FAST run, its span a multiple of 16 elements, is staged: the block before
+// it on the same CU brings its gradient and both code streams (4 of its 8
+// input bytes per element, as many register slots as fit the LDS budget)
+// into LDS with buffer-to-LDS loads issued in the middle of its own phase 2,
+// so the CU keeps HBM requests in flight through its reduction tail and the
+// block switch.  Measured on MI355X in one process, outputs bit-identical to
+// the one-shot kernel: 28,672-element rows 5.43-5.52 TB/s one-shot (512 x
+// 16), 5.72 with tickets alone, 5.88 staged, 5.95 staged in 1024 x 7;
+// 46,080-element rows 5.28-5.31 (512 x 24), 5.46, 5.54, 5.61 in 768 x 15.
+// A persistent form with a static block order (block i on workgroup i mod
 // grid) ran 4% below the one-shot kernel, staged or not: the slowest CUs set
 // the end.
 //

@@ -170,3 +170,13 @@ def test_summarize_muon_per_call_times(tmp_path):
     assert f"8192 x 28672 (LLaMA-3-70B MLP), 5 steps: 2 timed calls, kernel time per call {big:.1f} us" in txt
     assert f"-> {bench.ns_flops(8192, 28672) / big / 1e6:.1f} TFLOP/s" in txt
     assert f"2048 x 7168 (DeepSeek-V3 routed expert), 5 steps: 2 timed calls, kernel time per call {small:.1f} us" in txt
+
+
+def test_source_hash_ignores_comments_and_layout():
+    import bench
+    code = 'int f(int x) {\n  return x + 1;  // one more\n}\nconst char* s = "// kept";\n'
+    a = bench.strip_comments(code)
+    assert a == bench.strip_comments("/* a\n block */ int f(int x) { return x + 1; }\n  const char* s = \"// kept\";")
+    assert '"// kept"' in a and "one more" not in a
+    assert a != bench.strip_comments(code.replace("x + 1", "x + 2"))
+    assert bench.strip_comments("char c = '\\''; // q") == "char c = '\\'';"
