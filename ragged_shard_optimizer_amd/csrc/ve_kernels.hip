@@ -1187,6 +1187,9 @@ __global__ void __launch_bounds__(256) k_step_huge(StepArgs a) {
 // the last one resets both, so the next launch on the stream (or a graph
 // replay) starts from zero.  Launches that overlap in time must not share
 // the counters.
+#ifndef VE_DYN_MPRE
+#define VE_DYN_MPRE 2  // master groups of a staged block loaded by the block before it
+#endif
 #ifndef VE_DYN_SLOTS
 #define VE_DYN_SLOTS 16  // at most this many staged register slots (T x 16 bytes of LDS each)
 #endif
@@ -1212,6 +1215,12 @@ struct DynCfg {
     // faster than 4), at most GPT
     static constexpr int MA0 = GPT >= 12 ? 8 : 6;
     static constexpr int MA = MA0 < GPT ? MA0 : GPT;
+    // of those, the first MPRE of a staged block are loaded by the block
+    // before it, with its staging loads, into the master ring (dead in that
+    // block's phase 2): the block then starts without an HBM round trip.
+    // 28,672-element rows: 2 groups 0.75% faster than none, 1 or 3 less;
+    // 46,080-element rows: no change.
+    static constexpr int MPRE = VE_DYN_MPRE < MA ? VE_DYN_MPRE : MA;
     static_assert(T % 256 == 0, "waves split evenly into gradient, m and v pieces");
 };
 
@@ -1281,22 +1290,22 @@ __device__ __forceinline__ void dyn_stage(const DynItem& nt, uint8_t* sb) {
 template <int T, int GPT, bool STAGED>
 __device__ __forceinline__ uint32_t dyn_block(const DynItem& it, const StepArgs& A, uint32_t nx, uint32_t nitems,
                                               bool& stage_next, uint32_t* s_next, uint8_t* sb,
-                                              float (&red)[2][T / 64]) {
+                                              float (&red)[2][T / 64],
+                                              float (&mst)[DynCfg<T, GPT>::MA + 1][kWgChunk]) {
     constexpr int CH = kWgChunk;
     constexpr int MODE = kWgLinear;
     constexpr int PF = DynCfg<T, GPT>::PF, SPAN = DynCfg<T, GPT>::SPAN, DMA_AT = DynCfg<T, GPT>::DMA_AT;
-    constexpr int MA = DynCfg<T, GPT>::MA;
+    constexpr int MA = DynCfg<T, GPT>::MA, MPRE = DynCfg<T, GPT>::MPRE;
     constexpr bool LATE = WgLateCopy<T, GPT>::value;
     const StepScalars& sc = A.sc;
     const int tid = threadIdx.x;
     In<CH> x[GPT];
-    float mst[MA + 1][CH];
     const uint32_t off[GPT] = {};  // unused by LINEAR addressing
 #pragma unroll
     for (int c = 0; c < GPT; ++c) {
         const ChunkAddr ad = wg_addr<T, GPT, MODE>(it, off, c);
         if (!STAGED || c >= PF) load_in_fast(x[c], it.fb, ad);
-        if (c < MA) load_master_fast(mst[c % (MA + 1)], it.fb, ad);
+        if (c < MA && !(STAGED && c < MPRE)) load_master_fast(mst[c % (MA + 1)], it.fb, ad);
         __builtin_amdgcn_sched_barrier(0);
     }
     uint32_t ticket = 0;
@@ -1355,7 +1364,12 @@ __device__ __forceinline__ uint32_t dyn_block(const DynItem& it, const StepArgs&
     for (int c = 0; c < GPT; ++c) {
         if (c == DMA_AT) {
             __builtin_amdgcn_sched_barrier(0);
-            if (stage_next) dyn_stage<T, GPT>(nt, sb);
+            if (stage_next) {
+                dyn_stage<T, GPT>(nt, sb);
+#pragma unroll
+                for (int c2 = 0; c2 < MPRE; ++c2)
+                    load_master_fast(mst[c2 % (MA + 1)], nt.fb, wg_addr<T, GPT, MODE>(nt, off, c2));
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         make_opaque(x[c]);
@@ -1373,6 +1387,7 @@ __global__ void __launch_bounds__(T) k_step_dyn(StepArgs a, uint32_t nx, uint32_
     __shared__ float s_red[2][T / 64];
     __shared__ uint32_t s_next;
     __shared__ __attribute__((aligned(16))) uint8_t s_buf[DynCfg<T, GPT>::LDS];
+    float mst[DynCfg<T, GPT>::MA + 1][kWgChunk];  // master ring, carried from block to block
     if (threadIdx.x == 0) s_next = atomicAdd(a.sched, 1u);
     __syncthreads();
     uint32_t w = s_next;
@@ -1382,16 +1397,17 @@ __global__ void __launch_bounds__(T) k_step_dyn(StepArgs a, uint32_t nx, uint32_
         uint32_t wn;
         if (it.staged_ok) {
             __builtin_amdgcn_sched_barrier(0);
-            // This wave's staging loads went out before its last AFTER_DMA
-            // stores: wait for them (not for the stores), then for every wave.
+            // This wave's staging loads (and this block's first master
+            // loads) went out before its last AFTER_DMA stores: wait for
+            // them (not for the stores), then for every wave.
             // The barrier also separates the previous block's reads of s_red
             // and s_next from this block's writes.
             if (staged) __builtin_amdgcn_s_waitcnt(0x0F70 | (AFTER_DMA & 15) | (((AFTER_DMA >> 4) & 3) << 14));
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
             bool sn;
-            if (staged) wn = dyn_block<T, GPT, true>(it, a, nx, nitems, sn, &s_next, s_buf, s_red);
-            else wn = dyn_block<T, GPT, false>(it, a, nx, nitems, sn, &s_next, s_buf, s_red);
+            if (staged) wn = dyn_block<T, GPT, true>(it, a, nx, nitems, sn, &s_next, s_buf, s_red, mst);
+            else wn = dyn_block<T, GPT, false>(it, a, nx, nitems, sn, &s_next, s_buf, s_red, mst);
             staged = sn;
         } else {
             __builtin_amdgcn_s_waitcnt(0);
