@@ -1221,6 +1221,9 @@ struct DynCfg {
     // 28,672-element rows: 2 groups 0.75% faster than none, 1 or 3 less;
     // 46,080-element rows: no change.
     static constexpr int MPRE = VE_DYN_MPRE < MA ? VE_DYN_MPRE : MA;
+    // gradient-slice copy stored in phase 2 instead of phase 1 (as
+    // WgLateCopy): 768 x 15 0.8% faster that way, 1024 x 7 0.2% slower
+    static constexpr bool LATE = T == 768;
     static_assert(T % 256 == 0, "waves split evenly into gradient, m and v pieces");
 };
 
@@ -1296,7 +1299,7 @@ __device__ __forceinline__ uint32_t dyn_block(const DynItem& it, const StepArgs&
     constexpr int MODE = kWgLinear;
     constexpr int PF = DynCfg<T, GPT>::PF, SPAN = DynCfg<T, GPT>::SPAN, DMA_AT = DynCfg<T, GPT>::DMA_AT;
     constexpr int MA = DynCfg<T, GPT>::MA, MPRE = DynCfg<T, GPT>::MPRE;
-    constexpr bool LATE = WgLateCopy<T, GPT>::value;
+    constexpr bool LATE = DynCfg<T, GPT>::LATE;
     const StepScalars& sc = A.sc;
     const int tid = threadIdx.x;
     In<CH> x[GPT];
@@ -1381,7 +1384,7 @@ __device__ __forceinline__ uint32_t dyn_block(const DynItem& it, const StepArgs&
 
 template <int T, int GPT>
 __global__ void __launch_bounds__(T) k_step_dyn(StepArgs a, uint32_t nx, uint32_t nitems) {
-    constexpr int GROUP_STORES = WgLateCopy<T, GPT>::value ? 3 : 2;  // phase-2 stores per group
+    constexpr int GROUP_STORES = DynCfg<T, GPT>::LATE ? 3 : 2;  // phase-2 stores per group
     constexpr int AFTER_DMA = GROUP_STORES * (GPT - DynCfg<T, GPT>::DMA_AT);
     static_assert(AFTER_DMA <= 63, "vmcnt holds at most 63");
     __shared__ float s_red[2][T / 64];
