@@ -148,9 +148,13 @@ ve_status ve_dbuffer_copy_in(const ve_plan* plan, int32_t rank, const uint16_t* 
  * Padding of grad_shard and param_shard is written 0; master and the codes
  * at padding are not touched.
  * Blocks of the row-block shapes are handed out to persistent workgroups by
- * two counters that the plan holds per rank (zero between launches): calls
- * for one plan and rank must not overlap in time (issue them on one stream,
- * or order the streams); calls for different ranks or plans may.  With the
+ * two counters that the plan holds per rank (zero between launches), which
+ * admit one launch at a time: a call for a rank on another stream than the
+ * rank's previous such call first waits, on the GPU, for that call (the
+ * library records an event after each call; host threads are serialised
+ * per plan).  Calls for different ranks or plans are not ordered.  Under
+ * stream capture nothing is recorded or waited on: replays of a captured
+ * step must not overlap other calls for the same plan and rank.  With the
  * option "wg_dynamic" at 0 the step uses no counters. */
 ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_shard_state* states,
                                  int32_t n_states, const ve_adam_hparams* hp, int64_t step,
@@ -214,8 +218,8 @@ ve_status ve_dbuffer_group_op(const ve_plan* plan, int32_t rank, int32_t op, flo
  *   "wg_dynamic" (VE_WG_DYNAMIC, 1): 0 = the step's row-block shapes
  *       (512 threads, 14 to 24 groups per thread) launch one workgroup per
  *       block instead of one persistent workgroup per CU taking blocks from
- *       the plan's per-rank counters (same results, slower; no restriction
- *       on overlapping calls, see ve_shard_adam8bit_step).
+ *       the plan's per-rank counters (same results, slower; no ordering of
+ *       calls, see ve_shard_adam8bit_step).
  * ve_set_option changes a value for every later call of the process
  * (calls already queued are unaffected); ve_get_option reads it.  Errors:
  * an unknown name or a NULL value pointer gives VE_ERR_INVALID_ARG. */

@@ -199,9 +199,11 @@ class Plan:
         """``ve_shard_adam8bit_step`` over a :class:`StateTable` built for the
         same plan and ``rank`` (its scale arrays are sized to that rank's
         block count and its gradient tables checked for that rank's pieces).
-        Calls for one plan and rank must not overlap in time (their row
-        blocks are scheduled through that rank's counters); issue them on
-        one stream, or set the option ``wg_dynamic`` to 0."""
+        Row blocks are scheduled through counters the plan holds per rank;
+        a call for a rank on another stream than the rank's previous call
+        waits for it on the GPU.  Under graph capture there is no such
+        ordering: replays of a captured step must not overlap other calls
+        for the same plan and rank."""
         if states.plan is not self or states.rank != rank:
             raise ValueError("state table was built for another plan or rank")
         hp = AdamHParams(float(hparams["lr"]), float(hparams["beta1"]), float(hparams["beta2"]),

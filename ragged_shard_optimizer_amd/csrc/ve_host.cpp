@@ -132,6 +132,16 @@ struct ve_plan {
     size_t dev_bytes = 0;
     size_t off_sched = 0;        // per rank, kSchedStride bytes: the persistent step's two counters (zero at rest)
     int n_cu = 0;                // compute units of `device`
+    // Per rank: the stream of the last step call that used the counters and
+    // an event recorded after its launches, so that a call on another stream
+    // waits for it (the counters admit one launch at a time).
+    struct SchedOrder {
+        hipEvent_t done = nullptr;
+        hipStream_t stream = nullptr;
+        bool used = false;
+    };
+    mutable std::mutex sched_mu;
+    mutable std::vector<SchedOrder> sched_order;
 
     template <class T>
     const T* dptr(size_t off) const { return reinterpret_cast<const T*>(dev + off); }
@@ -469,6 +479,7 @@ ve_status ve_plan_load(const ve_tensor_spec* specs, int32_t n_tensors, int32_t f
             return st;
         }
         P->ranks.resize((size_t)fsdp_size);
+        P->sched_order.resize((size_t)fsdp_size);
         for (int32_t r = 0; r < fsdp_size; ++r) build_rank(*P, r, P->ranks[(size_t)r]);
         build_whole(*P);
         Packer pk;
@@ -521,6 +532,8 @@ ve_status ve_plan_free(ve_plan* plan) {
     ve_status st = VE_OK;
     if (plan->dev && plan->device >= 0) {
         DeviceGuard g(plan->device);
+        for (auto& o : plan->sched_order)
+            if (o.done && hipEventDestroy(o.done) != hipSuccess) st = fail(VE_ERR_DEVICE, "hipEventDestroy failed");
         if (hipFree(plan->dev) != hipSuccess) st = fail(VE_ERR_DEVICE, "hipFree of plan tables failed");
     }
     delete plan;
@@ -669,6 +682,13 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
         // shape (a rank's segments are sorted by block size, so a rank holding
         // the end of one tensor and most of a tensor with smaller blocks gets
         // two launches instead of running every block in the larger shape).
+        struct WgLaunch {
+            size_t i0, i1;
+            int threads, gpt;
+            bool dyn;
+        };
+        std::vector<WgLaunch> runs;
+        bool any_dyn = false;
         const size_t n = rt.wg.seg_idx.size();
         auto shape_of = [&](size_t i, int& t, int& g) { wg_shape(rt.segs[(size_t)rt.wg.seg_idx[i]].max_groups, t, g); };
         for (size_t i0 = 0; i0 < n;) {
@@ -679,17 +699,45 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
                 shape_of(i1, t1, g1);
                 if (t1 != threads || g1 != gpt) break;
             }
-            const int64_t nb = set_inline(a, rt, rt.wg, i0, i1);
-            i0 = i1;
-            if (nb == 0) continue;
+            const int64_t nb = rt.wg.prefix[i1] - rt.wg.prefix[i0];
             // Row-block shapes run persistent, the resident workgroups taking
-            // blocks from the rank's counters (launches on one stream run one
-            // after another, so they share them); tickets stay below 2^31.
-            const bool dyn = option(kOptWgDynamic) != 0 && wg_dynamic_shape(threads, gpt) &&
+            // blocks from the rank's counters; tickets stay below 2^31.
+            const bool dyn = nb > 0 && option(kOptWgDynamic) != 0 && wg_dynamic_shape(threads, gpt) &&
                              nb * n_states + (int64_t)kDynMaxPerCu * plan->n_cu < (int64_t(1) << 31);
-            if ((st = launch_status(launch_step_wg(a, n_states, threads, gpt, dyn ? plan->n_cu : 0, s),
+            runs.push_back({i0, i1, threads, gpt, dyn});
+            any_dyn = any_dyn || dyn;
+            i0 = i1;
+        }
+        // The counters admit one launch at a time.  Launches on one stream
+        // run one after another; a call on another stream than the rank's
+        // last one that used them first waits (on the GPU) for that call's
+        // launches.  Under stream capture no event is recorded or waited on:
+        // a captured step must not overlap other calls for this plan and rank.
+        std::unique_lock<std::mutex> order_lock;
+        bool capturing = false;
+        if (any_dyn) {
+            order_lock = std::unique_lock<std::mutex>(plan->sched_mu);
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            if (hipStreamIsCapturing(s, &cs) != hipSuccess)
+                return fail(VE_ERR_DEVICE, "hipStreamIsCapturing failed");
+            capturing = cs != hipStreamCaptureStatusNone;
+            const auto& o = plan->sched_order[(size_t)rank];
+            if (!capturing && o.used && o.stream != s && hipStreamWaitEvent(s, o.done, 0) != hipSuccess)
+                return fail(VE_ERR_DEVICE, "hipStreamWaitEvent on the rank's previous step failed");
+        }
+        for (const WgLaunch& w : runs) {
+            if (set_inline(a, rt, rt.wg, w.i0, w.i1) == 0) continue;
+            if ((st = launch_status(launch_step_wg(a, n_states, w.threads, w.gpt, w.dyn ? plan->n_cu : 0, s),
                                     "workgroup step")) != VE_OK)
                 return st;
+        }
+        if (any_dyn && !capturing) {
+            auto& o = plan->sched_order[(size_t)rank];
+            if (!o.done && hipEventCreateWithFlags(&o.done, hipEventDisableTiming) != hipSuccess)
+                return fail(VE_ERR_DEVICE, "hipEventCreateWithFlags failed");
+            if (hipEventRecord(o.done, s) != hipSuccess) return fail(VE_ERR_DEVICE, "hipEventRecord failed");
+            o.stream = s;
+            o.used = true;
         }
     }
     if (rt.small.prefix.back() > 0) {

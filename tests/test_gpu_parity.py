@@ -268,6 +268,74 @@ def test_persistent_step_replays_in_a_captured_graph():
     plan.close()
 
 
+def test_persistent_steps_of_two_ranks_overlap_on_two_streams():
+    """Each rank has its own scheduler counters, so step calls for different
+    ranks of one plan may run at the same time: ranks 0 and 1 on two
+    streams with no ordering between them, three steps, each equal to the
+    same steps run one after another on twin buckets."""
+    import torch
+    ve = _ve()
+    lay = plan_p0(DYN_TENSORS, 2)
+    cfg = Config("dyn", list(DYN_TENSORS), fsdp=2, grad_scale=1e-3, steps=3)
+    plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
+    hp = hp32()
+    run = {r: RankProblem(ve, cfg, lay, plan, r) for r in (0, 1)}
+    twin = {r: RankProblem(ve, cfg, lay, plan, r) for r in (0, 1)}
+    for p in list(run.values()) + list(twin.values()):
+        p.set_grads(1)
+    streams = {0: torch.cuda.Stream(), 1: torch.cuda.Stream()}
+    torch.cuda.synchronize()
+    _say("[gpu] dyn 512 x 16, ranks 0 and 1 on two streams")
+    with ve.options(wg_threads=512, wg_gpt=16, wg_dynamic=1):
+        for t in (1, 2, 3):
+            for r in (0, 1):
+                plan.step(r, run[r].table, hp, t, streams[r])
+        for t in (1, 2, 3):
+            for r in (0, 1):
+                plan.step(r, twin[r].table, hp, t)
+    torch.cuda.synchronize()
+    for r in (0, 1):
+        a, b = run[r].download(), twin[r].download()
+        for k in a:
+            assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), (r, k)
+        assert run[r].guards_intact() and twin[r].guards_intact()
+    plan.close()
+
+
+def test_persistent_steps_of_one_rank_on_two_streams_are_ordered():
+    """Two buckets of one rank stepped alternately on two streams with no
+    ordering by the caller: the library makes each call on a new stream wait
+    for the rank's previous one (the counters admit one launch at a time),
+    so every bucket equals the same steps run one after another."""
+    import torch
+    ve = _ve()
+    lay = plan_p0(DYN_TENSORS, 2)
+    cfg = Config("dyn", list(DYN_TENSORS), fsdp=2, grad_scale=1e-3, steps=3)
+    plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
+    hp = hp32()
+    r = 1
+    run = [RankProblem(ve, cfg, lay, plan, r, bucket=b) for b in (0, 1)]
+    twin = [RankProblem(ve, cfg, lay, plan, r, bucket=b) for b in (0, 1)]
+    for p in run + twin:
+        p.set_grads(1)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    _say("[gpu] dyn 512 x 16, one rank, two buckets on two streams")
+    with ve.options(wg_threads=512, wg_gpt=16, wg_dynamic=1):
+        for t in (1, 2, 3):
+            for b in (0, 1):
+                plan.step(r, run[b].table, hp, t, streams[b])
+        for t in (1, 2, 3):
+            for b in (0, 1):
+                plan.step(r, twin[b].table, hp, t)
+    torch.cuda.synchronize()
+    for b in (0, 1):
+        x, y = run[b].download(), twin[b].download()
+        for k in x:
+            assert np.array_equal(x[k].view(np.uint8), y[k].view(np.uint8)), (b, k)
+    plan.close()
+
+
 # A rank holding the end of one tensor and rows of another with smaller
 # blocks takes one launch per block shape (llama_mini rank 4: 3,584- and
 # 1,024-element rows; llama_rowblk rank 20: 28,672-element rows of `down`,
