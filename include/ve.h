@@ -147,7 +147,8 @@ ve_status ve_dbuffer_copy_in(const ve_plan* plan, int32_t rank, const uint16_t* 
  * clamp(rint(x*127/amax), -127, 127); amax 0 gives scale 0 and code 0).
  * Padding of grad_shard and param_shard is written 0; master and the codes
  * at padding are not touched.
- * Blocks of the row-block shapes are handed out to persistent workgroups by
+ * Blocks of the row-block shapes and row items (see the options "wg_dynamic"
+ * and "wg_rows") are handed out to persistent workgroups by
  * two counters that the plan holds per rank (zero between launches), which
  * admit one launch at a time: a call for a rank on another stream than the
  * rank's previous such call first waits, on the GPU, for that call (the
@@ -216,10 +217,16 @@ ve_status ve_dbuffer_group_op(const ve_plan* plan, int32_t rank, int32_t op, flo
  *   "gemm_xcd" (VE_GEMM_XCD, 1): 0 = plain tile order instead of the
  *       XCD-aware one;
  *   "wg_dynamic" (VE_WG_DYNAMIC, 1): 0 = the step's row-block shapes
- *       (512 threads, 14 to 24 groups per thread) launch one workgroup per
- *       block instead of one persistent workgroup per CU taking blocks from
- *       the plan's per-rank counters (same results, slower; no ordering of
- *       calls, see ve_shard_adam8bit_step).
+ *       (blocks of 4,097 to 12,288 groups: 512 threads with 14 to 24 groups
+ *       per thread, 768 threads, 1024 threads with 7 to 10) and the row
+ *       items below launch one workgroup per block instead of persistent
+ *       workgroups (one or a few per CU) taking work from the plan's
+ *       per-rank counters (same results, slower; no ordering of calls, see
+ *       ve_shard_adam8bit_step);
+ *   "wg_rows" (VE_WG_ROWS, 1): 0 = whole-row blocks of 2,048 or 4,096
+ *       groups (rows of 8K or 16K elements) run one workgroup per block
+ *       instead of persistent items of 4 or 2 consecutive blocks (same
+ *       results, slower; needs "wg_dynamic" and no pinned shape).
  * ve_set_option changes a value for every later call of the process
  * (calls already queued are unaffected); ve_get_option reads it.  Errors:
  * an unknown name or a NULL value pointer gives VE_ERR_INVALID_ARG. */

@@ -153,6 +153,12 @@ hipError_t launch_step_wg(const StepArgs& a, int n_states, int threads, int grou
                           hipStream_t s);
 constexpr int kDynMaxPerCu = 8;
 bool wg_dynamic_shape(int threads, int groups_per_thread);
+// Persistent form over items of `rows_per_item` (2 or 4) consecutive
+// whole-row blocks of 4,096 or 2,048 groups (8,192 groups an item), in
+// kRowsThreads x kRowsGpt workgroups; a.inl_prefix counts items, a.sched as
+// above, dyn_cu > 0.
+constexpr int kRowsThreads = 1024, kRowsGpt = 8, kRowsGroups = kRowsThreads * kRowsGpt;
+hipError_t launch_step_rows(const StepArgs& a, int n_states, int rows_per_item, int dyn_cu, hipStream_t s);
 hipError_t launch_step_huge(const StepArgs& a, int n_states, hipStream_t s);
 // Copy-in: out = bucket; grad pointers from `grad_ptrs`.
 hipError_t launch_runs_copy(const RunArgs& r, const uint16_t* const* grad_ptrs, uint16_t* out,
@@ -170,6 +176,7 @@ enum Option : int {
     kOptGemmCfg,        // "gemm_cfg" (VE_GEMM_CFG): product configuration, -1 = by shape
     kOptGemmXcd,        // "gemm_xcd" (VE_GEMM_XCD): 0 = plain tile order instead of the XCD-aware one
     kOptWgDynamic,      // "wg_dynamic" (VE_WG_DYNAMIC): 0 = one-shot launches for the row-block shapes too
+    kOptWgRows,         // "wg_rows" (VE_WG_ROWS): 0 = no multi-block items for blocks of 2,048 / 4,096 groups
     kNumOptions
 };
 int64_t option(Option o);

@@ -850,13 +850,14 @@ struct WgItem {
     uint32_t step;   // LINEAR: element offset between slots (wave-uniform)
 };
 
-// Item (state y, block xw of the launch's segment slice).
+// Item (state y, block `local` of segment sg); xw (the launch's work item)
+// sets the sweep rotation.
 template <int GPT>
-__device__ __forceinline__ WgItem wg_item_at(const StepArgs& a, int64_t y, int64_t xw) {
+__device__ __forceinline__ WgItem wg_item_for(const StepArgs& a, int64_t y, const Seg& sg, int64_t local,
+                                              int64_t xw) {
     constexpr int CH = kWgChunk;
     WgItem it;
-    int64_t local;
-    it.sg = find_inline(a, xw, local);
+    it.sg = sg;
     ve_shard_state st;
     {
         static_assert(sizeof(ve_shard_state) == 8 * sizeof(uint64_t), "eight pointers");
@@ -905,6 +906,14 @@ __device__ __forceinline__ WgItem wg_item_at(const StepArgs& a, int64_t y, int64
         it.fb.param = buf_rsrc(it.p.param + s0, 2 * span);
     }
     return it;
+}
+
+// Item (state y, block xw of the launch's segment slice).
+template <int GPT>
+__device__ __forceinline__ WgItem wg_item_at(const StepArgs& a, int64_t y, int64_t xw) {
+    int64_t local;
+    const Seg sg = find_inline(a, xw, local);
+    return wg_item_for<GPT>(a, y, sg, local, xw);
 }
 
 template <int T, int GPT>
@@ -1267,8 +1276,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 // per wave: the first half of the waves move its gradient, the next quarter
 // its m codes, the last quarter its v codes, 16 bytes per lane; reads past
 // the block's span return zeros, which no lane uses.
-template <int T, int GPT>
-__device__ __forceinline__ void dyn_stage(const DynItem& nt, uint8_t* sb) {
+template <int T, int GPT, class Item>
+__device__ __forceinline__ void dyn_stage(const Item& nt, uint8_t* sb) {
     constexpr int W = T / 64;
     constexpr int PF = DynCfg<T, GPT>::PF, SPAN = DynCfg<T, GPT>::SPAN;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -1438,6 +1447,244 @@ __global__ void __launch_bounds__(T) k_step_dyn(StepArgs a, uint32_t nx, uint32_
     __builtin_amdgcn_s_waitcnt(0);
 }
 
+// ---------------------------------------------------------------------------
+// Persistent form for short row blocks (2,048 or 4,096 groups: rows of 8K or
+// 16K elements): a work item is RPI consecutive blocks of one row-block
+// segment, one contiguous span of 8,192 groups that is staged and streamed
+// like a long row (1024 x 8), with one absmax, one scale pair and one
+// requantisation per block.  Slot c of a thread belongs to block c / SPR
+// (no sweep rotation), so every per-block index below is a compile-time
+// constant.  Items whose blocks are not all full rows of naturally aligned
+// data run block by block through the general workgroup code.
+// Measured on MI355X (a rank of 8,192-element rows, 80 buckets, against the
+// one-shot 256 x 8 kernel): see the shape rule in the host code.
+template <int RPI>
+struct RowsItem {
+    FastRsrc fb;
+    Geo geo;  // nchunks: the item's chunks; blk: its first block's scale slot
+    float sm[RPI], sv[RPI];
+    float* m_scale;
+    float* v_scale;
+    int rot;  // always 0
+    uint32_t lane0, step;
+    int nrows;       // blocks in this item (RPI but at a segment's end)
+    bool fast;       // all full rows, aligned: the item runs as one span
+    bool staged_ok;  // and its span is a multiple of 16 elements
+};
+
+template <int T, int GPT, int RPI>
+__device__ __forceinline__ RowsItem<RPI> rows_item(const StepArgs& a, uint32_t w, uint32_t nx, Seg& sg,
+                                                   int64_t& lb, uint32_t& y) {
+    constexpr int CH = kWgChunk;
+    RowsItem<RPI> d;
+    y = __builtin_amdgcn_readfirstlane(w / nx);
+    int64_t local;
+    sg = find_inline(a, w - y * nx, local);
+    lb = local * RPI;
+    const int64_t rem = sg.nblocks - lb;
+    d.nrows = (int)(rem < RPI ? rem : RPI);
+    ve_shard_state st;
+    {
+        const uint64_t* src = reinterpret_cast<const uint64_t*>(a.states + y);
+        uint64_t* dst = reinterpret_cast<uint64_t*>(&st);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dst[i] = sload(src + i);
+    }
+    const Ptrs p = make_ptrs<true>(st, sg.tensor);
+    const Geo g0 = block_geo<CH>(sg, lb);
+    d.geo = g0;
+    d.m_scale = st.m_scale;
+    d.v_scale = st.v_scale;
+#pragma unroll
+    for (int r = 0; r < RPI; ++r) {
+        d.sm[r] = r < d.nrows ? sload(st.m_scale + g0.blk + r) : 0.f;
+        d.sv[r] = r < d.nrows ? sload(st.v_scale + g0.blk + r) : 0.f;
+    }
+    // full rows only: every block of the item holds block_rows whole rows
+    const bool full = sg.tiles == 1 && (sg.panel0 + lb + d.nrows) * sg.block_rows <= sg.rows &&
+                      g0.run == T * CH * (GPT / RPI);
+    const int64_t span = (int64_t)d.nrows * g0.run;
+    d.fast = full && p.aligned && ((g0.e0 | sg.shard_base | g0.run) & (CH - 1)) == 0 && span < kFastMaxSpan;
+    d.staged_ok = d.fast && (g0.run & 15) == 0;
+    d.geo.nchunks = (int32_t)(span / CH);
+    d.rot = 0;
+    d.lane0 = threadIdx.x * CH;
+    d.step = T * CH;
+    if (d.fast) {
+        const int64_t s0 = sg.shard_base + g0.e0;
+        d.fb.grad = buf_rsrc(p.grad + g0.e0, 2 * span);
+        d.fb.grad_shard = buf_rsrc(p.grad_shard + s0, 2 * span);
+        d.fb.master = buf_rsrc(p.master + s0, 4 * span);
+        d.fb.m_q = buf_rsrc(p.m_q + s0, span);
+        d.fb.v_q = buf_rsrc(p.v_q + s0, span);
+        d.fb.param = buf_rsrc(p.param + s0, 2 * span);
+    }
+    return d;
+}
+
+// One item of RPI blocks as one span (see dyn_block): per-block absmax
+// accumulators, reduction, scales and requantisation.
+template <int T, int GPT, bool STAGED, int RPI>
+__device__ __forceinline__ bool rows_block(const RowsItem<RPI>& it, const StepArgs& A, uint32_t nx, uint32_t nitems,
+                                           RowsItem<RPI>& nt, uint32_t& wn, uint32_t* s_next, uint8_t* sb,
+                                           float (&red)[2][RPI][T / 64],
+                                           float (&mst)[DynCfg<T, GPT>::MA + 1][kWgChunk]) {
+    constexpr int CH = kWgChunk;
+    constexpr int MODE = kWgLinear;
+    constexpr int SPR = GPT / RPI;  // register slots per block
+    static_assert(SPR * RPI == GPT, "whole blocks per thread");
+    constexpr int PF = DynCfg<T, GPT>::PF, SPAN = DynCfg<T, GPT>::SPAN, DMA_AT = DynCfg<T, GPT>::DMA_AT;
+    constexpr int MA = DynCfg<T, GPT>::MA, MPRE = DynCfg<T, GPT>::MPRE;
+    constexpr bool LATE = DynCfg<T, GPT>::LATE;
+    const StepScalars& sc = A.sc;
+    const int tid = threadIdx.x;
+    In<CH> x[GPT];
+    const uint32_t off[GPT] = {};  // unused by LINEAR addressing
+#pragma unroll
+    for (int c = 0; c < GPT; ++c) {
+        const ChunkAddr ad = wg_addr<T, GPT, MODE>(it, off, c);
+        if (!STAGED || c >= PF) load_in_fast(x[c], it.fb, ad);
+        if (c < MA && !(STAGED && c < MPRE)) load_master_fast(mst[c % (MA + 1)], it.fb, ad);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    uint32_t ticket = 0;
+    if (tid == 0) ticket = atomicAdd(A.sched, 1u);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (STAGED) {
+#pragma unroll
+        for (int c = 0; c < PF; ++c) {
+            const bool ok = tid < it.geo.nchunks - c * T;
+            const uint2 g = *(const uint2*)(sb + c * T * 8 + tid * 8);
+            const uint32_t m = *(const uint32_t*)(sb + 2 * SPAN + c * T * 4 + tid * 4);
+            const uint32_t v = *(const uint32_t*)(sb + 3 * SPAN + c * T * 4 + tid * 4);
+            x[c].g[0] = ok ? g.x : 0u;
+            x[c].g[1] = ok ? g.y : 0u;
+            x[c].m[0] = ok ? m : 0u;
+            x[c].v[0] = ok ? v : 0u;
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float am[RPI], av[RPI];
+#pragma unroll
+    for (int r = 0; r < RPI; ++r) am[r] = av[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < GPT; ++c) {
+        if (c + MA < GPT) load_master_fast(mst[(c + MA) % (MA + 1)], it.fb, wg_addr<T, GPT, MODE>(it, off, c + MA));
+        phase1_fast<LATE>(x[c], mst[c % (MA + 1)], it.fb, wg_addr<T, GPT, MODE>(it, off, c), it.sm[c / SPR],
+                          it.sv[c / SPR], sc, am[c / SPR], av[c / SPR]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int r = 0; r < RPI; ++r) {
+        am[r] = wave_max(am[r]);
+        av[r] = wave_max(av[r]);
+        if ((tid & 63) == 0) {
+            red[0][r][tid >> 6] = am[r];
+            red[1][r][tid >> 6] = av[r];
+        }
+    }
+    if (tid == 0) *s_next = ticket;
+    lds_barrier();
+    wn = *s_next;
+    const bool more = wn < nitems;
+    Seg nsg;
+    int64_t nlb;
+    uint32_t ny;
+    nt = rows_item<T, GPT, RPI>(A, more ? wn : 0u, nx, nsg, nlb, ny);
+    const bool stage_next = more && nt.staged_ok;
+    float im[RPI], iv[RPI];
+#pragma unroll
+    for (int r = 0; r < RPI; ++r) {
+        float bm = 0.f, bv = 0.f;
+#pragma unroll
+        for (int i = 0; i < T / 64; ++i) {
+            bm = fmaxf(bm, red[0][r][i]);
+            bv = fmaxf(bv, red[1][r][i]);
+        }
+        im[r] = bm > 0.f ? 127.0f / bm : 0.f;
+        iv[r] = bv > 0.f ? 127.0f / bv : 0.f;
+        if (tid == r && r < it.nrows) {
+            ((VE_GLOBAL float*)it.m_scale)[it.geo.blk + r] = bm / 127.0f;
+            ((VE_GLOBAL float*)it.v_scale)[it.geo.blk + r] = bv / 127.0f;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < GPT; ++c) {
+        if (c == DMA_AT) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (stage_next) {
+                dyn_stage<T, GPT>(nt, sb);
+#pragma unroll
+                for (int c2 = 0; c2 < MPRE; ++c2)
+                    load_master_fast(mst[c2 % (MA + 1)], nt.fb, wg_addr<T, GPT, MODE>(nt, off, c2));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        make_opaque(x[c]);
+        phase2_fast<LATE>(x[c], it.fb, wg_addr<T, GPT, MODE>(it, off, c), it.sm[c / SPR], it.sv[c / SPR],
+                          im[c / SPR], iv[c / SPR], sc);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return stage_next;
+}
+
+template <int T, int GPT, int RPI>
+__global__ void __launch_bounds__(T) k_step_rows(StepArgs a, uint32_t nx, uint32_t nitems) {
+    constexpr int GROUP_STORES = DynCfg<T, GPT>::LATE ? 3 : 2;  // phase-2 stores per group
+    constexpr int AFTER_DMA = GROUP_STORES * (GPT - DynCfg<T, GPT>::DMA_AT);
+    static_assert(AFTER_DMA <= 63, "vmcnt holds at most 63");
+    __shared__ float s_red[2][RPI][T / 64];
+    __shared__ float s_red1[2][T / 64];  // the block-by-block fallback's
+    __shared__ uint32_t s_next;
+    __shared__ __attribute__((aligned(16))) uint8_t s_buf[DynCfg<T, GPT>::LDS];
+    float mst[DynCfg<T, GPT>::MA + 1][kWgChunk];  // master ring, carried from item to item
+    if (threadIdx.x == 0) s_next = atomicAdd(a.sched, 1u);
+    __syncthreads();
+    uint32_t w = s_next;
+    bool staged = false;
+    while (w < nitems) {
+        Seg sg;
+        int64_t lb;
+        uint32_t y;
+        const RowsItem<RPI> it = rows_item<T, GPT, RPI>(a, w, nx, sg, lb, y);
+        uint32_t wn;
+        if (it.fast) {
+            __builtin_amdgcn_sched_barrier(0);
+            // as in k_step_dyn: wait for this wave's staging loads, then for every wave
+            if (staged) __builtin_amdgcn_s_waitcnt(0x0F70 | (AFTER_DMA & 15) | (((AFTER_DMA >> 4) & 3) << 14));
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            RowsItem<RPI> nt;
+            if (staged) staged = rows_block<T, GPT, true, RPI>(it, a, nx, nitems, nt, wn, &s_next, s_buf, s_red, mst);
+            else staged = rows_block<T, GPT, false, RPI>(it, a, nx, nitems, nt, wn, &s_next, s_buf, s_red, mst);
+        } else {
+            // block by block through the general workgroup code
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_s_barrier();
+            if (threadIdx.x == 0) s_next = atomicAdd(a.sched, 1u);  // read after the blocks' barriers
+            for (int r = 0; r < it.nrows; ++r) {
+                const WgItem gi = wg_item_for<GPT>(a, y, sg, lb + r, lb + r);
+                if (r > 0) __syncthreads();  // the previous block's reads of s_red1
+                if (gi.mode == kWgLinear) wg_one<T, GPT, kWgLinear>(gi, s_red1, a.sc);
+                else if (gi.mode == kWgTiled) wg_one<T, GPT, kWgTiled>(gi, s_red1, a.sc);
+                else wg_one<T, GPT, kWgGeneral>(gi, s_red1, a.sc);
+            }
+            wn = s_next;
+            staged = false;
+        }
+        w = wn;
+    }
+    // as in k_step_dyn: the last workgroup out resets the counters
+    if (threadIdx.x == 0) {
+        const uint32_t left = atomicAdd(a.sched + 1, 1u);
+        if (left == gridDim.x - 1) {
+            atomicExch(a.sched, 0u);
+            atomicExch(a.sched + 1, 0u);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1474,6 +1721,30 @@ static hipError_t launch_wg_t(const StepArgs& a, int n_states, int dyn_cu, hipSt
     }
     hipLaunchKernelGGL((k_step_wg<T, GPT>), dim3(grid_x(a.work.total), n_states), dim3(T), 0, s, a);
     return hipGetLastError();
+}
+
+template <int RPI>
+static hipError_t launch_rows_t(const StepArgs& a, int n_states, int dyn_cu, hipStream_t s) {
+    static const int occ = [] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_step_rows<kRowsThreads, kRowsGpt, RPI>, kRowsThreads,
+                                                         0) != hipSuccess ||
+            n < 1)
+            n = 1;
+        return n < kDynMaxPerCu ? n : kDynMaxPerCu;
+    }();
+    const int64_t items = a.work.total * n_states;
+    const int64_t grid = std::min<int64_t>(items, (int64_t)dyn_cu * occ);
+    hipLaunchKernelGGL((k_step_rows<kRowsThreads, kRowsGpt, RPI>), dim3((unsigned)grid), dim3(kRowsThreads), 0, s, a,
+                       (uint32_t)a.work.total, (uint32_t)items);
+    return hipGetLastError();
+}
+
+hipError_t launch_step_rows(const StepArgs& a, int n_states, int rpi, int dyn_cu, hipStream_t s) {
+    if (dyn_cu < 1) return hipErrorInvalidValue;
+    if (rpi == 2) return launch_rows_t<2>(a, n_states, dyn_cu, s);
+    if (rpi == 4) return launch_rows_t<4>(a, n_states, dyn_cu, s);
+    return hipErrorInvalidValue;
 }
 
 bool wg_config_supported(int threads, int gpt) {

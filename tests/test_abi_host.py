@@ -197,11 +197,12 @@ def test_stream_copy_rejects_bad_arguments_without_a_device():
 
 def test_options_round_trip_and_restore():
     before = {k: ve.get_option(k) for k in ("wg_threads", "wg_gpt", "gemm_split", "gemm_cfg", "gemm_xcd",
-                                            "wg_dynamic")}
+                                            "wg_dynamic", "wg_rows")}
     assert before["gemm_split"] in (0, 1) and before["gemm_xcd"] in (0, 1) and before["wg_dynamic"] in (0, 1)
-    with ve.options(wg_threads=512, gemm_split=0, wg_dynamic=0):
+    assert before["wg_rows"] in (0, 1)
+    with ve.options(wg_threads=512, gemm_split=0, wg_dynamic=0, wg_rows=0):
         assert ve.get_option("wg_threads") == 512 and ve.get_option("gemm_split") == 0
-        assert ve.get_option("wg_dynamic") == 0
+        assert ve.get_option("wg_dynamic") == 0 and ve.get_option("wg_rows") == 0
     assert {k: ve.get_option(k) for k in before} == before
     L = ve.lib()
     assert L.ve_set_option(b"no_such_option", 1) == ve.VE_ERR_INVALID_ARG

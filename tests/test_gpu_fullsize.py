@@ -153,6 +153,39 @@ def test_full_size_persistent_equals_one_shot(name):
     torch.cuda.empty_cache()
 
 
+def test_full_size_row_items_equal_one_shot():
+    """A LLaMA rank that holds only 8,192-element rows (93 of the 128 ranks
+    hold such rows; rank 36 nothing else): every bucket stepped in items of
+    four rows against one workgroup a row (wg_rows = 0), two steps,
+    bit-identical."""
+    import torch
+    import ragged_shard_optimizer_amd as ve
+    cfg, lay = layout_of("llama")
+    rank = 36
+    rows = {lay.tensors[k].block_rows * lay.tensors[k].cols for k, *_ in lay.chunk_intervals(rank)}
+    assert rows == {8192}, rows
+    plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
+    hp = hp32()
+    buckets = device_buckets(cfg, lay, rank, DEV)
+    _say(f"[gpu] full-size llama: rank {rank}, {len(buckets)} buckets, row items vs one-shot")
+    itm = [ve.new_state(plan, rank, ve.grad_pointer_table(g, DEV), m) for g, m in buckets]
+    one = [ve.new_state(plan, rank, ve.grad_pointer_table(g, DEV), m.clone()) for g, m in buckets]
+    t_itm, t_one = ve.state_table(plan, rank, itm), ve.state_table(plan, rank, one)
+    keys = ("grad_shard", "master", "m_q", "v_q", "m_scale", "v_scale", "param_shard")
+    for t in (1, 2):
+        with ve.options(wg_dynamic=1, wg_rows=1):
+            plan.step(rank, t_itm, hp, t)
+        with ve.options(wg_dynamic=1, wg_rows=0):
+            plan.step(rank, t_one, hp, t)
+        torch.cuda.synchronize()
+        for b, (x, y) in enumerate(zip(itm, one)):
+            for k in keys:
+                assert torch.equal(x[k], y[k]), (t, b, k)
+    del itm, one, t_itm, t_one, buckets
+    plan.close()
+    torch.cuda.empty_cache()
+
+
 def test_adversarial_whole_bucket_copy_in():
     """Copy-in of the whole adversarial bucket (10,000 tensors, ~2.9 GB
     moved): every tensor lands at its offset bit for bit, all padding zero."""

@@ -227,6 +227,113 @@ def test_persistent_equals_one_shot():
     plan.close()
 
 
+# Whole-row blocks of 2,048 and 4,096 groups (rows of 8K and 16K elements)
+# run persistent in items of 4 or 2 consecutive blocks streamed as one span,
+# each block keeping its own absmax and scales.  Pieces whose block count is
+# not a multiple of the item size (a short last item), a one-row last panel
+# inside an item (that item goes block by block through the general code),
+# and 8,190-element rows (2,048 groups, not whole groups: every item of that
+# tensor goes block by block).
+ROW_TENSORS = [
+    TensorDef("r16k", 61, 16384, 1, 16384),   # 4,096 groups: 2 blocks an item
+    TensorDef("r8k", 203, 8192, 1, 8192),     # 2,048 groups: 4 blocks an item
+    TensorDef("r2x4k", 301, 4096, 2, 4096),   # 2-row blocks, 1-row last panel
+    TensorDef("r8190", 30, 8190, 1, 8190),    # 2,048 groups with a partial last one
+]
+
+
+def _row_layout(steps):
+    lay = plan_p0(ROW_TENSORS, 2)
+    return Config("rows", list(ROW_TENSORS), fsdp=2, grad_scale=1e-3, steps=steps), lay
+
+
+def test_row_items_parity():
+    ve = _ve()
+    cfg, lay = _row_layout(3)
+    for r in (0, 1):  # each rank holds ragged pieces of the row tensors
+        nbl = {lay.tensors[k].name: (hi - lo) // lay.tensors[k].unit for k, lo, hi, *_ in lay.chunk_intervals(r)}
+        assert any(n % 4 for n in nbl.values()), nbl
+    tally = Tally(cfg.name)
+    with ve.options(wg_dynamic=1, wg_rows=1):
+        _run_parity(cfg, lay, [0, 1], 3, tally)
+    tally.check()
+
+
+def _twin_sets(ve, cfg, lay, plan, r, n_buckets):
+    sets = []
+    for _ in range(2):
+        probs = [RankProblem(ve, cfg, lay, plan, r, bucket=b) for b in range(n_buckets)]
+        states = []
+        for p in probs:
+            p.set_grads(1)
+            st = {k: b.view for k, b in p.buf.items()}
+            st["grad_table"] = p.gt
+            states.append(st)
+        sets.append((probs, ve.state_table(plan, r, states)))
+    return sets
+
+
+def _assert_twins_equal(sets):
+    for p, q in zip(sets[0][0], sets[1][0]):
+        a, b = p.download(), q.download()
+        for k in a:
+            assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+        assert p.guards_intact() and q.guards_intact()
+
+
+def test_row_items_equal_one_shot():
+    """Three buckets in one call, the multi-block items against one-shot
+    launches (wg_rows = 0: one workgroup a block) on copies of the same
+    states: bit-identical over two steps, on both ranks."""
+    import torch
+    ve = _ve()
+    cfg, lay = _row_layout(2)
+    plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
+    hp = hp32()
+    for r in (0, 1):
+        sets = _twin_sets(ve, cfg, lay, plan, r, 3)
+        _say(f"[gpu] rows x3 rank {r}: row items vs one-shot")
+        for t in (1, 2):
+            with ve.options(wg_dynamic=1, wg_rows=1):
+                plan.step(r, sets[0][1], hp, t)
+            with ve.options(wg_dynamic=1, wg_rows=0):
+                plan.step(r, sets[1][1], hp, t)
+        torch.cuda.synchronize()
+        _assert_twins_equal(sets)
+    plan.close()
+
+
+def test_row_items_misaligned_state_buffers():
+    """State arrays shifted by one element: every row item goes block by
+    block through the general code, bit-identical to aligned arrays."""
+    import torch
+    ve = _ve()
+    cfg, lay = _row_layout(1)
+    plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
+    hp = hp32()
+    r = 0
+    prob = RankProblem(ve, cfg, lay, plan, r)
+    prob.set_grads(1)
+    shifted = {}
+    for k, b in prob.buf.items():
+        big = torch.zeros(b.view.numel() + 1, dtype=b.view.dtype, device=DEV)
+        big[1:].copy_(b.view)
+        shifted[k] = big[1:]
+    st = dict(shifted)
+    st["grad_table"] = prob.gt
+    table = ve.state_table(plan, r, [st])
+    _say("[gpu] rows rank 0, misaligned state arrays")
+    with ve.options(wg_dynamic=1, wg_rows=1):
+        plan.step(r, prob.table, hp, 1)
+        plan.step(r, table, hp, 1)
+    torch.cuda.synchronize()
+    for k in prob.buf:
+        a = prob.buf[k].view.cpu().numpy()
+        b = shifted[k].cpu().numpy()
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), k
+    plan.close()
+
+
 def test_persistent_step_replays_in_a_captured_graph():
     """Each persistent launch's last workgroup resets the rank's counters, so
     a captured step replays: three replays, with eager steps of another
