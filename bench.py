@@ -449,13 +449,13 @@ def _csv_rows(path):
         return list(csv.DictReader(fh))
 
 
-def _workload_alg(workload, buckets=None):
+def _workload_alg(workload, buckets=None, rank=None):
     """(algorithmic bytes of one all-bucket step launch, buckets, valid, blocks, shard)."""
     from synth import CONFIGS, plan_p0
     import ragged_shard_optimizer_amd as ve
     cfg = CONFIGS[workload]
     lay = plan_p0(cfg.tensors, cfg.fsdp)
-    rank = lay.largest_rank()
+    rank = lay.largest_rank() if rank is None else rank
     nv, nb, _ = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=-1).query(rank)
     nbk = buckets or cfg.n_buckets
     alg = nbk * (BYTES_PER_ELEM * nv + BYTES_PER_BLOCK * nb + BYTES_PER_PAD * (lay.shard - nv))
@@ -498,6 +498,8 @@ def summarize_counters(args):
     """HBM bytes per launch of the step kernel from two rocprofv3 --pmc runs
     (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each counter scaled by
     what it reads for the streaming copy of known size in the same run."""
+    if args.rank is not None:
+        raise SystemExit("counters are summarised for the default rank only (bench.py reads them back there)")
     import statistics
     f_rows = [r for r in _csv_rows(os.path.join(args.fetch_dir, "run_counter_collection.csv"))
               if r["Counter_Name"] == "FETCH_SIZE"]
@@ -593,8 +595,9 @@ def summarize_trace(args):
     skipped, st = len(st[:args.skip_first]), st[args.skip_first:]
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in st]
     avg = statistics.mean(durs)
-    alg, nbk, nv, nb, S = _workload_alg(args.workload, args.buckets)
-    t = [f"# Kernel trace of bench.py, {args.workload} workload (rocprofv3 --kernel-trace --stats)", "",
+    alg, nbk, nv, nb, S = _workload_alg(args.workload, args.buckets, args.rank)
+    who = args.workload + ("" if args.rank is None else f" rank {args.rank}")
+    t = [f"# Kernel trace of bench.py, {who} workload (rocprofv3 --kernel-trace --stats)", "",
          f"kernel sources hash: {kernel_source_hash(STEP_SOURCES)}", "",
          "command (run from the repository root, on the machine with the GPU):", "  " + args.command, "",
          f"{'kernel':72s} {'calls':>6s} {'avg us':>10s} {'min us':>10s} {'max us':>10s}"]
@@ -681,6 +684,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama", choices=["llama", "gptoss", "deepseek", "adversarial"])
     ap.add_argument("--buckets", type=int, default=None, help="override the number of buckets")
+    ap.add_argument("--rank", type=int, default=None,
+                    help="the rank whose step is timed (default: the one with the most valid elements)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-group-ops", action="store_true", help="skip timing the DBuffer group operations")
     ap.add_argument("--no-muon", action="store_true", help="skip timing Muon's Newton-Schulz iteration")
@@ -723,7 +728,12 @@ def main():
 
     cfg = CONFIGS[args.workload]
     lay = plan_p0(cfg.tensors, cfg.fsdp)
-    rank = lay.largest_rank()
+    rank = lay.largest_rank() if args.rank is None else args.rank
+    if not 0 <= rank < lay.fsdp:
+        print(f"bench.py: --rank {rank} outside [0, {lay.fsdp}) for the {args.workload} workload", file=sys.stderr)
+        sys.exit(2)
+    # the committed HBM counters were taken on the default rank
+    own_counters = rank == lay.largest_rank()
     nbk = args.buckets or cfg.n_buckets
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -767,7 +777,7 @@ def main():
     alg_bytes = nbk * (BYTES_PER_ELEM * valid + BYTES_PER_BLOCK * nblocks + BYTES_PER_PAD * (S - valid))
     gbs = alg_bytes / (ms / 1e3) / 1e9
     params_s = nbk * valid / (ms / 1e3)
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload) if own_counters else None
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -796,7 +806,7 @@ def main():
     }
     if not args.no_group_ops:
         out["group_ops"] = time_group_ops(torch, ve, plan, rank, states, lay, valid, 10, 2,
-                                          measured_group_traffic(args.workload))
+                                          measured_group_traffic(args.workload) if own_counters else None)
     del states, table, buckets
     torch.cuda.empty_cache()
     if not (args.no_copy_in and args.no_rank_sweep):

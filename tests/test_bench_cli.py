@@ -21,6 +21,32 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert "--gpus 2" in r.stderr and r.stdout == ""
 
 
+def test_rank_outside_the_workload_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--rank", "128"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2
+    assert "--rank 128 outside [0, 128)" in r.stderr and r.stdout == ""
+
+
+def test_summarize_trace_prices_the_named_rank(tmp_path):
+    """--rank 36 (LLaMA: 819 rows of 8,192 elements a bucket, 234 blocks on
+    the default rank): the launch is priced with that rank's blocks."""
+    import bench
+    step = "void ve::(anonymous namespace)::k_step_rows<1024, 8, 4>(ve::StepArgs, unsigned int, unsigned int)"
+    rows = [_trace_row(step, 0, 1000, 256 * 1024), _trace_row(step, 2000, 1200, 256 * 1024)]
+    _write_csv(str(tmp_path / "kt" / "run_kernel_trace.csv"), rows)
+    _write_csv(str(tmp_path / "kt" / "run_kernel_stats.csv"),
+               [{"Name": step, "Calls": 2, "AverageNs": 1100000, "MinNs": 1000000, "MaxNs": 1200000}])
+    out = tmp_path / "s.txt"
+    _summarize("trace", "--workload", "llama", "--rank", "36", "--trace-dir", str(tmp_path / "kt"), "--command",
+               "cmd", "--out", str(out))
+    alg36, _, nv, nb, _ = bench._workload_alg("llama", rank=36)
+    assert nb == 819 and alg36 != bench._workload_alg("llama")[0]
+    txt = out.read_text()
+    assert "llama rank 36 workload" in txt
+    assert f"{alg36 / 1100.0 / 1e3:.1f} GB/s" in txt
+
+
 def test_planner_leg_reports_padding_at_or_above_its_bound():
     import bench
     import ragged_shard_optimizer_amd as ve
