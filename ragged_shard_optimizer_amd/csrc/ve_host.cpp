@@ -339,28 +339,29 @@ int64_t set_inline(StepArgs& a, const RankTables& rt, const HostWork& w, size_t 
     return a.work.total;
 }
 
-// Blocks per persistent item for a workgroup-path segment, 0 for none: a
-// segment of whole-row blocks (one tile a panel) of 2,048 or 4,096 groups
-// runs items of 4 or 2 consecutive blocks, 8,192 groups, as one contiguous
-// span (option wg_rows; needs the persistent form and no pinned shape).
-// Measured on MI355X, a rank of 8,192-element rows: see the kernel.
-int row_items(const Seg& sg) {
-    if (option(kOptWgRows) == 0 || option(kOptWgDynamic) == 0) return 0;
-    if (option(kOptWgThreads) > 0 && option(kOptWgGpt) > 0) return 0;
-    if (sg.tiles != 1) return 0;
-    if (sg.max_groups == kRowsGroups / 4) return 4;
-    if (sg.max_groups == kRowsGroups / 2) return 2;
-    return 0;
+// Persistent multi-block item form of a workgroup-path segment (ItemForm),
+// kItemNone for none: segments of whole-row blocks (one tile a panel) of
+// 2,048 or 4,096 groups run items of 4 or 2 consecutive blocks, 8,192
+// groups, as one contiguous span (option wg_rows; needs the persistent
+// form and no pinned shape).  Measured on MI355X: see the kernel.
+int item_form(const Seg& sg) {
+    if (option(kOptWgRows) == 0 || option(kOptWgDynamic) == 0) return kItemNone;
+    if (option(kOptWgThreads) > 0 && option(kOptWgGpt) > 0) return kItemNone;
+    if (sg.tiles != 1) return kItemNone;
+    if (sg.max_groups == kItemGroups / 4) return kItemRows4;
+    if (sg.max_groups == kItemGroups / 2) return kItemRows2;
+    return kItemNone;
 }
 
-// Items of rpi blocks over segments [i0, i1) of a class's work list (each
-// segment's last item may hold fewer blocks); with `a`, writes the item
-// prefix into its inline table (after set_inline) and the item total.
-int64_t row_item_prefix(const RankTables& rt, const HostWork& w, size_t i0, size_t i1, int rpi, StepArgs* a) {
+// Items of item_blocks(form) blocks over segments [i0, i1) of a class's work
+// list (a segment's last item may hold fewer blocks); with `a`, writes the
+// item prefix into its inline table (after set_inline) and the item total.
+int64_t item_prefix(const RankTables& rt, const HostWork& w, size_t i0, size_t i1, int form, StepArgs* a) {
+    const int64_t per = item_blocks(form);
     int64_t tot = 0;
     for (size_t i = i0; i < i1; ++i) {
         if (a) a->inl_prefix[i - i0] = tot;
-        tot += ceil_div(rt.segs[(size_t)w.seg_idx[i]].nblocks, (int64_t)rpi);
+        tot += ceil_div(rt.segs[(size_t)w.seg_idx[i]].nblocks, per);
     }
     if (a) {
         a->inl_prefix[i1 - i0] = tot;
@@ -714,11 +715,11 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
         // the end of one tensor and most of a tensor with smaller blocks gets
         // two launches instead of running every block in the larger shape).
         // Segments of whole-row blocks of 2,048 or 4,096 groups (rows of 8K
-        // or 16K elements) run persistent with items of rows_per_item blocks
-        // (rpi > 0); see row_items().
+        // or 16K elements) and of 128 x 128 tiles run persistent with items
+        // of several blocks (form != kItemNone); see item_form().
         struct WgLaunch {
             size_t i0, i1;
-            int threads, gpt, rpi;
+            int threads, gpt, form;
             bool dyn;
         };
         std::vector<WgLaunch> runs;
@@ -727,25 +728,25 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
         auto shape_of = [&](size_t i, int& t, int& g, int& r) {
             const Seg& sg = rt.segs[(size_t)rt.wg.seg_idx[i]];
             wg_shape(sg.max_groups, t, g);
-            r = row_items(sg);
+            r = item_form(sg);
         };
         for (size_t i0 = 0; i0 < n;) {
-            int threads = 256, gpt = 1, rpi = 0;
-            shape_of(i0, threads, gpt, rpi);
+            int threads = 256, gpt = 1, form = kItemNone;
+            shape_of(i0, threads, gpt, form);
             size_t i1 = i0 + 1;
-            for (int t1, g1, r1; i1 < n && i1 - i0 < (size_t)kInlineSegs; ++i1) {
-                shape_of(i1, t1, g1, r1);
-                if (t1 != threads || g1 != gpt || r1 != rpi) break;
+            for (int t1, g1, f1; i1 < n && i1 - i0 < (size_t)kInlineSegs; ++i1) {
+                shape_of(i1, t1, g1, f1);
+                if (t1 != threads || g1 != gpt || f1 != form) break;
             }
-            const int64_t items = rpi > 0 ? row_item_prefix(rt, rt.wg, i0, i1, rpi, nullptr)
-                                          : rt.wg.prefix[i1] - rt.wg.prefix[i0];
+            const int64_t items = form != kItemNone ? item_prefix(rt, rt.wg, i0, i1, form, nullptr)
+                                                    : rt.wg.prefix[i1] - rt.wg.prefix[i0];
             // Row-block shapes run persistent, the resident workgroups taking
             // blocks from the rank's counters; tickets stay below 2^31.
             const bool fits = items * n_states + (int64_t)kDynMaxPerCu * plan->n_cu < (int64_t(1) << 31);
-            if (rpi > 0 && !fits) rpi = 0;
+            if (!fits) form = kItemNone;
             const bool dyn = items > 0 && fits && option(kOptWgDynamic) != 0 &&
-                             (rpi > 0 || wg_dynamic_shape(threads, gpt));
-            runs.push_back({i0, i1, threads, gpt, rpi, dyn});
+                             (form != kItemNone || wg_dynamic_shape(threads, gpt));
+            runs.push_back({i0, i1, threads, gpt, form, dyn});
             any_dyn = any_dyn || dyn;
             i0 = i1;
         }
@@ -767,11 +768,11 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
                 return fail(VE_ERR_DEVICE, "hipStreamWaitEvent on the rank's previous step failed");
         }
         for (const WgLaunch& w : runs) {
-            if (w.rpi > 0) {
+            if (w.form != kItemNone) {
                 if (set_inline(a, rt, rt.wg, w.i0, w.i1) == 0) continue;
-                row_item_prefix(rt, rt.wg, w.i0, w.i1, w.rpi, &a);
-                if ((st = launch_status(launch_step_rows(a, n_states, w.rpi, plan->n_cu, s), "row-item step")) !=
-                    VE_OK)
+                item_prefix(rt, rt.wg, w.i0, w.i1, w.form, &a);
+                if ((st = launch_status(launch_step_items(a, n_states, w.form, plan->n_cu, s),
+                                        "multi-block item step")) != VE_OK)
                     return st;
                 continue;
             }

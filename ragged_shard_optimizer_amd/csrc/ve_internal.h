@@ -153,12 +153,14 @@ hipError_t launch_step_wg(const StepArgs& a, int n_states, int threads, int grou
                           hipStream_t s);
 constexpr int kDynMaxPerCu = 8;
 bool wg_dynamic_shape(int threads, int groups_per_thread);
-// Persistent form over items of `rows_per_item` (2 or 4) consecutive
-// whole-row blocks of 4,096 or 2,048 groups (8,192 groups an item), in
-// kRowsThreads x kRowsGpt workgroups; a.inl_prefix counts items, a.sched as
-// above, dyn_cu > 0.
-constexpr int kRowsThreads = 1024, kRowsGpt = 8, kRowsGroups = kRowsThreads * kRowsGpt;
-hipError_t launch_step_rows(const StepArgs& a, int n_states, int rows_per_item, int dyn_cu, hipStream_t s);
+// Persistent form over items of several blocks, 8,192 groups an item, in
+// kItemThreads x kItemGpt workgroups: 2 or 4 consecutive whole-row blocks
+// of 4,096 or 2,048 groups (kItemRows2 / kItemRows4).  a.inl_prefix counts
+// items, a.sched as above, dyn_cu > 0.
+constexpr int kItemThreads = 1024, kItemGpt = 8, kItemGroups = kItemThreads * kItemGpt;
+enum ItemForm : int { kItemNone = 0, kItemRows2 = 2, kItemRows4 = 4 };
+constexpr int item_blocks(int form) { return form; }
+hipError_t launch_step_items(const StepArgs& a, int n_states, int form, int dyn_cu, hipStream_t s);
 hipError_t launch_step_huge(const StepArgs& a, int n_states, hipStream_t s);
 // Copy-in: out = bucket; grad pointers from `grad_ptrs`.
 hipError_t launch_runs_copy(const RunArgs& r, const uint16_t* const* grad_ptrs, uint16_t* out,

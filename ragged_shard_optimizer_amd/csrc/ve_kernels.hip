@@ -1658,16 +1658,17 @@ __global__ void __launch_bounds__(T) k_step_rows(StepArgs a, uint32_t nx, uint32
             if (staged) staged = rows_block<T, GPT, true, RPI>(it, a, nx, nitems, nt, wn, &s_next, s_buf, s_red, mst);
             else staged = rows_block<T, GPT, false, RPI>(it, a, nx, nitems, nt, wn, &s_next, s_buf, s_red, mst);
         } else {
-            // block by block through the general workgroup code
+            // block by block through the general workgroup code (such items
+            // are rare: shifted state arrays, rows that are not whole groups,
+            // a tensor's last item; the faster forms there would spill
+            // registers in the whole kernel)
             __builtin_amdgcn_s_waitcnt(0);
             __builtin_amdgcn_s_barrier();
             if (threadIdx.x == 0) s_next = atomicAdd(a.sched, 1u);  // read after the blocks' barriers
             for (int r = 0; r < it.nrows; ++r) {
                 const WgItem gi = wg_item_for<GPT>(a, y, sg, lb + r, lb + r);
                 if (r > 0) __syncthreads();  // the previous block's reads of s_red1
-                if (gi.mode == kWgLinear) wg_one<T, GPT, kWgLinear>(gi, s_red1, a.sc);
-                else if (gi.mode == kWgTiled) wg_one<T, GPT, kWgTiled>(gi, s_red1, a.sc);
-                else wg_one<T, GPT, kWgGeneral>(gi, s_red1, a.sc);
+                wg_one<T, GPT, kWgGeneral>(gi, s_red1, a.sc);
             }
             wn = s_next;
             staged = false;
@@ -1723,28 +1724,31 @@ static hipError_t launch_wg_t(const StepArgs& a, int n_states, int dyn_cu, hipSt
     return hipGetLastError();
 }
 
-template <int RPI>
-static hipError_t launch_rows_t(const StepArgs& a, int n_states, int dyn_cu, hipStream_t s) {
-    static const int occ = [] {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_step_rows<kRowsThreads, kRowsGpt, RPI>, kRowsThreads,
-                                                         0) != hipSuccess ||
-            n < 1)
-            n = 1;
-        return n < kDynMaxPerCu ? n : kDynMaxPerCu;
-    }();
-    const int64_t items = a.work.total * n_states;
-    const int64_t grid = std::min<int64_t>(items, (int64_t)dyn_cu * occ);
-    hipLaunchKernelGGL((k_step_rows<kRowsThreads, kRowsGpt, RPI>), dim3((unsigned)grid), dim3(kRowsThreads), 0, s, a,
-                       (uint32_t)a.work.total, (uint32_t)items);
-    return hipGetLastError();
+// Resident workgroups per CU of a persistent item kernel (its LDS and
+// registers decide), at most kDynMaxPerCu.
+template <class K>
+static int item_occupancy(K kernel) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kItemThreads, 0) != hipSuccess || n < 1) n = 1;
+    return n < kDynMaxPerCu ? n : kDynMaxPerCu;
 }
 
-hipError_t launch_step_rows(const StepArgs& a, int n_states, int rpi, int dyn_cu, hipStream_t s) {
+hipError_t launch_step_items(const StepArgs& a, int n_states, int form, int dyn_cu, hipStream_t s) {
+    constexpr int T = kItemThreads, G = kItemGpt;
     if (dyn_cu < 1) return hipErrorInvalidValue;
-    if (rpi == 2) return launch_rows_t<2>(a, n_states, dyn_cu, s);
-    if (rpi == 4) return launch_rows_t<4>(a, n_states, dyn_cu, s);
-    return hipErrorInvalidValue;
+    const int64_t items = a.work.total * n_states;
+    const uint32_t nx = (uint32_t)a.work.total, ni = (uint32_t)items;
+    auto grid = [&](int occ) { return dim3((unsigned)std::min<int64_t>(items, (int64_t)dyn_cu * occ)); };
+    if (form == kItemRows4) {
+        static const int occ = item_occupancy(k_step_rows<T, G, 4>);
+        hipLaunchKernelGGL((k_step_rows<T, G, 4>), grid(occ), dim3(T), 0, s, a, nx, ni);
+    } else if (form == kItemRows2) {
+        static const int occ = item_occupancy(k_step_rows<T, G, 2>);
+        hipLaunchKernelGGL((k_step_rows<T, G, 2>), grid(occ), dim3(T), 0, s, a, nx, ni);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 bool wg_config_supported(int threads, int gpt) {
