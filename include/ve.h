@@ -213,7 +213,8 @@ ve_status ve_dbuffer_group_op(const ve_plan* plan, int32_t rank, int32_t op, flo
  *   "gemm_cfg" (VE_GEMM_CFG, -1): pin a product configuration (0, 2: register
  *       staged 128^2 / 256^2 tiles; 6, 9: direct-to-LDS 4 waves of 128^2 /
  *       8 waves of 128x64; 13: 8 waves of 128x64, P direct to LDS in three
- *       stages, Q through registers); -1 = chosen by shape;
+ *       stages, Q through registers; 14: direct-to-LDS 128^2 tiles of 2
+ *       waves of 128x64, two workgroups a CU); -1 = chosen by shape;
  *   "gemm_xcd" (VE_GEMM_XCD, 1): 0 = plain tile order instead of the
  *       XCD-aware one;
  *   "wg_dynamic" (VE_WG_DYNAMIC, 1): 0 = the step's row-block shapes

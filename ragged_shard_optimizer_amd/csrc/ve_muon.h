@@ -37,7 +37,7 @@ struct GemmArgs {
     float* partial;
 };
 // Scratch for the split tail of a product: at most one launch's worth of
-// 256 x 256 fp32 tiles, one per CU.
+// 256 x 256 fp32 tiles, one per CU (or of 128 x 128 tiles, two per CU).
 constexpr int64_t kSplitPartialBytes = int64_t(256) * 256 * 256 * 4;
 hipError_t launch_gemm_nt(GemmArgs g, hipStream_t s);
 int64_t gemm_tiles(int64_t M, int64_t N);

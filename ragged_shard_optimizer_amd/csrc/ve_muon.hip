@@ -390,9 +390,9 @@ constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 
 // QST: Q is staged through registers (global -> VGPR two steps ahead ->
 // LDS one step ahead, two LDS stages) while P keeps the direct LDS DMA in
 // STAGES stages, so that both operands' loads have two steps to land.
-template <int WM_, int WN_, int BK_, int STAGES_, bool QST_ = false>
+template <int WM_, int WN_, int BK_, int STAGES_, bool QST_ = false, int BM_ = 256, int BN_ = 256>
 struct DmaCfg {
-    static constexpr int BM = 256, BN = 256, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_;
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_;
     static constexpr bool QST = QST_;
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, WAVES = WAVES_M * WAVES_N;
 #ifndef VE_EARLY_BARRIER
@@ -414,6 +414,9 @@ struct DmaCfg {
     static constexpr int SMEM = OP_BYTES > PASS_ROWS * LDC * 4 ? OP_BYTES : PASS_ROWS * LDC * 4;
     static_assert(DMA_PER_OP * ROWS_PER_DMA * WAVES == BM, "DMA rows must divide evenly");
     static_assert(SMEM <= 160 * 1024, "LDS");
+    // workgroups a CU holds at once, as its LDS allows (the split policy
+    // counts that many slots a CU)
+    static constexpr int PER_CU = (160 * 1024) / SMEM;
     // swizzle: rows sharing a bank line get distinct slots
     __device__ static __forceinline__ int swz(int r) {
         if constexpr (CHUNKS == 8) return (r & 7) ^ ((r >> 3) & 1);
@@ -421,10 +424,13 @@ struct DmaCfg {
     }
 };
 
-#define VE_DMA_CFGS(X)           \
-    X(6, 128, 128, 64, 2, false) \
-    X(9, 128, 64, 64, 2, false)  \
-    X(13, 128, 64, 64, 3, true)
+// (id, wave tile, K step, P stages, Q staged through registers, tile);
+// 14: 128 x 128 tiles of 2 waves in 64 KiB of LDS, two workgroups a CU.
+#define VE_DMA_CFGS(X)                     \
+    X(6, 128, 128, 64, 2, false, 256, 256) \
+    X(9, 128, 64, 64, 2, false, 256, 256)  \
+    X(13, 128, 64, 64, 3, true, 256, 256)  \
+    X(14, 128, 64, 64, 2, false, 128, 128)
 
 template <class CF, bool HAS_D, bool HAS_C, bool HAS_CT>
 __device__ __forceinline__ void dma_epilogue(const GemmArgs& g, f32x16 (&acc)[CF::TM][CF::TN], int ti, int tj,
@@ -1055,12 +1061,13 @@ hipError_t launch_gemm_t(GemmArgs g, hipStream_t s) {
 // in order and runs the epilogue.  Only over long contractions (at least 8
 // steps per slice).  Returns the slice count (1: no split) and the number of
 // tiles launched whole.  The option gemm_split = 0 turns it off.
-inline int tail_split(int64_t tiles, int64_t nk, bool has_partial, int64_t& full) {
+inline int tail_split(int64_t tiles, int64_t nk, bool has_partial, int64_t& full, int per_cu = 1) {
     full = tiles;
     if (!has_partial || option(kOptGemmSplit) == 0 || nk < 16) return 1;
-    const int64_t whole = tiles / kCUs * kCUs, tail = tiles - whole;
-    if (tail == 0 || (whole > 0 && tail * 4 > kCUs)) return 1;
-    const int64_t ks = std::min<int64_t>(std::min<int64_t>(kCUs / tail, nk / 8), 32);
+    const int64_t slots = (int64_t)kCUs * per_cu;  // workgroups resident at once
+    const int64_t whole = tiles / slots * slots, tail = tiles - whole;
+    if (tail == 0 || (whole > 0 && tail * 4 > slots)) return 1;
+    const int64_t ks = std::min<int64_t>(std::min<int64_t>(slots / tail, nk / 8), 32);
     if (ks < 2) return 1;
     full = whole;
     return (int)ks;
@@ -1073,14 +1080,14 @@ hipError_t launch_dma_t(GemmArgs g, hipStream_t s) {
     g.tile_base = 0;
     g.ksplit = 1;
     int64_t full = tiles;
-    const int ks = tail_split(tiles, g.K / CF::BK, g.partial != nullptr, full);
+    const int ks = tail_split(tiles, g.K / CF::BK, g.partial != nullptr, full, CF::PER_CU);
     if (ks <= 1) {
         hipLaunchKernelGGL((k_gemm_nt_dma<CF, HAS_D, HAS_C, HAS_CT>), dim3((unsigned)tiles), dim3(CF::THREADS), 0, s,
                            g);
         return hipGetLastError();
     }
     const int64_t tail = tiles - full;
-    static_assert(int64_t(CF::BM) * CF::BN * 4 * kCUs <= kSplitPartialBytes, "split scratch");
+    static_assert(int64_t(CF::BM) * CF::BN * 4 * kCUs * CF::PER_CU <= kSplitPartialBytes, "split scratch");
     if (full > 0)  // whole rounds first (none when the product is split whole)
         hipLaunchKernelGGL((k_gemm_nt_dma<CF, HAS_D, HAS_C, HAS_CT>), dim3((unsigned)full), dim3(CF::THREADS), 0, s,
                            g);
@@ -1143,7 +1150,9 @@ int gemm_cfg_override() { return (int)option(kOptGemmCfg); }
 // below that, the configuration with the smaller modelled time: rounds of
 // work items times their K steps, a 128 x 128 step costing 0.45 of a
 // 256 x 256 one (a quarter of the work at 56% of the rate, measured), split
-// slices adding their fp32 traffic (about 0.05 of a step each).
+// slices adding their fp32 traffic (about 0.05 of a step each).  Before
+// that model, symmetric products of at most one round of 128 x 128 tiles
+// take configuration 14.
 int gemm_cfg_auto(const GemmArgs& g) {
     const int64_t tm = (g.M + 255) / 256, tn = (g.N + 255) / 256;
     const int64_t active = g.symmetric ? tm * (tm + 1) / 2 : tm * tn;
@@ -1152,6 +1161,17 @@ int gemm_cfg_auto(const GemmArgs& g) {
     // the staged-Q form where its 32-bit row offsets reach, else the plain one
     const int big = dma_ok<DmaCfg<128, 64, 64, 3, true>>(g) ? 13 : 9;
     if (active >= 2 * kCUs) return big;
+    // A symmetric product whose 128 x 128 tiles fit in one round of the
+    // two-per-CU configuration 14 (then split along K over those slots).
+    // Measured, Newton-Schulz per call, interleaved on one box each time:
+    // 2048 x 7168 0.89-0.92 ms against 0.90-0.97, 1024 x 8192 0.48-0.49
+    // against 0.50-0.51; not for 5760 x 5760 (1,035 such tiles: 4.47
+    // against 4.20 ms), so only within one round.
+    using C14 = DmaCfg<128, 64, 64, 2, false, 128, 128>;
+    if (g.symmetric) {
+        const int64_t s = (g.M + C14::BM - 1) / C14::BM;
+        if (s * (s + 1) / 2 <= (int64_t)kCUs * C14::PER_CU && dma_ok<C14>(g)) return 14;
+    }
     const int64_t nk = g.K / 64;
     auto rounds = [](int64_t items) { return (double)((items + kCUs - 1) / kCUs); };
     int64_t full = active;
@@ -1179,10 +1199,12 @@ hipError_t launch_gemm_nt(GemmArgs g, hipStream_t s) {
         case ID: return launch_gemm_cfg<Cfg<BM, BN, BK, WM, WN>>(g, s);
         VE_GEMM_CFGS(VE_GEMM_CASE)
 #undef VE_GEMM_CASE
-#define VE_DMA_CASE(ID, WM, WN, BK, ST, QS)                                                         \
-        case ID:                                                                                    \
-            return dma_ok<DmaCfg<WM, WN, BK, ST, QS>>(g) ? launch_gemm_dma<DmaCfg<WM, WN, BK, ST, QS>>(g, s) \
-                                                         : launch_gemm_cfg<Cfg<256, 256, 64, 128, 64>>(g, s);
+#define VE_DMA_CASE(ID, WM, WN, BK, ST, QS, BM, BN)                                                   \
+        case ID:                                                                                        \
+            return dma_ok<DmaCfg<WM, WN, BK, ST, QS, BM, BN>>(g)                                        \
+                       ? launch_gemm_dma<DmaCfg<WM, WN, BK, ST, QS, BM, BN>>(g, s)                      \
+                       : (BM == 256 ? launch_gemm_cfg<Cfg<256, 256, 64, 128, 64>>(g, s)                 \
+                                    : launch_gemm_cfg<Cfg<128, 128, 64, 64, 64>>(g, s));
         VE_DMA_CFGS(VE_DMA_CASE)
 #undef VE_DMA_CASE
         default: return hipErrorInvalidValue;

@@ -373,11 +373,12 @@ def test_large_ragged_products_sampled(M, N, K, sym):
         assert abs(Ch[i, j] - want[0, 0]) <= bd[0, 0], (i, j, Ch[i, j], want[0, 0])
 
 
-# The large-tile product configurations: 6 (4 waves of 128 x 128, two LDS
-# stages), 9 (8 waves of 128 x 64, two stages) and 13 (8 waves, P in three
-# LDS stages, Q staged through registers; the default).  They feed the MFMAs
-# the same fragments in the same order, so their outputs agree bit for bit;
-# ragged edges (rows past M or N), a symmetric product and C^T included.
+# The direct-to-LDS product configurations: 6 (4 waves of 128 x 128, two
+# LDS stages), 9 (8 waves of 128 x 64, two stages), 13 (8 waves, P in three
+# LDS stages, Q staged through registers) and 14 (128 x 128 tiles of 2
+# waves of 128 x 64, two stages).  They feed the MFMAs the same fragments in
+# the same order, so their outputs agree bit for bit; ragged edges (rows
+# past M or N), a symmetric product and C^T included.
 @pytest.mark.parametrize("M,N,K,sym", [(7000, 7040, 1024, False), (2048, 2048, 7168, True), (300, 520, 640, False),
                                        (1000, 300, 2880, False)])
 def test_product_configurations_agree(M, N, K, sym):
@@ -391,7 +392,7 @@ def test_product_configurations_agree(M, N, K, sym):
     if sym:
         D = (D.view(torch.bfloat16) + D.view(torch.bfloat16).t()).contiguous().view(torch.int16)
     outs = {}
-    for cfg in (9, 6, 13):
+    for cfg in (9, 6, 13, 14):
         C = _empty((M, N))
         CT = None if sym else _empty((N, M))
         _say(f"[gpu] product configuration {cfg}: M={M} N={N} K={K} symmetric={sym}")
@@ -399,7 +400,7 @@ def test_product_configurations_agree(M, N, K, sym):
             ve.gemm_bf16_nt(P, Q, C=C, CT=CT, D=D, alpha=0.75, beta=-0.5, symmetric=sym)
         torch.cuda.synchronize()
         outs[cfg] = (C, CT)
-    for cfg in (6, 13):
+    for cfg in (6, 13, 14):
         assert torch.equal(outs[cfg][0], outs[9][0]), cfg
         if not sym:
             assert torch.equal(outs[cfg][1], outs[9][1]), cfg

@@ -334,18 +334,31 @@ def test_row_items_misaligned_state_buffers():
     plan.close()
 
 
-def test_persistent_step_replays_in_a_captured_graph():
+# The two persistent kernels that take work from the rank's counters: the
+# row-block form (forced to 512 x 16 on DYN_TENSORS) and the row items.
+PERSISTENT_FORMS = {
+    "rowblock": (DYN_TENSORS, dict(wg_threads=512, wg_gpt=16, wg_dynamic=1), 1),
+    "rowitems": (ROW_TENSORS, dict(wg_dynamic=1, wg_rows=1), 0),
+}
+
+
+def _persistent_form(name, steps):
+    tensors, opts, rank = PERSISTENT_FORMS[name]
+    lay = plan_p0(tensors, 2)
+    return Config(name, list(tensors), fsdp=2, grad_scale=1e-3, steps=steps), lay, opts, rank
+
+
+@pytest.mark.parametrize("form", list(PERSISTENT_FORMS))
+def test_persistent_step_replays_in_a_captured_graph(form):
     """Each persistent launch's last workgroup resets the rank's counters, so
     a captured step replays: three replays, with eager steps of another
     bucket on the same plan and rank in between, each bit-identical to an
     eager step of a twin bucket."""
     import torch
     ve = _ve()
-    lay = plan_p0(DYN_TENSORS, 2)
-    cfg = Config("dyn", list(DYN_TENSORS), fsdp=2, grad_scale=1e-3, steps=2)
+    cfg, lay, opts, r = _persistent_form(form, 2)
     plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
     hp = hp32()
-    r = 1
     # cap and twin: two copies of bucket 0's state and gradients
     cap, twin, other = (RankProblem(ve, cfg, lay, plan, r, bucket=b) for b in (0, 0, 1))
     cap.set_grads(1)
@@ -354,8 +367,8 @@ def test_persistent_step_replays_in_a_captured_graph():
     torch.cuda.synchronize()
     a, b = cap.download(), twin.download()
     assert all(np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)) for k in a)
-    with ve.options(wg_threads=512, wg_gpt=16, wg_dynamic=1):
-        _say("[gpu] dyn 512 x 16 step captured in a graph")
+    with ve.options(**opts):
+        _say(f"[gpu] {form} step captured in a graph, rank {r}")
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         with torch.cuda.graph(g, stream=side):
@@ -375,15 +388,15 @@ def test_persistent_step_replays_in_a_captured_graph():
     plan.close()
 
 
-def test_persistent_steps_of_two_ranks_overlap_on_two_streams():
+@pytest.mark.parametrize("form", list(PERSISTENT_FORMS))
+def test_persistent_steps_of_two_ranks_overlap_on_two_streams(form):
     """Each rank has its own scheduler counters, so step calls for different
     ranks of one plan may run at the same time: ranks 0 and 1 on two
     streams with no ordering between them, three steps, each equal to the
     same steps run one after another on twin buckets."""
     import torch
     ve = _ve()
-    lay = plan_p0(DYN_TENSORS, 2)
-    cfg = Config("dyn", list(DYN_TENSORS), fsdp=2, grad_scale=1e-3, steps=3)
+    cfg, lay, opts, _ = _persistent_form(form, 3)
     plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
     hp = hp32()
     run = {r: RankProblem(ve, cfg, lay, plan, r) for r in (0, 1)}
@@ -392,8 +405,8 @@ def test_persistent_steps_of_two_ranks_overlap_on_two_streams():
         p.set_grads(1)
     streams = {0: torch.cuda.Stream(), 1: torch.cuda.Stream()}
     torch.cuda.synchronize()
-    _say("[gpu] dyn 512 x 16, ranks 0 and 1 on two streams")
-    with ve.options(wg_threads=512, wg_gpt=16, wg_dynamic=1):
+    _say(f"[gpu] {form}, ranks 0 and 1 on two streams")
+    with ve.options(**opts):
         for t in (1, 2, 3):
             for r in (0, 1):
                 plan.step(r, run[r].table, hp, t, streams[r])
@@ -409,26 +422,25 @@ def test_persistent_steps_of_two_ranks_overlap_on_two_streams():
     plan.close()
 
 
-def test_persistent_steps_of_one_rank_on_two_streams_are_ordered():
+@pytest.mark.parametrize("form", list(PERSISTENT_FORMS))
+def test_persistent_steps_of_one_rank_on_two_streams_are_ordered(form):
     """Two buckets of one rank stepped alternately on two streams with no
     ordering by the caller: the library makes each call on a new stream wait
     for the rank's previous one (the counters admit one launch at a time),
     so every bucket equals the same steps run one after another."""
     import torch
     ve = _ve()
-    lay = plan_p0(DYN_TENSORS, 2)
-    cfg = Config("dyn", list(DYN_TENSORS), fsdp=2, grad_scale=1e-3, steps=3)
+    cfg, lay, opts, r = _persistent_form(form, 3)
     plan = ve.Plan(lay.spec_array(), lay.fsdp, lay.shard, device=0)
     hp = hp32()
-    r = 1
     run = [RankProblem(ve, cfg, lay, plan, r, bucket=b) for b in (0, 1)]
     twin = [RankProblem(ve, cfg, lay, plan, r, bucket=b) for b in (0, 1)]
     for p in run + twin:
         p.set_grads(1)
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     torch.cuda.synchronize()
-    _say("[gpu] dyn 512 x 16, one rank, two buckets on two streams")
-    with ve.options(wg_threads=512, wg_gpt=16, wg_dynamic=1):
+    _say(f"[gpu] {form}, rank {r}, two buckets on two streams")
+    with ve.options(**opts):
         for t in (1, 2, 3):
             for b in (0, 1):
                 plan.step(r, run[b].table, hp, t, streams[b])
