@@ -469,6 +469,28 @@ def test_rank_with_two_block_shapes(name, rank):
     tally.check()
 
 
+# One call, two persistent launches on the rank's counters: 28,672-element
+# rows (the row-block form, 1024 x 7) and 8,192-element rows (row items),
+# as on LLaMA's rank 35; three steps, so each launch must leave the counters
+# at zero for the next.
+MIXED_PERSISTENT = [
+    TensorDef("down", 40, 28672, 1, 28672),
+    TensorDef("gate", 301, 8192, 1, 8192),
+]
+
+
+def test_rank_with_row_blocks_and_row_items():
+    ve = _ve()
+    lay = plan_p0(MIXED_PERSISTENT, 2)
+    cfg = Config("mixed", list(MIXED_PERSISTENT), fsdp=2, grad_scale=1e-3, steps=3)
+    both = [r for r in (0, 1) if {lay.tensors[k].name for k, *_ in lay.chunk_intervals(r)} == {"down", "gate"}]
+    assert both, "a rank holding both tensors"
+    tally = Tally(cfg.name)
+    with ve.options(wg_dynamic=1, wg_rows=1):
+        _run_parity(cfg, lay, both, 3, tally)
+    tally.check()
+
+
 def test_one_element_blocks_codes_exact():
     # 1-element blocks: every nonzero code is +-127 and the scale is |m|/127
     cfg, lay = _explicit("unit", [TensorDef("a", 999, 1, 1, 1), TensorDef("b", 21, 17, 1, 1)], [0, 1008], 2, 768)
