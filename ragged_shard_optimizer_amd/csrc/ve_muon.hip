@@ -1151,8 +1151,8 @@ int gemm_cfg_override() { return (int)option(kOptGemmCfg); }
 // work items times their K steps, a 128 x 128 step costing 0.45 of a
 // 256 x 256 one (a quarter of the work at 56% of the rate, measured), split
 // slices adding their fp32 traffic (about 0.05 of a step each).  Before
-// that model, symmetric products of at most one round of 128 x 128 tiles
-// take configuration 14.
+// that model, symmetric products with K >= 4096 and at most one round of
+// 128 x 128 tiles take configuration 14.
 int gemm_cfg_auto(const GemmArgs& g) {
     const int64_t tm = (g.M + 255) / 256, tn = (g.N + 255) / 256;
     const int64_t active = g.symmetric ? tm * (tm + 1) / 2 : tm * tn;
@@ -1161,14 +1161,16 @@ int gemm_cfg_auto(const GemmArgs& g) {
     // the staged-Q form where its 32-bit row offsets reach, else the plain one
     const int big = dma_ok<DmaCfg<128, 64, 64, 3, true>>(g) ? 13 : 9;
     if (active >= 2 * kCUs) return big;
-    // A symmetric product whose 128 x 128 tiles fit in one round of the
-    // two-per-CU configuration 14 (then split along K over those slots).
-    // Measured, Newton-Schulz per call, interleaved on one box each time:
-    // 2048 x 7168 0.89-0.92 ms against 0.90-0.97, 1024 x 8192 0.48-0.49
-    // against 0.50-0.51; not for 5760 x 5760 (1,035 such tiles: 4.47
-    // against 4.20 ms), so only within one round.
+    // A symmetric product with a long contraction (K >= 4096, X X^T) whose
+    // 128 x 128 tiles fit in one round of the two-per-CU configuration 14
+    // (then split along K over those slots).  Measured, Newton-Schulz per
+    // call, interleaved on one box: 2048 x 7168 0.86 ms against 0.90,
+    // 1024 x 8192 0.445 against 0.49.  Not for A A at those sizes (K = m:
+    // slices of ~11 steps do not pay for their sums: 0.90 and 0.48 ms with
+    // it), nor beyond one round (5760 x 5760, 1,035 such tiles: 4.47
+    // against 4.20 ms).
     using C14 = DmaCfg<128, 64, 64, 2, false, 128, 128>;
-    if (g.symmetric) {
+    if (g.symmetric && g.K >= 4096) {
         const int64_t s = (g.M + C14::BM - 1) / C14::BM;
         if (s * (s + 1) / 2 <= (int64_t)kCUs * C14::PER_CU && dma_ok<C14>(g)) return 14;
     }
