@@ -217,13 +217,16 @@ ve_status ve_dbuffer_group_op(const ve_plan* plan, int32_t rank, int32_t op, flo
  *       waves of 128x64, two workgroups a CU); -1 = chosen by shape;
  *   "gemm_xcd" (VE_GEMM_XCD, 1): 0 = plain tile order instead of the
  *       XCD-aware one;
- *   "wg_dynamic" (VE_WG_DYNAMIC, 1): 0 = the step's row-block shapes
+ *   "wg_dynamic" (VE_WG_DYNAMIC, 1): how the step's row-block shapes
  *       (blocks of 4,097 to 12,288 groups: 512 threads with 14 to 24 groups
  *       per thread, 768 threads, 1024 threads with 7 to 10) and the row
- *       items below launch one workgroup per block instead of persistent
- *       workgroups (one or a few per CU) taking work from the plan's
- *       per-rank counters (same results, slower; no ordering of calls, see
- *       ve_shard_adam8bit_step);
+ *       items below launch.  1: persistent workgroups (one or a few per
+ *       CU) taking work from the plan's per-rank counters, for launches
+ *       with at least 5 such blocks (or 32 row items) per CU, one
+ *       workgroup per block below that (the persistent forms' fixed cost
+ *       exceeds their gain there); 2: persistent whatever the amount of
+ *       work; 0: never (no counters, no ordering of calls, see
+ *       ve_shard_adam8bit_step).  Same results in every case;
  *   "wg_rows" (VE_WG_ROWS, 1): 0 = whole-row blocks of 2,048 or 4,096
  *       groups (rows of 8K or 16K elements) run one workgroup per block
  *       instead of persistent items of 4 or 2 consecutive blocks (same

@@ -386,7 +386,7 @@ int64_t item_prefix(const RankTables& rt, const HostWork& w, size_t i0, size_t i
 //     least 6 groups (fewer leave the per-block prologue exposed), else 256.
 // The options wg_threads / wg_gpt pin it (launch-shape tuning) for blocks
 // that fit the pinned shape.
-void wg_shape(int32_t groups, int& threads, int& gpt) {
+void wg_shape(int32_t groups, int& threads, int& gpt, bool persistent) {
     const int64_t ot = option(kOptWgThreads), og = option(kOptWgGpt);
     if (ot > 0 && og > 0 && ot <= kWgMaxThreads && og <= 64) {
         threads = (int)ot;
@@ -404,7 +404,7 @@ void wg_shape(int32_t groups, int& threads, int& gpt) {
         gpt = g;
         return;
     }
-    if (groups > 4096 && groups <= 12288 && option(kOptWgDynamic) != 0) {
+    if (groups > 4096 && groups <= 12288 && persistent) {
         // idle fraction (t * g - groups) / (t * g), compared as fractions
         int64_t bt = 0, bg = 0;
         auto better = [&](int64_t t, int64_t gg) {
@@ -727,8 +727,30 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
         const size_t n = rt.wg.seg_idx.size();
         auto shape_of = [&](size_t i, int& t, int& g, int& r) {
             const Seg& sg = rt.segs[(size_t)rt.wg.seg_idx[i]];
-            wg_shape(sg.max_groups, t, g);
+            wg_shape(sg.max_groups, t, g, option(kOptWgDynamic) != 0);
             r = item_form(sg);
+        };
+        // Persistent launches pay a fixed cost (about 9 us a launch, 13 us with
+        // row items) that only enough work hides: measured on MI355X, LLaMA
+        // rows, against the one-shot launch: 28,672-element rows from about
+        // 5 blocks per CU on (6 buckets of rank 0: 23.6 against 24.0 us a
+        // bucket; 1 bucket: 37.0 against 28.0 us), row items from about 32
+        // per CU on (48 buckets of rank 36: 20.7 against 21.1 us a bucket;
+        // 16 buckets: 21.8 against 21.0).  Below that, the run takes the
+        // one-shot shapes; wg_dynamic = 2 keeps the persistent forms anyway.
+        const int64_t dyn_opt = option(kOptWgDynamic);
+        auto push_runs = [&](size_t i0, size_t i1, bool persistent) {
+            for (size_t a0 = i0; a0 < i1;) {
+                int threads = 256, gpt = 1;
+                wg_shape(rt.segs[(size_t)rt.wg.seg_idx[a0]].max_groups, threads, gpt, persistent);
+                size_t a1 = a0 + 1;
+                for (int t1, g1; a1 < i1; ++a1) {
+                    wg_shape(rt.segs[(size_t)rt.wg.seg_idx[a1]].max_groups, t1, g1, persistent);
+                    if (t1 != threads || g1 != gpt) break;
+                }
+                runs.push_back({a0, a1, threads, gpt, kItemNone, false});
+                a0 = a1;
+            }
         };
         for (size_t i0 = 0; i0 < n;) {
             int threads = 256, gpt = 1, form = kItemNone;
@@ -743,11 +765,15 @@ ve_status ve_shard_adam8bit_step(const ve_plan* plan, int32_t rank, const ve_sha
             // Row-block shapes run persistent, the resident workgroups taking
             // blocks from the rank's counters; tickets stay below 2^31.
             const bool fits = items * n_states + (int64_t)kDynMaxPerCu * plan->n_cu < (int64_t(1) << 31);
-            if (!fits) form = kItemNone;
-            const bool dyn = items > 0 && fits && option(kOptWgDynamic) != 0 &&
-                             (form != kItemNone || wg_dynamic_shape(threads, gpt));
-            runs.push_back({i0, i1, threads, gpt, form, dyn});
-            any_dyn = any_dyn || dyn;
+            const bool candidate = dyn_opt != 0 && (form != kItemNone || wg_dynamic_shape(threads, gpt));
+            const int64_t min_work = (form != kItemNone ? kItemMinPerCu : kDynMinPerCu) * (int64_t)plan->n_cu;
+            if (candidate && (!fits || (dyn_opt != 2 && items * n_states < min_work))) {
+                push_runs(i0, i1, false);  // one-shot shapes
+            } else {
+                const bool dyn = items > 0 && candidate;
+                runs.push_back({i0, i1, threads, gpt, form, dyn});
+                any_dyn = any_dyn || dyn;
+            }
             i0 = i1;
         }
         // The counters admit one launch at a time.  Launches on one stream

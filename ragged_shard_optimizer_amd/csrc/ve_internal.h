@@ -152,6 +152,9 @@ hipError_t launch_step_small(const StepArgs& a, int n_states, hipStream_t s);
 hipError_t launch_step_wg(const StepArgs& a, int n_states, int threads, int groups_per_thread, int dyn_cu,
                           hipStream_t s);
 constexpr int kDynMaxPerCu = 8;
+// Work a launch needs for the persistent forms (option wg_dynamic = 1):
+// blocks per CU for the row-block form, items per CU for row items.
+constexpr int kDynMinPerCu = 5, kItemMinPerCu = 32;
 bool wg_dynamic_shape(int threads, int groups_per_thread);
 // Persistent form over items of several blocks, 8,192 groups an item, in
 // kItemThreads x kItemGpt workgroups: 2 or 4 consecutive whole-row blocks
@@ -177,7 +180,8 @@ enum Option : int {
     kOptGemmSplit,      // "gemm_split" (VE_GEMM_SPLIT): 0 = never split a product's short last round
     kOptGemmCfg,        // "gemm_cfg" (VE_GEMM_CFG): product configuration, -1 = by shape
     kOptGemmXcd,        // "gemm_xcd" (VE_GEMM_XCD): 0 = plain tile order instead of the XCD-aware one
-    kOptWgDynamic,      // "wg_dynamic" (VE_WG_DYNAMIC): 0 = one-shot launches for the row-block shapes too
+    kOptWgDynamic,      // "wg_dynamic" (VE_WG_DYNAMIC): 0 = one-shot launches only; 1 = persistent forms where a
+                        // launch has enough work; 2 = persistent forms whatever the work
     kOptWgRows,         // "wg_rows" (VE_WG_ROWS): 0 = no multi-block items for blocks of 2,048 / 4,096 groups
     kNumOptions
 };

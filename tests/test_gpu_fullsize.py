@@ -140,7 +140,7 @@ def test_full_size_persistent_equals_one_shot(name):
     t_dyn, t_one = ve.state_table(plan, rank, dyn), ve.state_table(plan, rank, one)
     keys = ("grad_shard", "master", "m_q", "v_q", "m_scale", "v_scale", "param_shard")
     for t in (1, 2):
-        with ve.options(wg_dynamic=1):
+        with ve.options(wg_dynamic=2):
             plan.step(rank, t_dyn, hp, t)
         with ve.options(wg_dynamic=0):
             plan.step(rank, t_one, hp, t)
@@ -173,9 +173,9 @@ def test_full_size_row_items_equal_one_shot():
     t_itm, t_one = ve.state_table(plan, rank, itm), ve.state_table(plan, rank, one)
     keys = ("grad_shard", "master", "m_q", "v_q", "m_scale", "v_scale", "param_shard")
     for t in (1, 2):
-        with ve.options(wg_dynamic=1, wg_rows=1):
+        with ve.options(wg_dynamic=2, wg_rows=1):
             plan.step(rank, t_itm, hp, t)
-        with ve.options(wg_dynamic=1, wg_rows=0):
+        with ve.options(wg_dynamic=2, wg_rows=0):
             plan.step(rank, t_one, hp, t)
         torch.cuda.synchronize()
         for b, (x, y) in enumerate(zip(itm, one)):

@@ -185,7 +185,7 @@ def test_persistent_row_shapes(shape):
     assert max(t.block_rows * t.block_cols for t in DYN_TENSORS) <= 4 * shape[0] * shape[1]
     cfg = Config("dyn", list(DYN_TENSORS), fsdp=2, grad_scale=1e-3, steps=3)
     tally = Tally(cfg.name)
-    with ve.options(wg_threads=shape[0], wg_gpt=shape[1], wg_dynamic=1):
+    with ve.options(wg_threads=shape[0], wg_gpt=shape[1], wg_dynamic=2):
         _run_parity(cfg, lay, [0, 1], 3, tally)
     tally.check()
 
@@ -214,7 +214,7 @@ def test_persistent_equals_one_shot():
     _say("[gpu] dyn x3 persistent vs one-shot, 512 x 16")
     with ve.options(wg_threads=512, wg_gpt=16):
         for t in (1, 2):
-            with ve.options(wg_dynamic=1):
+            with ve.options(wg_dynamic=2):
                 plan.step(r, sets[0][1], hp, t)
             with ve.options(wg_dynamic=0):
                 plan.step(r, sets[1][1], hp, t)
@@ -254,7 +254,7 @@ def test_row_items_parity():
         nbl = {lay.tensors[k].name: (hi - lo) // lay.tensors[k].unit for k, lo, hi, *_ in lay.chunk_intervals(r)}
         assert any(n % 4 for n in nbl.values()), nbl
     tally = Tally(cfg.name)
-    with ve.options(wg_dynamic=1, wg_rows=1):
+    with ve.options(wg_dynamic=2, wg_rows=1):
         _run_parity(cfg, lay, [0, 1], 3, tally)
     tally.check()
 
@@ -294,9 +294,9 @@ def test_row_items_equal_one_shot():
         sets = _twin_sets(ve, cfg, lay, plan, r, 3)
         _say(f"[gpu] rows x3 rank {r}: row items vs one-shot")
         for t in (1, 2):
-            with ve.options(wg_dynamic=1, wg_rows=1):
+            with ve.options(wg_dynamic=2, wg_rows=1):
                 plan.step(r, sets[0][1], hp, t)
-            with ve.options(wg_dynamic=1, wg_rows=0):
+            with ve.options(wg_dynamic=2, wg_rows=0):
                 plan.step(r, sets[1][1], hp, t)
         torch.cuda.synchronize()
         _assert_twins_equal(sets)
@@ -323,7 +323,7 @@ def test_row_items_misaligned_state_buffers():
     st["grad_table"] = prob.gt
     table = ve.state_table(plan, r, [st])
     _say("[gpu] rows rank 0, misaligned state arrays")
-    with ve.options(wg_dynamic=1, wg_rows=1):
+    with ve.options(wg_dynamic=2, wg_rows=1):
         plan.step(r, prob.table, hp, 1)
         plan.step(r, table, hp, 1)
     torch.cuda.synchronize()
@@ -337,8 +337,8 @@ def test_row_items_misaligned_state_buffers():
 # The two persistent kernels that take work from the rank's counters: the
 # row-block form (forced to 512 x 16 on DYN_TENSORS) and the row items.
 PERSISTENT_FORMS = {
-    "rowblock": (DYN_TENSORS, dict(wg_threads=512, wg_gpt=16, wg_dynamic=1), 1),
-    "rowitems": (ROW_TENSORS, dict(wg_dynamic=1, wg_rows=1), 0),
+    "rowblock": (DYN_TENSORS, dict(wg_threads=512, wg_gpt=16, wg_dynamic=2), 1),
+    "rowitems": (ROW_TENSORS, dict(wg_dynamic=2, wg_rows=1), 0),
 }
 
 
@@ -486,7 +486,7 @@ def test_rank_with_row_blocks_and_row_items():
     both = [r for r in (0, 1) if {lay.tensors[k].name for k, *_ in lay.chunk_intervals(r)} == {"down", "gate"}]
     assert both, "a rank holding both tensors"
     tally = Tally(cfg.name)
-    with ve.options(wg_dynamic=1, wg_rows=1):
+    with ve.options(wg_dynamic=2, wg_rows=1):
         _run_parity(cfg, lay, both, 3, tally)
     tally.check()
 
