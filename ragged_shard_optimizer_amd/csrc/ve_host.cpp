@@ -343,7 +343,7 @@ int64_t set_inline(StepArgs& a, const RankTables& rt, const HostWork& w, size_t 
 // kItemNone for none: segments of whole-row blocks (one tile a panel) of
 // 2,048 or 4,096 groups run items of 4 or 2 consecutive blocks, 8,192
 // groups, as one contiguous span (option wg_rows; needs the persistent
-// form and no pinned shape).  Measured on MI355X: see the kernel.
+// form and no pinned shape; k_step_rows gives the measurements).
 int item_form(const Seg& sg) {
     if (option(kOptWgRows) == 0 || option(kOptWgDynamic) == 0) return kItemNone;
     if (option(kOptWgThreads) > 0 && option(kOptWgGpt) > 0) return kItemNone;
