@@ -47,6 +47,15 @@ def test_summarize_trace_prices_the_named_rank(tmp_path):
     assert f"{alg36 / 1100.0 / 1e3:.1f} GB/s" in txt
 
 
+def test_counter_summary_refuses_another_rank(tmp_path):
+    """bench.py reads the committed HBM counters back for the default rank
+    only, so they are never summarised for another one."""
+    import pytest
+    with pytest.raises(SystemExit, match="default rank only"):
+        _summarize("counters", "--workload", "llama", "--rank", "36", "--fetch-dir", str(tmp_path),
+                   "--write-dir", str(tmp_path))
+
+
 def test_planner_leg_reports_padding_at_or_above_its_bound():
     import bench
     import ragged_shard_optimizer_amd as ve
