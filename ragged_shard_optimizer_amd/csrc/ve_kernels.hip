@@ -22,6 +22,10 @@
 // Row blocks of 16K to 49K elements run a persistent form of the wg class
 // (k_step_dyn): one workgroup per CU takes blocks from a ticket counter and
 // stages the next block's gradient and codes in LDS during its own phase 2.
+// Whole-row blocks of 8K or 16K elements take the same loop in items of
+// four or two consecutive blocks (k_step_rows), each block keeping its own
+// absmax and scales.  The host uses both only where a launch has enough
+// blocks per CU to repay their fixed cost.
 //
 // Block-size classes (decided per rank segment at plan load):
 //   small  <= 64 chunks of kSmallChunk (4) elements: a group of G (power of
